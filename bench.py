@@ -1,0 +1,178 @@
+"""Throughput of causal prefill attention on one MI355X, one JSON line.
+
+A step is one pass of the hot path over the 16K-token workloads: BF16
+attention on the MLA-prefill shape (batch 1, seqlen 16384, 16 heads,
+d_qk 192 / d_v 128, bhsd) is the headline value; when the FP8 path is built,
+the step also quantizes q, k and v of the GQA FP8 workload (batch 1, seqlen
+16384, 32 / 8 heads, d 128) and runs FP8 attention on it. Inputs are
+resident in HBM before timing starts. Each kernel's average duration is
+measured with HIP events on the stream it is launched on.
+
+Throughput is causal TFLOP/s = B * H * S^2 * (d_qk + d_v) / time, the
+count of the "ZYFA" README's kernel-benchmark protocol.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X published dense MFMA peaks
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def time_launches(fn, steps, warmup):
+    """Average milliseconds of fn() over `steps` back-to-back launches,
+    bracketed by events on the current stream (the stream fn launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    stop = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        start[i].record()
+        fn()
+        stop[i].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in zip(start, stop)]
+    return sum(ms) / len(ms), ms
+
+
+def cpu_baseline(seconds_budget: float):
+    """The float64 oracle on a bounded sample of the headline workload: the
+    last query rows of one (batch, head), timed on the host."""
+    import numpy as np
+    import oracle
+    from workloads import WORKLOADS
+    w = WORKLOADS[4]
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    S, dqk, dv = w.seqlen, w.d_qk, w.d_v
+    rows_done, flops, heads, t0 = 0, 0.0, 0, time.perf_counter()
+    block = 512
+    while time.perf_counter() - t0 < seconds_budget:
+        # one (batch, head) slice of the workload's shape per pass
+        q = oracle.bf16_round(rng.standard_normal((S, dqk), dtype=np.float32))[None, None]
+        k = oracle.bf16_round(rng.standard_normal((S, dqk), dtype=np.float32))[None, None]
+        v = oracle.bf16_round(rng.standard_normal((S, dv), dtype=np.float32))[None, None]
+        for r1 in range(S, 0, -block):
+            rows = np.arange(max(0, r1 - block), r1)
+            oracle.causal_attention_rows_ref(q, k, v, 0, 0, rows, layout="bhsd")
+            flops += float(np.sum(rows + 1)) * (dqk + dv) * 2.0
+            rows_done += len(rows)
+            if time.perf_counter() - t0 >= seconds_budget:
+                break
+        heads += 1
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 oracle on {rows_done} query rows ({heads} head slice(s), last rows first) of the "
+                      f"bf16 d_qk=192 S=16384 workload, {dt:.1f} s; causal FLOPs of those rows / wall time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import causal_flashattention_prefill_amd as zy
+    from workloads import WORKLOADS, generate
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    results = {}
+
+    def stage(w):
+        q, k, v = generate(w)
+        return tuple(torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
+
+    # BF16, MLA-prefill shape at 16K (headline)
+    w4 = WORKLOADS[4]
+    q, k, v = stage(w4)
+    out = torch.empty(w4.shape("q")[:-1] + (w4.d_v,), dtype=torch.bfloat16, device=dev)
+    zy.zyfa_fwd(q, k, v, out, layout=w4.layout)
+    ms, _ = time_launches(lambda: zy.zyfa_fwd(q, k, v, out, layout=w4.layout), args.steps, args.warmup)
+    results["bf16_d192_s16384"] = (w4.flops(), ms)
+    del q, k, v, out
+
+    # BF16 on the GQA d=128 16K shape (context row)
+    w3 = WORKLOADS[3]
+    q, k, v = stage(w3)
+    out = torch.empty(w3.shape("q")[:-1] + (w3.d_v,), dtype=torch.bfloat16, device=dev)
+    ms3, _ = time_launches(lambda: zy.zyfa_fwd(q, k, v, out, layout=w3.layout), args.steps, args.warmup)
+    results["bf16_d128_gqa_s16384"] = (w3.flops(), ms3)
+
+    fp8 = {}
+    try:
+        q8, qs = zy.zyfa_fp8_quantize(q)
+        k8, ks = zy.zyfa_fp8_quantize(k)
+        v8, vs = zy.zyfa_fp8_quantize(v)
+        zy.zyfa_fwd(q8, k8, v8, out, layout=w3.layout, q_descale=qs, k_descale=ks, v_descale=vs)
+        torch.cuda.synchronize()
+        msf, _ = time_launches(lambda: zy.zyfa_fwd(q8, k8, v8, out, layout=w3.layout, q_descale=qs,
+                                                   k_descale=ks, v_descale=vs), args.steps, args.warmup)
+        msq, _ = time_launches(lambda: (zy.zyfa_fp8_quantize(q, q8, qs), zy.zyfa_fp8_quantize(k, k8, ks),
+                                        zy.zyfa_fp8_quantize(v, v8, vs)), args.steps, args.warmup)
+        fp8 = {"fp8_d128_gqa_s16384_tflops": w3.flops() / (msf * 1e-3) / 1e12,
+               "fp8_d128_gqa_s16384_ms": msf, "fp8_quantize_qkv_ms": msq}
+    except zy.ZyfaError as e:
+        fp8 = {"fp8": f"not available: {e}"}
+    del q, k, v, out
+
+    flops, ms = results["bf16_d192_s16384"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    t3 = results["bf16_d128_gqa_s16384"][0] / (results["bf16_d128_gqa_s16384"][1] * 1e-3) / 1e12
+    line = {
+        "metric": "causal prefill attention TFLOP/s (bf16, fp8) at 16K tokens; % of MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal MLA-prefill form: batch 1, seqlen 16384, nheads 16 = nheads_k, d_qk 192, d_v 128, "
+                        "bhsd, q/k/v N(0,1) bf16",
+            "global_batch": 1, "seq_len": 16384, "parallelism": "none (1 GPU)",
+            "pct_of_bf16_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2),
+            "bf16_d128_gqa_s16384_tflops": round(t3, 2),
+            **{k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in fp8.items()},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS["bf16"], 4), "traffic": None},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+"""Causal prefill attention for MI355X (gfx950): Python binding of libzyfa.so.
+
+A thin ctypes layer over the C ABI in include/zyfa.h, with the same names.
+It only marshals arguments: torch tensors supply device memory and the
+current stream, and every step of the computation runs in the library's HIP
+kernels. There is no fallback: if libzyfa.so is missing or cannot be loaded,
+importing the binding succeeds but every call raises.
+
+    out, lse = zyfa_fwd(q, k, v, return_lse=True)             # bf16
+    q8, qs = zyfa_fp8_quantize(q)                               # fp8 + device descale
+    out = zyfa_fwd(q8, k8, v8, q_descale=qs, k_descale=ks, v_descale=vs)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzyfa.so")
+
+LAYOUTS = {"bshd": 0, "bhsd": 1}
+DTYPE_BF16, DTYPE_FP8, DTYPE_FP32 = 0, 1, 2
+
+ZYFA_OK = 0
+STATUS = {
+    "ZYFA_ERR_NULL": -1, "ZYFA_ERR_SHAPE": -2, "ZYFA_ERR_HEADDIM": -3, "ZYFA_ERR_GQA": -4,
+    "ZYFA_ERR_DTYPE": -5, "ZYFA_ERR_LAYOUT": -6, "ZYFA_ERR_DESCALE": -7, "ZYFA_ERR_CAPTURE": -8,
+    "ZYFA_ERR_HIP": -9, "ZYFA_ERR_RANGE": -10, "ZYFA_ERR_ALIGN": -11,
+}
+
+_lib = None
+_lib_err: Optional[str] = None
+
+
+class ZyfaError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({zyfa_status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it is not built or cannot load)."""
+    global _lib, _lib_err
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libzyfa.so not built ({LIB_PATH}); run causal_flashattention_prefill_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
+    fwd_args = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp]
+    L.zyfa_fwd.argtypes = fwd_args + [vp]
+    L.zyfa_fwd.restype = i
+    L.zyfa_fwd_ex.argtypes = fwd_args + [f, vp]
+    L.zyfa_fwd_ex.restype = i
+    L.zyfa_prepare.argtypes = [i, i, i, i, i, i, i, i, i, vp]
+    L.zyfa_prepare.restype = i
+    L.zyfa_fp8_quantize.argtypes = [vp, i, ll, vp, vp, vp]
+    L.zyfa_fp8_quantize.restype = i
+    L.zyfa_status_string.argtypes = [i]
+    L.zyfa_status_string.restype = ctypes.c_char_p
+    L.zyfa_release.argtypes = []
+    L.zyfa_release.restype = None
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.zyfa_plan_jobs.argtypes = [i, i, i, i, i, i, i, ip, ip, ip, vp, ll]
+    L.zyfa_plan_jobs.restype = i
+    _lib = L
+    return L
+
+
+def zyfa_status_string(status: int) -> str:
+    return lib().zyfa_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != ZYFA_OK:
+        raise ZyfaError(rc, what)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return DTYPE_FP8
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def _dims(q, k, v, layout: str):
+    if layout == "bshd":
+        B, S, H, dqk = q.shape
+        Hk = k.shape[2]
+    else:
+        B, H, S, dqk = q.shape
+        Hk = k.shape[1]
+    return B, S, H, Hk, dqk, v.shape[-1]
+
+
+def zyfa_fwd(q, k, v, out=None, lse=None, *, layout: str = "bshd", return_lse: bool = False,
+             q_descale=None, k_descale=None, v_descale=None, softmax_scale: Optional[float] = None,
+             stream=None):
+    """Causal forward attention. q, k, v: contiguous CUDA tensors (bf16, or
+    float8_e4m3fn / uint8 codes with fp32 device descales). Returns out, or
+    (out, lse) when return_lse (or an lse tensor is passed)."""
+    import torch
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k and v must be contiguous")
+    B, S, H, Hk, dqk, dv = _dims(q, k, v, layout)
+    dt = _dtype_code(q)
+    if out is None:
+        shape = (B, S, H, dv) if layout == "bshd" else (B, H, S, dv)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    L = lib()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S, H, Hk, dqk, dv, LAYOUTS[layout], dt,
+            _ptr(q_descale), _ptr(k_descale), _ptr(v_descale))
+    if softmax_scale is None:
+        rc = L.zyfa_fwd(*args, _stream(stream))
+    else:
+        rc = L.zyfa_fwd_ex(*args, float(softmax_scale), _stream(stream))
+    _check(rc, "zyfa_fwd")
+    return (out, lse) if lse is not None else out
+
+
+def zyfa_prepare(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout="bshd", dtype=DTYPE_BF16, with_lse=False,
+                 stream=None) -> None:
+    _check(lib().zyfa_prepare(batch, seqlen, nheads, nheads_k, d_qk, d_v, LAYOUTS[layout], dtype, int(with_lse),
+                              _stream(stream)), "zyfa_prepare")
+
+
+def zyfa_fp8_quantize(x, x8=None, descale=None, stream=None):
+    """Per-tensor power-of-two e4m3fn quantization of a bf16 or fp32 CUDA
+    tensor. Returns (codes as torch.float8_e4m3fn, descale as a 1-element fp32
+    CUDA tensor)."""
+    import torch
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    xd = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}.get(x.dtype)
+    if xd is None:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if x8 is None:
+        x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    if descale is None:
+        descale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().zyfa_fp8_quantize(_ptr(x), xd, x.numel(), _ptr(x8), _ptr(descale), _stream(stream)),
+           "zyfa_fp8_quantize")
+    return x8, descale
+
+
+def zyfa_release() -> None:
+    lib().zyfa_release()
+
+
+def zyfa_plan_jobs(batch, seqlen, nheads, nheads_k, d_qk=128, dtype=DTYPE_BF16, num_cus=256):
+    """Host-only job table: returns (tile_q, num_wgs, jobs_per_wg, table) with
+    table an int array of shape (jobs_per_wg, num_wgs, 2)."""
+    import numpy as np
+    L = lib()
+    tq, nw, jp = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(L.zyfa_plan_jobs(batch, seqlen, nheads, nheads_k, d_qk, dtype, num_cus, ctypes.byref(tq),
+                            ctypes.byref(nw), ctypes.byref(jp), None, 0), "zyfa_plan_jobs")
+    table = np.empty((jp.value, nw.value, 2), dtype=np.int32)
+    _check(L.zyfa_plan_jobs(batch, seqlen, nheads, nheads_k, d_qk, dtype, num_cus, ctypes.byref(tq),
+                            ctypes.byref(nw), ctypes.byref(jp), table.ctypes.data, table.size), "zyfa_plan_jobs")
+    return tq.value, nw.value, jp.value, table

@@ -1,0 +1,284 @@
+// Host side of the C ABI (include/zyfa.h): argument checks, the per-shape
+// plan cache, and kernel launches. Nothing here computes attention; every
+// step of the path runs in the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "../../include/zyfa.h"
+#include "plan.h"
+#include "zyfa_internal.h"
+
+namespace zyfa {
+namespace {
+
+struct PlanKey {
+  int device, batch, seqlen, nheads, nheads_k, d_qk, dtype;
+  bool operator<(const PlanKey& o) const {
+    return std::tie(device, batch, seqlen, nheads, nheads_k, d_qk, dtype) <
+           std::tie(o.device, o.batch, o.seqlen, o.nheads, o.nheads_k, o.d_qk, o.dtype);
+  }
+};
+
+struct Plan {
+  int2* jobs = nullptr;  // device copy of the job table
+  int num_wgs = 0;
+  int jobs_per_wg = 0;
+  int n_qtiles = 0;
+  int tile_q = 0;
+};
+
+struct DeviceScratch {
+  unsigned* amax = nullptr;  // partial maxima of the FP8 quantizer
+};
+
+std::mutex g_mu;
+std::map<PlanKey, Plan> g_plans;
+std::map<int, DeviceScratch> g_scratch;
+std::map<int, int> g_num_cus;
+
+int current_device(int* dev) {
+  return hipGetDevice(dev) == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
+}
+
+int num_cus(int dev) {
+  auto it = g_num_cus.find(dev);
+  if (it != g_num_cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  g_num_cus[dev] = n;
+  return n;
+}
+
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+
+int check_shape(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype) {
+  if (batch <= 0 || seqlen <= 0 || nheads <= 0 || nheads_k <= 0) return ZYFA_ERR_SHAPE;
+  if (!((d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128))) return ZYFA_ERR_HEADDIM;
+  if (nheads % nheads_k != 0) return ZYFA_ERR_GQA;
+  if (dtype != ZYFA_DTYPE_BF16 && dtype != ZYFA_DTYPE_FP8_E4M3FN) return ZYFA_ERR_DTYPE;
+  if (layout != ZYFA_LAYOUT_BSHD && layout != ZYFA_LAYOUT_BHSD) return ZYFA_ERR_LAYOUT;
+  return ZYFA_OK;
+}
+
+// Finds or builds the plan; caller holds g_mu.
+int get_plan(const PlanKey& key, hipStream_t stream, const Plan** out) {
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) {
+    *out = &it->second;
+    return ZYFA_OK;
+  }
+  if (stream_capturing(stream)) return ZYFA_ERR_CAPTURE;
+  const int tq = tile_q_rows(key.d_qk, key.dtype);
+  JobTable t = build_job_table(key.batch, key.seqlen, key.nheads, key.nheads_k, tq, num_cus(key.device));
+  Plan p;
+  p.num_wgs = t.num_wgs;
+  p.jobs_per_wg = t.jobs_per_wg;
+  p.n_qtiles = t.n_qtiles;
+  p.tile_q = t.tile_q;
+  const size_t bytes = t.entries.size() * sizeof(int32_t);
+  if (hipMalloc(&p.jobs, bytes) != hipSuccess) return ZYFA_ERR_HIP;
+  if (hipMemcpy(p.jobs, t.entries.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    hipFree(p.jobs);
+    return ZYFA_ERR_HIP;
+  }
+  *out = &(g_plans[key] = p);
+  return ZYFA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Strides (elements) of a (batch, heads, seqlen, dim) view of a contiguous tensor.
+void strides(int layout, int seqlen, int heads, int dim, long long* sb, long long* sh, long long* ss) {
+  if (layout == ZYFA_LAYOUT_BSHD) {
+    *sb = (long long)seqlen * heads * dim;
+    *sh = dim;
+    *ss = (long long)heads * dim;
+  } else {
+    *sb = (long long)heads * seqlen * dim;
+    *sh = (long long)seqlen * dim;
+    *ss = dim;
+  }
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen,
+             int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale,
+             const float* k_descale, const float* v_descale, float softmax_scale, void* stream_) {
+  int rc = check_shape(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype);
+  if (rc) return rc;
+  if (!q || !k || !v || !out) return ZYFA_ERR_NULL;
+  if (dtype == ZYFA_DTYPE_FP8_E4M3FN && (!q_descale || !k_descale || !v_descale)) return ZYFA_ERR_DESCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ZYFA_ERR_ALIGN;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const int esz = dtype == ZYFA_DTYPE_BF16 ? 2 : 1;
+
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  const Plan* plan = nullptr;
+  PlanKey key{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype};
+  if ((rc = get_plan(key, stream, &plan))) return rc;
+
+  AttnArgs a{};
+  a.q.ptr = q;
+  a.k.ptr = k;
+  a.v.ptr = v;
+  strides(layout, seqlen, nheads, d_qk, &a.q.stride_b, &a.q.stride_h, &a.q.stride_s);
+  strides(layout, seqlen, nheads_k, d_qk, &a.k.stride_b, &a.k.stride_h, &a.k.stride_s);
+  strides(layout, seqlen, nheads_k, d_v, &a.v.stride_b, &a.v.stride_h, &a.v.stride_s);
+  strides(layout, seqlen, nheads, d_v, &a.o_stride_b, &a.o_stride_h, &a.o_stride_s);
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.nheads = nheads;
+  a.nheads_k = nheads_k;
+  a.n_qtiles = plan->n_qtiles;
+  a.jobs_per_wg = plan->jobs_per_wg;
+  a.jobs = plan->jobs;
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)d_qk);
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  // Byte extent of one (batch, head) slice from its base: rows past seqlen
+  // fall outside it and read as zero. Offsets up to the padded length must
+  // fit in 31 bits.
+  const long long s_pad = (long long)plan->n_qtiles * plan->tile_q;
+  auto extent = [&](long long ss, int dim) { return ((long long)(seqlen - 1) * ss + dim) * esz; };
+  auto reach = [&](long long ss, int dim) { return ((s_pad + 64) * ss + dim) * esz; };
+  const long long lim = 0x7FFFFFFFll;
+  if (reach(a.q.stride_s, d_qk) > lim || reach(a.k.stride_s, d_qk) > lim || reach(a.v.stride_s, d_v) > lim)
+    return ZYFA_ERR_RANGE;
+  a.q_bytes = (unsigned)extent(a.q.stride_s, d_qk);
+  a.k_bytes = (unsigned)extent(a.k.stride_s, d_qk);
+  a.v_bytes = (unsigned)extent(a.v.stride_s, d_v);
+
+  hipError_t e;
+  if (dtype == ZYFA_DTYPE_BF16)
+    e = launch_attn_bf16(a, d_qk, lse != nullptr, plan->num_wgs, stream);
+  else
+    e = launch_attn_fp8(a, d_qk, lse != nullptr, plan->num_wgs, stream);
+  return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace zyfa
+
+using namespace zyfa;
+
+extern "C" {
+
+int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen, int nheads,
+             int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale, const float* k_descale,
+             const float* v_descale, void* stream) {
+  return fwd_impl(q, k, v, out, lse, batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype, q_descale, k_descale,
+                  v_descale, 0.f, stream);
+}
+
+int zyfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen,
+                int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale,
+                const float* k_descale, const float* v_descale, float softmax_scale, void* stream) {
+  return fwd_impl(q, k, v, out, lse, batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype, q_descale, k_descale,
+                  v_descale, softmax_scale, stream);
+}
+
+int zyfa_prepare(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype,
+                 int with_lse, void* stream) {
+  (void)with_lse;
+  int rc = check_shape(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype);
+  if (rc) return rc;
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  const Plan* plan = nullptr;
+  PlanKey key{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype};
+  return get_plan(key, reinterpret_cast<hipStream_t>(stream), &plan);
+}
+
+int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale, void* stream_) {
+  if (x_dtype != ZYFA_DTYPE_BF16 && x_dtype != ZYFA_DTYPE_FP32) return ZYFA_ERR_DTYPE;
+  if (numel < 0) return ZYFA_ERR_SHAPE;
+  if (!descale || (numel > 0 && (!x || !x8))) return ZYFA_ERR_NULL;
+  if (numel > 0 && (!aligned16(x) || !aligned16(x8))) return ZYFA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(descale) & 3u) return ZYFA_ERR_ALIGN;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceScratch& sc = g_scratch[dev];
+  if (!sc.amax) {
+    if (stream_capturing(stream)) return ZYFA_ERR_CAPTURE;
+    if (hipMalloc(&sc.amax, sizeof(unsigned) * quantize_scratch_slots()) != hipSuccess) {
+      sc.amax = nullptr;
+      return ZYFA_ERR_HIP;
+    }
+  }
+  hipError_t e = launch_fp8_quantize(x, x_dtype == ZYFA_DTYPE_BF16 ? 0 : 2, numel, x8, descale, sc.amax,
+                                     quantize_scratch_slots(), stream);
+  return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
+}
+
+const char* zyfa_status_string(int status) {
+  switch (status) {
+    case ZYFA_OK: return "ok";
+    case ZYFA_ERR_NULL: return "a required pointer is NULL";
+    case ZYFA_ERR_SHAPE: return "batch, seqlen, nheads and nheads_k must be positive (numel non-negative)";
+    case ZYFA_ERR_HEADDIM: return "unsupported head dims: (d_qk, d_v) must be (128, 128) or (192, 128)";
+    case ZYFA_ERR_GQA: return "nheads must be a multiple of nheads_k";
+    case ZYFA_ERR_DTYPE: return "unknown dtype";
+    case ZYFA_ERR_LAYOUT: return "unknown layout (0 = bshd, 1 = bhsd)";
+    case ZYFA_ERR_DESCALE: return "FP8 inputs need q, k and v descale pointers";
+    case ZYFA_ERR_CAPTURE: return "the plan for this shape must be built (zyfa_prepare) before graph capture";
+    case ZYFA_ERR_HIP: return "a HIP runtime call failed";
+    case ZYFA_ERR_RANGE: return "a (batch, head) slice is too large for 32-bit offsets";
+    case ZYFA_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+void zyfa_release(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int cur = 0;
+  hipGetDevice(&cur);
+  for (auto& kv : g_plans) {
+    hipSetDevice(kv.first.device);
+    hipFree(kv.second.jobs);
+  }
+  g_plans.clear();
+  for (auto& kv : g_scratch) {
+    hipSetDevice(kv.first);
+    if (kv.second.amax) hipFree(kv.second.amax);
+  }
+  g_scratch.clear();
+  hipSetDevice(cur);
+}
+
+int zyfa_plan_jobs(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int dtype, int num_cus_, int* out_tile_q,
+                   int* out_num_wgs, int* out_jobs_per_wg, int* table, long long table_capacity) {
+  int rc = check_shape(batch, seqlen, nheads, nheads_k, d_qk, 128, ZYFA_LAYOUT_BSHD, dtype);
+  if (rc) return rc;
+  if (num_cus_ <= 0) return ZYFA_ERR_SHAPE;
+  if (!out_tile_q || !out_num_wgs || !out_jobs_per_wg) return ZYFA_ERR_NULL;
+  JobTable t = build_job_table(batch, seqlen, nheads, nheads_k, tile_q_rows(d_qk, dtype), num_cus_);
+  *out_tile_q = t.tile_q;
+  *out_num_wgs = t.num_wgs;
+  *out_jobs_per_wg = t.jobs_per_wg;
+  if (table) {
+    if (table_capacity < (long long)t.entries.size()) return ZYFA_ERR_SHAPE;
+    for (size_t i = 0; i < t.entries.size(); ++i) table[i] = t.entries[i];
+  }
+  return ZYFA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,289 @@
+// Causal forward attention, BF16 inputs, for gfx950 (CDNA4).
+//
+// What is computed: "ZYFA" README, Usage and Supported configurations
+// (causal, seqlen_q == seqlen_k, GQA head sharing, natural-log LSE, BF16
+// output, zero padding to the query-tile multiple).
+//
+// Structure (one workgroup = 8 waves = 512 threads, persistent):
+//  - A job is a pair of 256-row query tiles (i, n-1-i) of one (batch, head)
+//    (README, Kernel design: work distribution). Each wave owns 32 query
+//    rows (two 16-row groups) for the whole key loop.
+//  - Keys stream in 64-key tiles through a two-stage LDS ring; global loads
+//    of tile t+1 are issued before the MFMA work on tile t.
+//  - Scores are computed transposed, S^T = K Q^T, with K as the MFMA A
+//    operand (README, Kernel design: transposed scores), using
+//    v_mfma_f32_16x16x32_bf16. Lane (g, n) (g = lane/16, n = lane%16) then
+//    holds, for query column n, the keys 16*kb + 4*g + i of each 16-key
+//    block kb: a lane owns part of one query row, and P goes from registers
+//    straight into the PV product as the B operand.
+//  - O^T += V^T P^T with V^T read from LDS by ds_read_b64_tr_b16, which
+//    transposes 16-bit values during the read, so V is stored in LDS as it
+//    arrives from memory.
+//  - Online softmax in base 2 (log2(e) folded into the scale) with a lazy
+//    reference maximum: the reference moves only when some score passes it by
+//    kTau; one wave-wide ballot decides, and the rescale runs out of line
+//    (README, Kernel design: lazy rescaling).
+//  - The row sum is an fp32 sum of the unrounded probabilities, so that the
+//    LSE holds to ~1e-7 relative; P is rounded to bf16 (RNE) for the MFMA.
+//  - Every conversion rounds to nearest even (README, Kernel design).
+#include "device_common.h"
+#include "zyfa_internal.h"
+
+namespace zyfa {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kTileQ = 256;
+constexpr int kTileK = 64;
+constexpr float kTau = 8.0f;           // lazy-rescale threshold, log2 units
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <int DQK, bool WITH_LSE>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnArgs a) {
+  constexpr int DV = 128;
+  constexpr int KCH = DQK / 8;                 // 16-byte chunks per K row
+  constexpr int VCH = DV / 8;                  // 16-byte chunks per V row
+  constexpr int KPITCH = DQK * 2;              // bytes per K row in LDS
+  constexpr int VPITCH = DV * 2;
+  constexpr int KSWZ = (KCH % 16 == 0) ? 15 : 7;
+  constexpr int KBYTES = kTileK * KPITCH;
+  constexpr int VBYTES = kTileK * VPITCH;
+  constexpr int STAGE = KBYTES + VBYTES;
+  constexpr int NC = DQK / 32;                 // MFMA k-steps over d_qk
+  constexpr int KLD = kTileK * KCH / kThreads; // 16-byte K loads per thread per tile
+  constexpr int VLD = kTileK * VCH / kThreads;
+  static_assert(KLD * kThreads == kTileK * KCH && VLD * kThreads == kTileK * VCH, "tile split");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int S = a.seqlen;
+  const float sl2 = a.scale_log2;
+
+  for (int it = 0; it < a.jobs_per_wg; ++it) {
+    const int2 job = a.jobs[it * (int)gridDim.x + (int)blockIdx.x];
+    if (job.x < 0) break;
+    const int b = job.x / a.nheads;
+    const int h = job.x - b * a.nheads;
+    const int hk = (int)(((long long)h * a.nheads_k) / a.nheads);
+
+    const char* qbase = (const char*)a.q.ptr + 2 * (b * a.q.stride_b + h * a.q.stride_h);
+    const char* kbase = (const char*)a.k.ptr + 2 * (b * a.k.stride_b + hk * a.k.stride_h);
+    const char* vbase = (const char*)a.v.ptr + 2 * (b * a.v.stride_b + hk * a.v.stride_h);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, a.q_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, a.k_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, a.v_bytes);
+    const int qrs = (int)(2 * a.q.stride_s);
+    const int krs = (int)(2 * a.k.stride_s);
+    const int vrs = (int)(2 * a.v.stride_s);
+
+    const int tA = job.y;
+    const int tB = a.n_qtiles - 1 - job.y;
+    const int ntiles = (tA == tB) ? 1 : 2;
+    for (int tt = 0; tt < ntiles; ++tt) {
+      const int qt = tt == 0 ? tA : tB;
+      const int q0 = qt * kTileQ;
+      const int qw0 = q0 + wave * 32;
+      const int qend = min(q0 + kTileQ, S);
+      const int n_kt = (qend - 1) / kTileK + 1;
+      const int kt_w = (qw0 < S) ? min((qw0 + 31) / kTileK, n_kt - 1) : -1;
+
+      // Q fragments, MFMA B operand: lane (g, n) holds q[row n][32c + 8g .. +7].
+      bf16x8 qf[2][NC];
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          qf[qg][c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (qw0 + 16 * qg + n) * qrs + (32 * c + 8 * g) * 2));
+
+      f32x4 o[2][8];
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float mref[2] = {neg_inf(), neg_inf()};
+      float lsum[2] = {0.f, 0.f};
+
+      u32x4 kr[KLD], vr[VLD];
+      auto load_kv = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < KLD; ++u) {
+          const int id = tid + kThreads * u, row = id / KCH, x = id % KCH;
+          kr[u] = buf_load16(rk, (kt * kTileK + row) * krs + x * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < VLD; ++u) {
+          const int id = tid + kThreads * u, row = id / VCH, x = id % VCH;
+          vr[u] = buf_load16(rv, (kt * kTileK + row) * vrs + x * 16);
+        }
+      };
+      // K rows keep their 16-byte chunks XOR-swizzled by row so that the 16
+      // lanes reading one chunk column of 16 rows hit distinct banks; V rows
+      // are swizzled by even values so the 8-byte halves the transposing
+      // read needs stay intact.
+      auto store_kv = [&](int st) {
+        char* ks = smem + st * STAGE;
+#pragma unroll
+        for (int u = 0; u < KLD; ++u) {
+          const int id = tid + kThreads * u, row = id / KCH, x = id % KCH;
+          lds_store(ks + row * KPITCH + ((x ^ (row & KSWZ)) << 4), kr[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < VLD; ++u) {
+          const int id = tid + kThreads * u, row = id / VCH, x = id % VCH;
+          lds_store(ks + KBYTES + row * VPITCH + ((x ^ ((row & 7) << 1)) << 4), vr[u]);
+        }
+      };
+
+      load_kv(0);
+      store_kv(0);
+      __syncthreads();
+
+      for (int kt = 0; kt < n_kt; ++kt) {
+        const int st = kt & 1;
+        if (kt + 1 < n_kt) load_kv(kt + 1);
+        if (kt <= kt_w) {
+          const char* ks = smem + st * STAGE;
+          const char* vs = ks + KBYTES;
+          // ---- S^T = K Q^T
+          f32x4 s[2][4];
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) s[qg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              const int row = 16 * kb + n;
+              const int x = 4 * c + g;
+              const bf16x8 kf = lds_load<bf16x8>(ks + row * KPITCH + ((x ^ (row & KSWZ)) << 4));
+#pragma unroll
+              for (int qg = 0; qg < 2; ++qg)
+                s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qg][c], s[qg][kb], 0, 0, 0);
+            }
+          // ---- scale, causal mask (diagonal tiles only), lazy max
+          const int kbase = kt * kTileK;
+          const bool diag = kbase + kTileK - 1 > qw0;
+          float mx[2];
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            float m = neg_inf();
+            const int q = qw0 + 16 * qg + n;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                float v = s[qg][kb][i] * sl2;
+                if (diag && (kbase + 16 * kb + 4 * g + i > q)) v = neg_inf();
+                s[qg][kb][i] = v;
+                m = fmaxf(m, v);
+              }
+            mx[qg] = m;
+          }
+          const bool need = (mx[0] > mref[0] + kTau) || (mx[1] > mref[1] + kTau);
+          if (wave_any(need)) {
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg) {
+              float rm = fmaxf(mx[qg], __shfl_xor(mx[qg], 16));
+              rm = fmaxf(rm, __shfl_xor(rm, 32));
+              const float mn = fmaxf(mref[qg], rm);
+              const float f = fast_exp2(mref[qg] - mn);
+              lsum[qg] *= f;
+#pragma unroll
+              for (int db = 0; db < 8; ++db) o[qg][db] *= f;
+              mref[qg] = mn;
+            }
+          }
+          // ---- P = exp2(s - mref), fp32 row sum, RNE pack to bf16
+          // Operands are assembled as whole 32-bit words (two bf16 each):
+          // building them element by element from 16-bit values has been
+          // lowered incorrectly (every slot took the first element).
+          bf16x8 pb[2][2];
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            float ls = 0.f;
+            u32x4 w[2];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              f32x4 p;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                p[i] = fast_exp2(s[qg][kb][i] - mref[qg]);
+                ls += p[i];
+              }
+              w[kb >> 1][2 * (kb & 1) + 0] = pack_bf16x2(p[0], p[1]);
+              w[kb >> 1][2 * (kb & 1) + 1] = pack_bf16x2(p[2], p[3]);
+            }
+            pb[qg][0] = __builtin_bit_cast(bf16x8, w[0]);
+            pb[qg][1] = __builtin_bit_cast(bf16x8, w[1]);
+            lsum[qg] += ls;
+          }
+          // ---- O^T += V^T P^T
+#pragma unroll
+          for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+              u32x2 t[2];
+#pragma unroll
+              for (int hf = 0; hf < 2; ++hf) {
+                const int row = 32 * kc + 16 * hf + 4 * g + (n >> 2);
+                const int dcol = 16 * db + 4 * (n & 3);
+                const int x = dcol >> 3;
+                const char* p = vs + row * VPITCH + ((x ^ ((row & 7) << 1)) << 4) + ((dcol >> 2) & 1) * 8;
+                t[hf] = __builtin_bit_cast(u32x2, lds_read_tr16(p));
+              }
+              const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{t[0][0], t[0][1], t[1][0], t[1][1]});
+#pragma unroll
+              for (int qg = 0; qg < 2; ++qg)
+                o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qg][kc], o[qg][db], 0, 0, 0);
+            }
+        }
+        if (kt + 1 < n_kt) store_kv(st ^ 1);
+        __syncthreads();
+      }
+
+      // ---- epilogue: O / l (RNE to bf16), LSE = ln2 * (m + log2 l)
+      if (kt_w >= 0) {
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+          float lt = lsum[qg] + __shfl_xor(lsum[qg], 16);
+          lt += __shfl_xor(lt, 32);
+          const float inv = 1.0f / lt;
+          const int q = qw0 + 16 * qg + n;
+          if (q < S) {
+            __bf16* orow = (__bf16*)a.out + (b * a.o_stride_b + h * a.o_stride_h + (long long)q * a.o_stride_s);
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+              const u32x2 w = {pack_bf16x2(o[qg][db][0] * inv, o[qg][db][1] * inv),
+                               pack_bf16x2(o[qg][db][2] * inv, o[qg][db][3] * inv)};
+              *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g) = w;
+            }
+            if (WITH_LSE && g == 0)
+              a.lse[((long long)b * a.nheads + h) * S + q] = (mref[qg] + fast_log2(lt)) * kLn2;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int d_qk, bool with_lse, int grid, hipStream_t s) {
+  const dim3 gd(grid), bd(kThreads);
+  if (d_qk == 128) {
+    if (with_lse) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), gd, bd, 0, s, a);
+  } else {
+    if (with_lse) hipLaunchKernelGGL((attn_fwd_bf16_kernel<192, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<192, false>), gd, bd, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace zyfa

@@ -1,0 +1,75 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, buffer
+// resources (range-checked loads that return zero past the end), LDS access
+// and the few CDNA4 builtins the kernels use.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace zyfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+
+// Word 3 of a gfx9-family buffer resource: 32-bit data format, raw access.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, kBufferWord3);
+}
+
+// 16-byte load at a byte offset; returns zeros when the offset is past the
+// resource's extent (this is how rows past seqlen read as zero padding).
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+template <class T>
+__device__ __forceinline__ T lds_load(const char* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+template <class T>
+__device__ __forceinline__ void lds_store(char* p, const T& v) {
+  *reinterpret_cast<T*>(p) = v;
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, the lanes' 8-byte reads
+// form a 4 x 16 block of 16-bit values (row r from lanes 4r..4r+3); lane i
+// receives column i, rows 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const_cast<char*>(p)));
+}
+
+// ds_read_b64_tr_b8: within each 16-lane group, the lanes' 8-byte reads
+// form an 8 x 16 block of bytes (row r from lanes 2r, 2r+1); lane i receives
+// column i, rows 0..7.
+__device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(const_cast<char*>(p)));
+}
+
+// Two floats -> two bf16 (round to nearest even) in one 32-bit word, low
+// half first (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+}  // namespace zyfa

@@ -1,0 +1,38 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace zyfa {
+
+// One (batch, head) slice of a tensor: base offset strides in elements.
+struct TensorDesc {
+  const void* ptr;
+  long long stride_b;   // elements between batches
+  long long stride_h;   // elements between heads
+  long long stride_s;   // elements between positions (rows)
+};
+
+struct AttnArgs {
+  TensorDesc q, k, v;
+  void* out;
+  long long o_stride_b, o_stride_h, o_stride_s;
+  float* lse;                 // may be null
+  int batch, seqlen, nheads, nheads_k;
+  int n_qtiles;               // query tiles per (batch, head)
+  int jobs_per_wg;
+  const int2* jobs;           // [jobs_per_wg][gridDim.x]
+  float scale_log2;           // softmax_scale * log2(e)
+  const float* q_descale;     // fp8 only
+  const float* k_descale;
+  const float* v_descale;
+  unsigned q_bytes, k_bytes, v_bytes;  // extent of one (b, h) slice, bytes from its base
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int d_qk, bool with_lse, int grid, hipStream_t s);
+hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, int grid, hipStream_t s);
+hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
+                               unsigned* scratch_amax, int scratch_slots, hipStream_t s);
+int quantize_scratch_slots();
+
+}  // namespace zyfa

@@ -1,0 +1,153 @@
+/*
+ * zyfa.h - C ABI of the causal prefill attention library for MI355X (gfx950).
+ *
+ * What the library computes is defined on the "ZYFA" README (GitHub page of
+ * Zyphra/zyfa), sections Usage and Supported configurations: the causal
+ * forward attention pass of LLM prefill (seqlen_q == seqlen_k),
+ *     out[i] = sum_{j<=i} softmax_j(scale * <q_i, k_j>) * v_j,
+ * with an optional natural-log log-sum-exp per row, for BF16 inputs or FP8
+ * e4m3fn inputs with one descale per tensor, for MHA, GQA and MQA, and for
+ * head dims d_qk = d_v = 128 or d_qk = 192 with d_v = 128. The output is
+ * always BF16.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers to contiguous tensors owned by the
+ *    caller; the library never frees or retains them past the call.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream). Work is
+ *    enqueued asynchronously; no call waits on the host in the steady state.
+ *  - Every call returns ZYFA_OK (0) or a negative ZYFA_ERR_* status and
+ *    never throws. Argument checks happen before anything is enqueued.
+ */
+#ifndef ZYFA_H
+#define ZYFA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum zyfa_status {
+  ZYFA_OK = 0,
+  ZYFA_ERR_NULL = -1,      /* a required pointer is NULL */
+  ZYFA_ERR_SHAPE = -2,     /* batch, seqlen, nheads or nheads_k <= 0, or numel < 0 */
+  ZYFA_ERR_HEADDIM = -3,   /* (d_qk, d_v) not (128, 128) or (192, 128) */
+  ZYFA_ERR_GQA = -4,       /* nheads is not a multiple of nheads_k */
+  ZYFA_ERR_DTYPE = -5,     /* unknown dtype enum */
+  ZYFA_ERR_LAYOUT = -6,    /* unknown layout enum */
+  ZYFA_ERR_DESCALE = -7,   /* FP8 call without all three descale pointers */
+  ZYFA_ERR_CAPTURE = -8,   /* a per-shape plan must be built while the stream is capturing */
+  ZYFA_ERR_HIP = -9,       /* a HIP runtime call failed (launch, allocation, copy) */
+  ZYFA_ERR_RANGE = -10,    /* one (batch, head) slice spans more than 2^31 bytes */
+  ZYFA_ERR_ALIGN = -11     /* a tensor pointer is not 16-byte aligned */
+};
+
+enum zyfa_layout {
+  ZYFA_LAYOUT_BSHD = 0,    /* (batch, seqlen, heads, head_dim) */
+  ZYFA_LAYOUT_BHSD = 1     /* (batch, heads, seqlen, head_dim) */
+};
+
+enum zyfa_dtype {
+  ZYFA_DTYPE_BF16 = 0,
+  ZYFA_DTYPE_FP8_E4M3FN = 1,  /* OCP e4m3fn: 4 exponent bits (bias 7), 3 mantissa bits, max 448 */
+  ZYFA_DTYPE_FP32 = 2         /* accepted by zyfa_fp8_quantize as its input only */
+};
+
+/*
+ * zyfa_fwd - causal forward attention ("ZYFA" README: Usage; Supported
+ * configurations).
+ *
+ *  q    [batch, seqlen, nheads,   d_qk] (bshd) or [batch, nheads,   seqlen, d_qk] (bhsd)
+ *  k    [batch, seqlen, nheads_k, d_qk] or [batch, nheads_k, seqlen, d_qk]
+ *  v    [batch, seqlen, nheads_k, d_v ] or [batch, nheads_k, seqlen, d_v ]
+ *  out  q's layout with head dim d_v, always bf16, written for real rows only.
+ *  lse  NULL, or fp32 [batch, nheads, seqlen]: natural-log log-sum-exp of
+ *       each row of scaled scores. For FP8 it is taken from the same rounded
+ *       probabilities that multiply V (README, Accuracy).
+ *  dtype ZYFA_DTYPE_BF16 (q, k, v bf16) or ZYFA_DTYPE_FP8_E4M3FN (q, k, v
+ *       e4m3fn codes). For FP8, q_descale/k_descale/v_descale each point to
+ *       ONE positive normal fp32 value in device memory; the kernel reads and
+ *       applies them itself, and does not check them (README, Usage). They
+ *       are ignored (may be NULL) for BF16.
+ *  Query head h uses KV head floor(h * nheads_k / nheads) (consecutive
+ *  query heads share a KV head). The softmax scale is 1/sqrt(d_qk).
+ *  Any seqlen >= 1 works: rows past seqlen read as zeros up to the kernel's
+ *  query-tile multiple, which is exact for causal attention (README, Usage).
+ *  The first call for a shape builds a plan (job table) with a blocking
+ *  host-to-device copy; call zyfa_prepare first if the call is to be
+ *  captured into a graph.
+ */
+int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v,
+             int layout, int dtype,
+             const float* q_descale, const float* k_descale, const float* v_descale,
+             void* stream);
+
+/* zyfa_fwd with an explicit softmax scale (flash-attn's softmax_scale
+ * argument, README: Differences from flash-attn); softmax_scale <= 0 selects
+ * 1/sqrt(d_qk). */
+int zyfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v,
+                int layout, int dtype,
+                const float* q_descale, const float* k_descale, const float* v_descale,
+                float softmax_scale, void* stream);
+
+/*
+ * zyfa_prepare - build (or find) the per-shape plan ahead of time so that a
+ * later zyfa_fwd with the same shape allocates nothing and copies nothing
+ * from the host (README, Usage: run each new shape once before capturing).
+ * Returns ZYFA_ERR_CAPTURE if the plan is missing and `stream` is capturing.
+ */
+int zyfa_prepare(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v,
+                 int layout, int dtype, int with_lse, void* stream);
+
+/*
+ * zyfa_fp8_quantize - per-tensor power-of-two FP8 quantization (README,
+ * Usage: fp8_quantize returns the e4m3 tensor and its descale as a device
+ * fp32 scalar).
+ *   amax    = max |x| over all numel elements (x finite)
+ *   descale = 2^ceil(log2(amax / 448)), or 1 when amax == 0, and never
+ *             below 2^-126 (a descale must be a normal float32)
+ *   x8[i]   = e4m3fn code of x[i] / descale, round to nearest even
+ *  x       device pointer, numel elements of x_dtype (ZYFA_DTYPE_BF16 or
+ *          ZYFA_DTYPE_FP32)
+ *  x8      device pointer, numel bytes (caller-owned)
+ *  descale device pointer to one fp32 (caller-owned); written on device, the
+ *          host never reads it.
+ *  numel == 0 writes descale = 1. Deterministic: the result does not depend
+ *  on timing.
+ */
+int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
+                      void* stream);
+
+/* zyfa_status_string - static, human-readable text of a status code. */
+const char* zyfa_status_string(int status);
+
+/* zyfa_release - free every cached plan on every device (device memory of
+ * job tables and scratch). Must not race with calls in flight. */
+void zyfa_release(void);
+
+/*
+ * zyfa_plan_jobs - host-only view of the job table a shape would use (no HIP
+ * call, no device memory), for inspection and tests. The work distribution
+ * follows the README's Kernel design list (work distribution): query tiles
+ * of one (batch, head) are paired first with last so every job has the same
+ * work, a persistent grid of num_wgs workgroups loops over jobs, and
+ * consecutive jobs go to workgroups on the same XCD (blockIdx % 8).
+ *  num_cus      compute units to fill (256 on MI355X)
+ *  out_tile_q   receives the query-tile height in rows
+ *  out_num_wgs  receives the persistent grid size
+ *  out_jobs_per_wg receives the number of table rows
+ *  table        NULL, or int[2 * num_wgs * jobs_per_wg] receiving, for row r
+ *               and workgroup w at index 2*(r*num_wgs + w), the pair
+ *               {batch*nheads + head, first tile i} (the job covers query
+ *               tiles i and n-1-i, or only i when they coincide); {-1, -1}
+ *               marks the end of a workgroup's list.
+ *  table_capacity number of ints available in table (ignored when NULL).
+ */
+int zyfa_plan_jobs(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int dtype,
+                   int num_cus, int* out_tile_q, int* out_num_wgs, int* out_jobs_per_wg,
+                   int* table, long long table_capacity);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZYFA_H */

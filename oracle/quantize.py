@@ -10,6 +10,10 @@ never saturates is
     descale = 2^ceil(log2(amax / 448))     (descale = 1 when amax == 0)
     code    = e4m3fn_RNE(x / descale)
 
+The README also requires a tensor descale to be a positive normal float32
+(Usage), so the descale is never below 2^-126 (it only matters for tensors
+whose largest magnitude is below 448 * 2^-127).
+
 x / descale is exact (a power of two), so each code is one RNE rounding
 (Kernel design: every conversion rounds to nearest even).
 """
@@ -35,7 +39,7 @@ def pow2_descale(amax: float) -> float:
         e += 1
     while math.ldexp(E4M3FN_MAX, e - 1) >= amax:
         e -= 1
-    return math.ldexp(1.0, e)
+    return math.ldexp(1.0, max(e, -126))
 
 
 def fp8_quantize_ref(x):

@@ -1,0 +1,75 @@
+"""Helpers shared by the GPU parity tests: input staging and tolerances.
+
+Both sides see the same inputs: the seeded float32 draws of `workloads`
+are cast to bf16 by torch for the GPU and by the oracle's own codec for the
+oracle; `bf16_pair` checks that the two casts agree bit for bit.
+"""
+import numpy as np
+import torch
+
+import oracle
+
+# BF16 gate: max |d out| <= 1e-2 and |d LSE| <= 1e-3. The output is bf16, so
+# an exactly computed result still carries up to half an ulp of rounding,
+# 2^-8 |ref| (over 1e-2 once |ref| >= 2.56); the element bound adds exactly
+# that allowance. The literal max is reported beside it.
+BF16_OUT_ABS = 1e-2
+BF16_OUT_REL_ROUND = 2.0 ** -8
+BF16_LSE_ABS = 1e-3
+# FP8 gate (oracle on the dequantized inputs): max <= 6e-2, mean <= 5e-3,
+# with the same bf16 output-rounding allowance on the max.
+FP8_OUT_MAX = 6e-2
+FP8_OUT_MEAN = 5e-3
+
+
+def bf16_pair(x: np.ndarray, device="cuda"):
+    """(torch bf16 CUDA tensor, float64 values the oracle uses)."""
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
+    ref = oracle.bf16_round(x)
+    bits_torch = t.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits_torch, oracle.bf16_encode_bits(x)), "bf16 casts disagree"
+    return t.to(device), ref
+
+
+def out_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def score_magnitude(qh: np.ndarray, kh: np.ndarray, scale: float, rows) -> np.ndarray:
+    """scale * max_{j <= i} sum_c |q_ic k_jc| for the given rows of one head:
+    the size of the terms an fp32 score accumulation rounds."""
+    rows = np.asarray(rows)
+    a = np.abs(qh[rows]) @ np.abs(kh[: int(rows.max()) + 1]).T
+    a[np.arange(a.shape[1])[None, :] > rows[:, None]] = 0.0
+    return scale * a.max(axis=1)
+
+
+# fp32 score accumulation (MFMA, d_qk terms) rounds at about 2^-24 of the term
+# magnitude per step; 2^-20 of it is the LSE allowance added on rows whose
+# scores are large (activation-like inputs). On N(0, 1) inputs it is < 1e-5.
+LSE_ROUND_REL = 2.0 ** -20
+
+
+def check_bf16(out, ref_out, lse=None, ref_lse=None, what="", lse_mag=None):
+    d = np.abs(out - ref_out)
+    bound = BF16_OUT_ABS + BF16_OUT_REL_ROUND * np.abs(ref_out)
+    worst = np.unravel_index(np.argmax(d - bound), d.shape)
+    msg = f"{what}: max|dout|={d.max():.3e} mean={d.mean():.2e} worst at {worst} (ref {ref_out[worst]:.4f} got {out[worst]:.4f})"
+    assert np.all(np.isfinite(out)), what + ": non-finite output"
+    assert np.all(d <= bound), msg
+    if lse is not None:
+        dl = np.abs(lse - ref_lse)
+        assert np.all(np.isfinite(lse)), what + ": non-finite lse"
+        allow = BF16_LSE_ABS if lse_mag is None else BF16_LSE_ABS + LSE_ROUND_REL * lse_mag
+        assert np.all(dl <= allow), f"{what}: max|dLSE|={dl.max():.3e}"
+    return d.max()
+
+
+def check_fp8(out, ref_out, what=""):
+    d = np.abs(out - ref_out)
+    bound = FP8_OUT_MAX + BF16_OUT_REL_ROUND * np.abs(ref_out)
+    assert np.all(np.isfinite(out)), what + ": non-finite output"
+    worst = np.unravel_index(np.argmax(d - bound), d.shape)
+    assert np.all(d <= bound), f"{what}: max|dout|={d.max():.3e} at {worst} (ref {ref_out[worst]:.4f} got {out[worst]:.4f})"
+    assert d.mean() <= FP8_OUT_MEAN, f"{what}: mean|dout|={d.mean():.3e}"
+    return d.max(), d.mean()

@@ -1,0 +1,115 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+rejects bad arguments before touching the GPU, and builds sound job tables."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import causal_flashattention_prefill_amd as zy
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "zyfa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(zyfa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "zyfa_fwd" in names and "zyfa_fp8_quantize" in names and "zyfa_prepare" in names
+    L = zy.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert zy.zyfa_status_string(0) == "ok"
+    for code in zy.STATUS.values():
+        assert zy.zyfa_status_string(code) != "unknown status"
+
+
+def _fwd(**kw):
+    a = dict(q=16, k=16, v=16, out=16, lse=None, B=1, S=128, H=4, Hk=2, dqk=128, dv=128, layout=0, dtype=0,
+             qd=None, kd=None, vd=None, stream=None)
+    a.update(kw)
+    return zy.lib().zyfa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["S"], a["H"], a["Hk"], a["dqk"],
+                             a["dv"], a["layout"], a["dtype"], a["qd"], a["kd"], a["vd"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), "ZYFA_ERR_SHAPE"), (dict(S=0), "ZYFA_ERR_SHAPE"), (dict(H=-1), "ZYFA_ERR_SHAPE"),
+    (dict(dqk=64, dv=64), "ZYFA_ERR_HEADDIM"), (dict(dqk=128, dv=192), "ZYFA_ERR_HEADDIM"),
+    (dict(dqk=192, dv=192), "ZYFA_ERR_HEADDIM"), (dict(H=6, Hk=4), "ZYFA_ERR_GQA"),
+    (dict(dtype=7), "ZYFA_ERR_DTYPE"), (dict(layout=3), "ZYFA_ERR_LAYOUT"), (dict(q=None), "ZYFA_ERR_NULL"),
+    (dict(out=None), "ZYFA_ERR_NULL"), (dict(dtype=1), "ZYFA_ERR_DESCALE"), (dict(dtype=1, qd=16, kd=16), "ZYFA_ERR_DESCALE"),
+    (dict(k=24), "ZYFA_ERR_ALIGN"),
+])
+def test_fwd_argument_errors(kw, status):
+    assert _fwd(**kw) == zy.STATUS[status]
+
+
+def test_quantize_argument_errors():
+    L = zy.lib()
+    assert L.zyfa_fp8_quantize(16, 5, 10, 16, 16, None) == zy.STATUS["ZYFA_ERR_DTYPE"]
+    assert L.zyfa_fp8_quantize(16, 0, -1, 16, 16, None) == zy.STATUS["ZYFA_ERR_SHAPE"]
+    assert L.zyfa_fp8_quantize(16, 0, 10, 16, None, None) == zy.STATUS["ZYFA_ERR_NULL"]
+    assert L.zyfa_fp8_quantize(None, 0, 10, 16, 16, None) == zy.STATUS["ZYFA_ERR_NULL"]
+    assert L.zyfa_fp8_quantize(8, 0, 10, 16, 16, None) == zy.STATUS["ZYFA_ERR_ALIGN"]
+
+
+def test_prepare_argument_errors():
+    L = zy.lib()
+    assert L.zyfa_prepare(1, 128, 4, 3, 128, 128, 0, 0, 0, None) == zy.STATUS["ZYFA_ERR_GQA"]
+    assert L.zyfa_prepare(1, 128, 4, 4, 96, 128, 0, 0, 0, None) == zy.STATUS["ZYFA_ERR_HEADDIM"]
+
+
+@pytest.mark.parametrize("B,S,H,Hk", [(1, 256, 4, 4), (1, 8192, 32, 8), (1, 16384, 32, 8), (1, 16384, 16, 16),
+                                      (2, 32000, 32, 8), (3, 1000, 6, 2), (1, 1, 1, 1), (1, 300, 2, 1),
+                                      (1, 16384, 4, 1)])
+def test_job_table_covers_every_tile_once(B, S, H, Hk):
+    tq, nw, jp, table = zy.zyfa_plan_jobs(B, S, H, Hk)
+    n = -(-S // tq)
+    assert 1 <= nw <= 256
+    seen = {}
+    work = np.zeros(nw)
+    for w in range(nw):
+        ended = False
+        for r in range(jp):
+            bh, i = table[r, w]
+            if bh < 0:
+                ended = True
+                continue
+            assert not ended, "a job after the end marker"
+            assert 0 <= bh < B * H and 0 <= i <= n - 1 - i
+            for t in {i, n - 1 - i}:
+                key = (bh, t)
+                assert key not in seen
+                seen[key] = w
+                work[w] += t + 1          # key tiles ~ tile index + 1
+    assert len(seen) == B * H * n
+    # every workgroup's job count differs by at most one
+    counts = (table[:, :, 0] >= 0).sum(axis=0)
+    assert counts.max() - counts.min() <= 1
+
+
+def test_job_pairs_have_equal_work():
+    tq, nw, jp, table = zy.zyfa_plan_jobs(1, 16384, 32, 8)
+    n = 16384 // tq
+    for bh, i in table.reshape(-1, 2):
+        if bh >= 0:
+            assert (i + 1) + (n - 1 - i + 1) == n + 1
+
+
+def test_job_table_xcd_locality():
+    # in each table row, the workgroups of one XCD (blockIdx % 8) hold
+    # consecutive jobs, so at most two heads per XCD per row
+    tq, nw, jp, table = zy.zyfa_plan_jobs(1, 16384, 32, 8)
+    assert nw == 256 and jp == 4
+    for r in range(jp):
+        for x in range(8):
+            heads = {int(table[r, w, 0]) for w in range(x, nw, 8)}
+            assert len(heads) <= 2

@@ -1,0 +1,128 @@
+"""GPU parity of the BF16 path against the float64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, Workload, generate
+from parity import bf16_pair, check_bf16, out_to_f64, score_magnitude
+
+pytestmark = pytest.mark.gpu
+
+zy = pytest.importorskip("causal_flashattention_prefill_amd")
+
+
+def run_case(w: Workload, seed=None, with_lse=True, heads=None):
+    q, k, v = generate(w, seed)
+    (tq, rq), (tk, rk), (tv, rv) = bf16_pair(q), bf16_pair(k), bf16_pair(v)
+    print(f"case {w.name} B{w.batch} S{w.seqlen} H{w.nheads}/{w.nheads_k} d{w.d_qk}/{w.d_v} {w.layout}", flush=True)
+    res = zy.zyfa_fwd(tq, tk, tv, layout=w.layout, return_lse=with_lse)
+    torch.cuda.synchronize()
+    out, lse = res if with_lse else (res, None)
+    ref_out, ref_lse = oracle.causal_attention_ref(rq, rk, rv, layout=w.layout, heads=heads)
+    o = out_to_f64(out)
+    if heads is not None:
+        hax = 2 if w.layout == "bshd" else 1
+        o = np.take(o, heads, axis=hax)
+        ref_out = np.take(ref_out, heads, axis=hax)
+        ref_lse = ref_lse[:, heads]
+    l = None if lse is None else lse.cpu().numpy().astype(np.float64)
+    if l is not None and heads is not None:
+        l = l[:, heads]
+    mag = None
+    if w.activation_like and with_lse:
+        mag = _magnitudes(rq, rk, w, heads)
+    return check_bf16(o, ref_out, l, ref_lse if with_lse else None, w.name, lse_mag=mag)
+
+
+def _heads_view(x, layout):
+    return np.swapaxes(x, 1, 2) if layout == "bshd" else x
+
+
+def _magnitudes(rq, rk, w, heads=None):
+    Q, K = _heads_view(rq, w.layout), _heads_view(rk, w.layout)
+    hs = range(w.nheads) if heads is None else heads
+    g = w.nheads // w.nheads_k
+    rows = np.arange(w.seqlen)
+    return np.stack([np.stack([score_magnitude(Q[b, h], K[b, h // g], w.softmax_scale, rows) for h in hs])
+                     for b in range(w.batch)])
+
+
+def test_workload1_full():
+    run_case(WORKLOADS[1])
+
+
+@pytest.mark.parametrize("B,S,H,Hk,dqk,layout", [
+    (2, 700, 4, 2, 128, "bshd"),     # several tiles, ragged tail, GQA, 2 batches
+    (1, 1000, 4, 1, 128, "bhsd"),    # MQA, bhsd, ragged
+    (1, 600, 2, 2, 192, "bhsd"),     # d_qk = 192
+    (2, 520, 3, 3, 192, "bshd"),
+    (1, 1, 2, 1, 128, "bshd"),       # single token
+    (1, 63, 2, 2, 128, "bshd"),
+    (1, 255, 2, 2, 128, "bhsd"),
+    (1, 257, 2, 1, 128, "bshd"),
+    (1, 4097, 2, 1, 128, "bshd"),
+])
+def test_small_shapes(B, S, H, Hk, dqk, layout):
+    w = Workload("small", B, S, H, Hk, dqk, 128, layout, ("bf16",), True, False, 1000 + S)
+    run_case(w)
+
+
+def test_no_lse_matches_lse_variant():
+    w = WORKLOADS[1]
+    q, k, v = generate(w)
+    tq, tk, tv = (bf16_pair(x)[0] for x in (q, k, v))
+    a = zy.zyfa_fwd(tq, tk, tv)
+    b, _ = zy.zyfa_fwd(tq, tk, tv, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_activation_like_small():
+    w = WORKLOADS[5].resized(batch=1, seqlen=1536, name="act_small")
+    run_case(w)
+
+
+def _sample_rows(S, rng, n=24):
+    base = [0, 1, 2, 63, 64, 65, 255, 256, 257, S // 2, S - 257, S - 256, S - 65, S - 2, S - 1]
+    rows = set(r for r in base if 0 <= r < S)
+    rows.update(rng.integers(0, S, n).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("wid", [2, 4, 5])
+def test_full_size_sampled_rows(wid):
+    # the benchmark's shapes; the oracle computes sampled rows one by one
+    w = WORKLOADS[wid]
+    q, k, v = generate(w)
+    (tq, rq), (tk, rk), (tv, rv) = bf16_pair(q), bf16_pair(k), bf16_pair(v)
+    print(f"case full {w.name}", flush=True)
+    out, lse = zy.zyfa_fwd(tq, tk, tv, layout=w.layout, return_lse=True)
+    torch.cuda.synchronize()
+    o = out_to_f64(out)
+    l = lse.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(wid)
+    for b in range(w.batch):
+        for h in sorted(set([0, w.nheads - 1] + rng.integers(0, w.nheads, 2).tolist())):
+            rows = _sample_rows(w.seqlen, rng)
+            ro, rl = oracle.causal_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout)
+            got = o[b, rows, h] if w.layout == "bshd" else o[b, h, rows]
+            mag = None
+            if w.activation_like:
+                Q, K = _heads_view(rq, w.layout), _heads_view(rk, w.layout)
+                mag = score_magnitude(Q[b, h], K[b, h // (w.nheads // w.nheads_k)], w.softmax_scale, rows)
+            check_bf16(got, ro, l[b, h, rows], rl, f"{w.name} b{b} h{h}", lse_mag=mag)
+
+
+def test_bitwise_deterministic():
+    w = WORKLOADS[2].resized(seqlen=2048)
+    q, k, v = generate(w)
+    tq, tk, tv = (bf16_pair(x)[0] for x in (q, k, v))
+    first, flse = zy.zyfa_fwd(tq, tk, tv, return_lse=True)
+    a = torch.randn(2048, 2048, device="cuda")
+    for i in range(10):
+        if i % 2:
+            _ = a @ a  # a GEMM between launches
+        o, l = zy.zyfa_fwd(tq, tk, tv, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, first) and torch.equal(l, flse), f"run {i} differs"

@@ -10,14 +10,14 @@ from workloads import WORKLOADS
 @pytest.mark.parametrize("amax,want", [
     (448.0, 1.0), (448.0 * 1.0001, 2.0), (449.0, 2.0), (224.0, 0.5), (224.5, 1.0),
     (0.0, 1.0), (448.0 * 2 ** -20, 2.0 ** -20), (5.5, 2.0 ** -6), (7.0, 2.0 ** -6), (7.01, 2.0 ** -5),
-    (1e30, 2.0 ** 91),
+    (1e30, 2.0 ** 91), (448.0 * 2.0 ** -126, 2.0 ** -126), (1e-40, 2.0 ** -126),
 ])
 def test_descale_rule(amax, want):
     assert pow2_descale(amax) == want
     # the defining properties: amax/d <= 448 and amax/(d/2) > 448
     d = pow2_descale(amax)
     assert amax / d <= 448.0
-    if amax:
+    if amax and d > 2.0 ** -126:
         assert amax / (d / 2) > 448.0
 
 
