@@ -156,7 +156,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   // fit in 31 bits.
   const long long s_pad = (long long)plan->n_qtiles * plan->tile_q;
   auto extent = [&](long long ss, int dim) { return ((long long)(seqlen - 1) * ss + dim) * esz; };
-  auto reach = [&](long long ss, int dim) { return ((s_pad + 64) * ss + dim) * esz; };
+  auto reach = [&](long long ss, int dim) { return ((s_pad + 128) * ss + dim) * esz; };
   const long long lim = 0x7FFFFFFFll;
   if (reach(a.q.stride_s, d_qk) > lim || reach(a.k.stride_s, d_qk) > lim || reach(a.v.stride_s, d_v) > lim)
     return ZYFA_ERR_RANGE;

@@ -8,8 +8,9 @@
 //  - A job is a pair of 256-row query tiles (i, n-1-i) of one (batch, head)
 //    (README, Kernel design: work distribution). Each wave owns 32 query
 //    rows (two 16-row groups) for the whole key loop.
-//  - Keys stream in 64-key tiles through a two-stage LDS ring; global loads
-//    of tile t+1 are issued before the MFMA work on tile t.
+//  - Keys stream in 64-key tiles through a two-stage LDS ring filled by
+//    direct global-to-LDS loads; the loads of tile t+1 are issued before the
+//    MFMA work on tile t.
 //  - Scores are computed transposed, S^T = K Q^T, with K as the MFMA A
 //    operand (README, Kernel design: transposed scores), using
 //    v_mfma_f32_16x16x32_bf16. Lane (g, n) (g = lane/16, n = lane%16) then
@@ -50,9 +51,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   constexpr int VBYTES = kTileK * VPITCH;
   constexpr int STAGE = KBYTES + VBYTES;
   constexpr int NC = DQK / 32;                 // MFMA k-steps over d_qk
-  constexpr int KLD = kTileK * KCH / kThreads; // 16-byte K loads per thread per tile
-  constexpr int VLD = kTileK * VCH / kThreads;
-  static_assert(KLD * kThreads == kTileK * KCH && VLD * kThreads == kTileK * VCH, "tile split");
+  constexpr int KLD = KBYTES / 1024 / 8;       // 1 KiB direct-to-LDS loads per wave per tile
+  constexpr int VLD = VBYTES / 1024 / 8;
+  static_assert(KLD * 8 * 1024 == KBYTES && VLD * 8 * 1024 == VBYTES, "tile split");
 
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -108,44 +109,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       float mref[2] = {neg_inf(), neg_inf()};
       float lsum[2] = {0.f, 0.f};
 
-      u32x4 kr[KLD], vr[VLD];
-      auto load_kv = [&](int kt) {
-#pragma unroll
-        for (int u = 0; u < KLD; ++u) {
-          const int id = tid + kThreads * u, row = id / KCH, x = id % KCH;
-          kr[u] = buf_load16(rk, (kt * kTileK + row) * krs + x * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < VLD; ++u) {
-          const int id = tid + kThreads * u, row = id / VCH, x = id % VCH;
-          vr[u] = buf_load16(rv, (kt * kTileK + row) * vrs + x * 16);
-        }
-      };
-      // K rows keep their 16-byte chunks XOR-swizzled by row so that the 16
-      // lanes reading one chunk column of 16 rows hit distinct banks; V rows
-      // are swizzled by even values so the 8-byte halves the transposing
-      // read needs stay intact.
-      auto store_kv = [&](int st) {
+      // K/V tiles go straight from memory into LDS (buffer_load ... lds).
+      // Wave-instruction I fills bytes [1024 I, 1024 I + 1024) of a region;
+      // lane L's 16 bytes land at p = 1024 I + 16 L, which is row p / pitch,
+      // chunk slot (p % pitch) / 16, so the lane fetches the global chunk
+      // that belongs in that slot. K chunks are XOR-swizzled by row so the 16
+      // lanes that read one chunk column of 16 rows hit distinct banks; V
+      // chunks are swizzled by even values, keeping the 8-byte halves the
+      // transposing read needs intact.
+      auto issue_kv = [&](int kt, int st) {
         char* ks = smem + st * STAGE;
 #pragma unroll
         for (int u = 0; u < KLD; ++u) {
-          const int id = tid + kThreads * u, row = id / KCH, x = id % KCH;
-          lds_store(ks + row * KPITCH + ((x ^ (row & KSWZ)) << 4), kr[u]);
+          const int I = wave * KLD + u;
+          const int p = I * 1024 + lane * 16;
+          const int row = p / KPITCH, x = ((p % KPITCH) >> 4) ^ (row & KSWZ);
+          buf_load16_lds(rk, (kt * kTileK + row) * krs + x * 16, ks + I * 1024);
         }
 #pragma unroll
         for (int u = 0; u < VLD; ++u) {
-          const int id = tid + kThreads * u, row = id / VCH, x = id % VCH;
-          lds_store(ks + KBYTES + row * VPITCH + ((x ^ ((row & 7) << 1)) << 4), vr[u]);
+          const int I = wave * VLD + u;
+          const int p = I * 1024 + lane * 16;
+          const int row = p / VPITCH, x = ((p % VPITCH) >> 4) ^ ((row & 7) << 1);
+          buf_load16_lds(rv, (kt * kTileK + row) * vrs + x * 16, ks + KBYTES + I * 1024);
         }
       };
 
-      load_kv(0);
-      store_kv(0);
+      issue_kv(0, 0);
+      wait_all_memory();
       __syncthreads();
 
       for (int kt = 0; kt < n_kt; ++kt) {
         const int st = kt & 1;
-        if (kt + 1 < n_kt) load_kv(kt + 1);
+        if (kt + 1 < n_kt) issue_kv(kt + 1, st ^ 1);
         if (kt <= kt_w) {
           const char* ks = smem + st * STAGE;
           const char* vs = ks + KBYTES;
@@ -243,7 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
                 o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qg][kc], o[qg][db], 0, 0, 0);
             }
         }
-        if (kt + 1 < n_kt) store_kv(st ^ 1);
+        wait_all_memory();
         __syncthreads();
       }
 

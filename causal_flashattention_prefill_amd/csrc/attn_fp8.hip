@@ -1,8 +1,322 @@
-// Causal forward attention, FP8 e4m3fn inputs (placeholder until the FP8
-// kernel lands: reports "not supported").
+// Causal forward attention, FP8 e4m3fn inputs with one descale per tensor,
+// BF16 output, for gfx950 (CDNA4).
+//
+// What is computed: "ZYFA" README, Usage (descales read from device memory
+// and applied by the kernel), Supported configurations, Accuracy (the output
+// is divided by the sum of the same rounded probabilities that multiply V,
+// and the LSE comes from those rounded probabilities).
+//
+// Structure (shared with the BF16 kernel: persistent 8-wave workgroups, jobs
+// = pairs of 256-row query tiles, 32 query rows per wave, transposed scores):
+//  - Keys stream in 128-key tiles through a two-stage LDS ring filled by
+//    direct global-to-LDS loads.
+//  - S^T = K Q^T with v_mfma_scale_f32_16x16x128_f8f6f4 (neutral scales);
+//    the three descales and the softmax scale are folded into one base-2
+//    factor read from device memory at kernel start.
+//  - P is exact: p = exp2(s - m_ref), then per-block power-of-two scaling
+//    (README, Kernel design: per-block scaling): each 32-key block of a query
+//    row (the scale block of the scaled MFMA) is divided by 2^floor(log2 of
+//    its largest p) while rounding to e4m3fn (v_cvt_scalef32_pk_fp8_f32,
+//    RNE), so the block's largest value lands in [1, 2) and stays normal.
+//    The PV MFMA multiplies the same power of two back in through its B-scale
+//    operand at no extra cost.
+//  - The row sum is one extra MFMA of the rounded, scaled P against a block
+//    of ones (README, Kernel design: row sum on the matrix unit), so the
+//    denominator is the sum of exactly the values that multiply V.
+//  - V^T is read from LDS with ds_read_b64_tr_b8 (transposes bytes during
+//    the read), so V is stored as it arrives.
+//  - Lazy rescale of the running maximum with one wave ballot, as in BF16.
+//  - d_qk = 192 adds one MFMA per score block over d 128..191 with the
+//    remaining half of the K dimension zero.
+//
+// Fragment layout of the 16x16x128 FP8 MFMA (lane = 16*g + r, g = lane/16):
+// A (16 x 128): lane holds row r, bytes 0..15 = k 16g..16g+15 and bytes
+// 16..31 = k 64+16g..; B (128 x 16) likewise for column r; D: lane holds
+// rows 4g..4g+3 of column r. The scale of A row r (B column r) for k-block
+// b (32 wide) comes from lane r + 16b.
 #include "device_common.h"
 #include "zyfa_internal.h"
 
 namespace zyfa {
-hipError_t launch_attn_fp8(const AttnArgs&, int, bool, int, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kTileQ = 256;
+constexpr int kTileK = 128;
+constexpr float kTau = 8.0f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kE8M0One = 127;           // E8M0 scale 2^0
+
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Largest power of two <= x for x > 0 (exponent field only), at least 2^-126.
+__device__ __forceinline__ float pow2_floor(float x) {
+  const unsigned e = __builtin_bit_cast(unsigned, x) & 0x7F800000u;
+  return __builtin_bit_cast(float, e < 0x00800000u ? 0x00800000u : e);
+}
+
+// Four floats / scale -> four e4m3fn codes (RNE) in one word.
+__device__ __forceinline__ unsigned cvt4_fp8(float a, float b, float c, float d, float scale) {
+  i16x2 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, scale, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
+  return __builtin_bit_cast(unsigned, w);
+}
+
+template <int DQK, bool WITH_LSE>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArgs a) {
+  constexpr int DV = 128;
+  constexpr bool D192 = DQK == 192;
+  constexpr int KA_BYTES = kTileK * 128;       // K region for d 0..127
+  constexpr int KB_BYTES = D192 ? kTileK * 64 : 0;  // K region for d 128..191
+  constexpr int V_BYTES = kTileK * DV;
+  constexpr int STAGE = KA_BYTES + KB_BYTES + V_BYTES;
+  static_assert(KA_BYTES == 16 * 1024 && V_BYTES == 16 * 1024 && (!D192 || KB_BYTES == 8 * 1024), "tile split");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int S = a.seqlen;
+  // Scores in base-2 units: S_codes * (softmax_scale * log2 e * dq * dk).
+  const float sl2 = a.scale_log2 * a.q_descale[0] * a.k_descale[0];
+  const float dvs = a.v_descale[0];
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3fn 1.0
+
+  for (int it = 0; it < a.jobs_per_wg; ++it) {
+    const int2 job = a.jobs[it * (int)gridDim.x + (int)blockIdx.x];
+    if (job.x < 0) break;
+    const int b = job.x / a.nheads;
+    const int h = job.x - b * a.nheads;
+    const int hk = (int)(((long long)h * a.nheads_k) / a.nheads);
+    const char* qbase = (const char*)a.q.ptr + (b * a.q.stride_b + h * a.q.stride_h);
+    const char* kbase = (const char*)a.k.ptr + (b * a.k.stride_b + hk * a.k.stride_h);
+    const char* vbase = (const char*)a.v.ptr + (b * a.v.stride_b + hk * a.v.stride_h);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, a.q_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, a.k_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, a.v_bytes);
+    const int qrs = (int)a.q.stride_s;
+    const int krs = (int)a.k.stride_s;
+    const int vrs = (int)a.v.stride_s;
+
+    const int tA = job.y;
+    const int tB = a.n_qtiles - 1 - job.y;
+    const int ntiles = (tA == tB) ? 1 : 2;
+    for (int tt = 0; tt < ntiles; ++tt) {
+      const int qt = tt == 0 ? tA : tB;
+      const int q0 = qt * kTileQ;
+      const int qw0 = q0 + wave * 32;
+      const int qend = min(q0 + kTileQ, S);
+      const int n_kt = (qend - 1) / kTileK + 1;
+      const int kt_w = (qw0 < S) ? min((qw0 + 31) / kTileK, n_kt - 1) : -1;
+
+      // Q fragments (B operand): lane (g, n) holds q[row n][16g..16g+15] and
+      // q[row n][64+16g..]; for d 192 also q[row n][128+16g..] (upper half 0).
+      i32x8 qf[2], qf2[2];
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg) {
+        const int off = (qw0 + 16 * qg + n) * qrs;
+        const u32x4 lo = buf_load16(rq, off + 16 * g);
+        const u32x4 hi = buf_load16(rq, off + 64 + 16 * g);
+        qf[qg] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        if (D192) {
+          const u32x4 x = buf_load16(rq, off + 128 + 16 * g);
+          qf2[qg] = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+        }
+      }
+
+      f32x4 o[2][8];
+      f32x4 lacc[2];
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg) {
+        lacc[qg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      float mref[2] = {neg_inf(), neg_inf()};
+
+      // Direct global-to-LDS tile loads (see the BF16 kernel); LDS layouts,
+      // 16-byte chunks XOR-swizzled by row:
+      //  K d 0..127:   row * 128 + ((c ^ ((row >> 1) & 7)) << 4)
+      //  K d 128..191: row * 64  + ((c ^ ((row >> 2) & 3)) << 4)
+      //  V:            row * 128 + ((c ^ ((row >> 1) & 7)) << 4)
+      auto issue_kv = [&](int kt, int st) {
+        char* base = smem + st * STAGE;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int I = wave * 2 + u;
+          const int p = I * 1024 + lane * 16;
+          const int row = p >> 7, x = ((p & 127) >> 4) ^ ((row >> 1) & 7);
+          buf_load16_lds(rk, (kt * kTileK + row) * krs + x * 16, base + I * 1024);
+          buf_load16_lds(rv, (kt * kTileK + row) * vrs + x * 16, base + KA_BYTES + KB_BYTES + I * 1024);
+        }
+        if (D192) {
+          const int p = wave * 1024 + lane * 16;
+          const int row = p >> 6, x = ((p & 63) >> 4) ^ ((row >> 2) & 3);
+          buf_load16_lds(rk, (kt * kTileK + row) * krs + 128 + x * 16, base + KA_BYTES + wave * 1024);
+        }
+      };
+
+      issue_kv(0, 0);
+      wait_all_memory();
+      __syncthreads();
+
+      for (int kt = 0; kt < n_kt; ++kt) {
+        const int st = kt & 1;
+        if (kt + 1 < n_kt) issue_kv(kt + 1, st ^ 1);
+        if (kt <= kt_w) {
+          const char* ka = smem + st * STAGE;
+          const char* kb2 = ka + KA_BYTES;
+          const char* vs = ka + KA_BYTES + KB_BYTES;
+          // ---- S^T = K Q^T (8 blocks of 16 keys)
+          f32x4 s[2][8];
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            const int row = 16 * kb + n;
+            const int sw = (row >> 1) & 7;
+            const u32x4 lo = lds_load<u32x4>(ka + row * 128 + ((g ^ sw) << 4));
+            const u32x4 hi = lds_load<u32x4>(ka + row * 128 + (((4 + g) ^ sw) << 4));
+            const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg)
+              s[qg][kb] = mfma_fp8(kf, qf[qg], f32x4{0.f, 0.f, 0.f, 0.f}, kE8M0One, kE8M0One);
+            if (D192) {
+              const u32x4 x = lds_load<u32x4>(kb2 + row * 64 + ((g ^ ((row >> 2) & 3)) << 4));
+              const i32x8 kf2 = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+#pragma unroll
+              for (int qg = 0; qg < 2; ++qg) s[qg][kb] = mfma_fp8(kf2, qf2[qg], s[qg][kb], kE8M0One, kE8M0One);
+            }
+          }
+          // ---- scale, causal mask, lazy max
+          const int kbase = kt * kTileK;
+          const bool diag = kbase + kTileK - 1 > qw0;
+          float mx[2];
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            float m = neg_inf();
+            const int q = qw0 + 16 * qg + n;
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                float v = s[qg][kb][i] * sl2;
+                if (diag && (kbase + 16 * kb + 4 * g + i > q)) v = neg_inf();
+                s[qg][kb][i] = v;
+                m = fmaxf(m, v);
+              }
+            mx[qg] = m;
+          }
+          const bool need = (mx[0] > mref[0] + kTau) || (mx[1] > mref[1] + kTau);
+          if (wave_any(need)) {
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg) {
+              float rm = fmaxf(mx[qg], __shfl_xor(mx[qg], 16));
+              rm = fmaxf(rm, __shfl_xor(rm, 32));
+              const float mn = fmaxf(mref[qg], rm);
+              const float f = fast_exp2(mref[qg] - mn);
+              lacc[qg] *= f;
+#pragma unroll
+              for (int db = 0; db < 8; ++db) o[qg][db] *= f;
+              mref[qg] = mn;
+            }
+          }
+          // ---- exact P, per-block power-of-two scale, RNE to e4m3fn
+          i32x8 pf[2];
+          int psc[2];
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            float h0 = 0.f, h1 = 0.f;   // largest p of blocks kb 0..3 and 4..7
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(s[qg][kb][i] - mref[qg]);
+                s[qg][kb][i] = p;
+                if (kb < 4) h0 = fmaxf(h0, p); else h1 = fmaxf(h1, p);
+              }
+            // scale block of kb 0..3 is g/2, of kb 4..7 is 2 + g/2; each is
+            // shared with lane ^ 16 (the other half of the block)
+            h0 = fmaxf(h0, __shfl_xor(h0, 16));
+            h1 = fmaxf(h1, __shfl_xor(h1, 16));
+            const float sc0 = pow2_floor(h0), sc1 = pow2_floor(h1);
+            // lane 16*b + n supplies the scale of block b: groups 1 and 2
+            // swap the maxima they do not hold themselves
+            const float other = __shfl_xor((g & 1) ? sc1 : sc0, 48);
+            const float mine = g == 0 ? sc0 : (g == 3 ? sc1 : other);
+            psc[qg] = (int)(__builtin_bit_cast(unsigned, mine) >> 23);
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+              pf[qg][kb] = (int)cvt4_fp8(s[qg][kb][0], s[qg][kb][1], s[qg][kb][2], s[qg][kb][3], kb < 4 ? sc0 : sc1);
+          }
+          // ---- row sum of the rounded P on the matrix unit
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) lacc[qg] = mfma_fp8(ones, pf[qg], lacc[qg], kE8M0One, psc[qg]);
+          // ---- O^T += V^T P^T
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            i32x8 vf;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              // rows of this 8-key read: byte e of lane group g is key
+              // 32t + 16*(e/4) + 4g + e%4; lane 2r+hh supplies row r, columns
+              // 16db + 8hh .. +7
+              const int r = n >> 1, hh = n & 1;
+              const int row = 32 * t + 16 * (r >> 2) + 4 * g + (r & 3);
+              const char* p = vs + row * 128 + ((db ^ ((row >> 1) & 7)) << 4) + hh * 8;
+              const i32x2 w = lds_read_tr8(p);
+              vf[2 * t] = w[0];
+              vf[2 * t + 1] = w[1];
+            }
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg) o[qg][db] = mfma_fp8(vf, pf[qg], o[qg][db], kE8M0One, psc[qg]);
+          }
+        }
+        wait_all_memory();
+        __syncthreads();
+      }
+
+      // ---- epilogue: O * dv / l (RNE to bf16), LSE = ln2 * (m + log2 l)
+      if (kt_w >= 0) {
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+          const float lt = lacc[qg][0];
+          const float f = dvs / lt;
+          const int q = qw0 + 16 * qg + n;
+          if (q < S) {
+            __bf16* orow = (__bf16*)a.out + (b * a.o_stride_b + h * a.o_stride_h + (long long)q * a.o_stride_s);
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+              const u32x2 w = {pack_bf16x2(o[qg][db][0] * f, o[qg][db][1] * f),
+                               pack_bf16x2(o[qg][db][2] * f, o[qg][db][3] * f)};
+              *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g) = w;
+            }
+            if (WITH_LSE && g == 0)
+              a.lse[((long long)b * a.nheads + h) * S + q] = (mref[qg] + fast_log2(lt)) * kLn2;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, int grid, hipStream_t s) {
+  const dim3 gd(grid), bd(kThreads);
+  if (d_qk == 128) {
+    if (with_lse) hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false>), gd, bd, 0, s, a);
+  } else {
+    if (with_lse) hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, false>), gd, bd, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace zyfa

@@ -35,6 +35,18 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// Direct global-to-LDS load (buffer_load_dwordx4 ... lds): lane L of the
+// wave writes its 16 bytes to lds_wave_base + 16 * L. lds_wave_base must be
+// the same for the whole wave. Past the resource's extent the bytes are zero.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, int off, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0,
+                                           0, 0);
+}
+
+// Wait until every outstanding memory operation of this wave (including
+// direct-to-LDS loads) has completed.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
 template <class T>
 __device__ __forceinline__ T lds_load(const char* p) {
   return *reinterpret_cast<const T*>(p);

@@ -22,6 +22,9 @@ namespace {
 constexpr int kQThreads = 256;
 constexpr int kMaxPartials = 1024;
 
+// Scalars are passed by value: __builtin_bit_cast applied directly to an
+// element of an ext_vector (w[1]) has been compiled as a cast of element 0.
+__device__ __forceinline__ float as_float(unsigned u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
@@ -116,10 +119,10 @@ __global__ __launch_bounds__(kQThreads) void convert_kernel(const void* x, long 
       }
       reinterpret_cast<u32x2*>(x8)[i] = outw;
     } else {
-      int p = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_bit_cast(float, w[0]) * inv,
-                                              __builtin_bit_cast(float, w[1]) * inv, 0, false);
-      p = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_bit_cast(float, w[2]) * inv,
-                                          __builtin_bit_cast(float, w[3]) * inv, p, true);
+      int p = __builtin_amdgcn_cvt_pk_fp8_f32(as_float(w[0]) * inv,
+                                              as_float(w[1]) * inv, 0, false);
+      p = __builtin_amdgcn_cvt_pk_fp8_f32(as_float(w[2]) * inv,
+                                          as_float(w[3]) * inv, p, true);
       reinterpret_cast<unsigned*>(x8)[i] = (unsigned)p;
     }
   }

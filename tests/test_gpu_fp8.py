@@ -1,0 +1,152 @@
+"""GPU parity of the FP8 path: the quantizer bit for bit against the oracle's,
+and FP8 attention against the float64 oracle run on the oracle's own
+dequantized inputs (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, Workload, generate
+from parity import bf16_pair, check_fp8, fp8_score_allowance, out_to_f64
+
+pytestmark = pytest.mark.gpu
+
+zy = pytest.importorskip("causal_flashattention_prefill_amd")
+
+
+def quantize_both(x32: np.ndarray):
+    """GPU quantize of the bf16 tensor; oracle quantize of the same values.
+    Checks codes and descale bit for bit; returns (gpu codes, gpu descale,
+    oracle dequantized float64 values)."""
+    t, ref = bf16_pair(x32)
+    x8, ds = zy.zyfa_fp8_quantize(t)
+    torch.cuda.synchronize()
+    codes_ref, d_ref = oracle.fp8_quantize_ref(ref)
+    got = x8.view(torch.uint8).cpu().numpy()
+    assert float(ds.item()) == float(d_ref), f"descale {ds.item()} vs {d_ref}"
+    neq = np.count_nonzero(got != codes_ref)
+    assert neq == 0, f"{neq} codes differ"
+    return x8, ds, oracle.e4m3fn_decode(codes_ref) * float(d_ref)
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 4096 * 16 + 3, 1 << 20])
+@pytest.mark.parametrize("scale", [1.0, 37.5, 1e-3])
+def test_quantize_bitwise_bf16(n, scale):
+    rng = np.random.default_rng(n)
+    x = (rng.standard_normal(n) * scale).astype(np.float32)
+    quantize_both(x)
+
+
+def test_quantize_fp32_input_and_zero():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(100003) * 3).astype(np.float32)
+    t = torch.from_numpy(x).cuda()
+    x8, ds = zy.zyfa_fp8_quantize(t)
+    torch.cuda.synchronize()
+    codes, d = oracle.fp8_quantize_ref(x.astype(np.float64))
+    assert ds.item() == d and np.array_equal(x8.view(torch.uint8).cpu().numpy(), codes)
+    z = torch.zeros(1000, dtype=torch.bfloat16, device="cuda")
+    x8, ds = zy.zyfa_fp8_quantize(z)
+    torch.cuda.synchronize()
+    assert ds.item() == 1.0 and int(x8.view(torch.uint8).max()) == 0
+
+
+def test_quantize_workload3_full_size():
+    w = WORKLOADS[3]
+    q, k, v = generate(w)
+    for x in (q, k, v):
+        quantize_both(x)
+
+
+def _allowance(rq, rk, rv, w):
+    """Per-(b, s, h) FP8 score-precision allowance, in out's (bshd/bhsd) order."""
+    hv = lambda x: np.swapaxes(x, 1, 2) if w.layout == "bshd" else x
+    Q, K, V = hv(rq), hv(rk), hv(rv)
+    g = w.nheads // w.nheads_k
+    rows = np.arange(w.seqlen)
+    al = np.stack([np.stack([fp8_score_allowance(Q[b, h], K[b, h // g], V[b, h // g], w.softmax_scale, rows)
+                             for h in range(w.nheads)]) for b in range(w.batch)])   # (B, H, S)
+    return np.swapaxes(al, 1, 2) if w.layout == "bshd" else al
+
+
+def run_case(w: Workload, seed=None, with_lse=False):
+    q, k, v = generate(w, seed)
+    print(f"case fp8 {w.name} B{w.batch} S{w.seqlen} H{w.nheads}/{w.nheads_k} d{w.d_qk} {w.layout}", flush=True)
+    (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
+    res = zy.zyfa_fwd(q8, k8, v8, layout=w.layout, return_lse=with_lse, q_descale=qs, k_descale=ks, v_descale=vs)
+    torch.cuda.synchronize()
+    out, lse = res if with_lse else (res, None)
+    ref_out, ref_lse = oracle.causal_attention_ref(rq, rk, rv, layout=w.layout)
+    extra = _allowance(rq, rk, rv, w) if w.activation_like else None
+    md, mn = check_fp8(out_to_f64(out), ref_out, w.name, extra=extra)
+    if with_lse:
+        dl = np.abs(lse.cpu().numpy() - ref_lse)
+        # the FP8 LSE comes from the rounded probabilities; one e4m3 rounding
+        # moves a row sum by at most 2^-4 relative, i.e. < 0.065 nats
+        assert np.all(np.isfinite(dl)) and dl.max() < 0.065, f"max|dLSE|={dl.max():.3e}"
+    return md, mn
+
+
+@pytest.mark.parametrize("B,S,H,Hk,dqk,layout", [
+    (1, 256, 4, 4, 128, "bshd"),
+    (2, 700, 4, 2, 128, "bshd"),
+    (1, 1000, 4, 1, 128, "bhsd"),
+    (1, 600, 2, 2, 192, "bhsd"),
+    (2, 520, 3, 3, 192, "bshd"),
+    (1, 1, 2, 1, 128, "bshd"),
+    (1, 129, 2, 2, 192, "bshd"),
+    (1, 4097, 2, 1, 128, "bshd"),
+])
+def test_small_shapes(B, S, H, Hk, dqk, layout):
+    w = Workload("small_fp8", B, S, H, Hk, dqk, 128, layout, ("fp8",), False, False, 2000 + S)
+    run_case(w, with_lse=True)
+
+
+def test_activation_like_small():
+    run_case(WORKLOADS[5].resized(batch=1, seqlen=1536, name="act_small_fp8"))
+
+
+def _sample_rows(S, rng, n=24):
+    base = [0, 1, 2, 127, 128, 129, 255, 256, 257, S // 2, S - 257, S - 256, S - 129, S - 2, S - 1]
+    rows = set(r for r in base if 0 <= r < S)
+    rows.update(rng.integers(0, S, n).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("wid", [3, 4, 5])
+def test_full_size_sampled_rows(wid):
+    w = WORKLOADS[wid]
+    q, k, v = generate(w)
+    print(f"case full fp8 {w.name}", flush=True)
+    (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
+    out = zy.zyfa_fwd(q8, k8, v8, layout=w.layout, q_descale=qs, k_descale=ks, v_descale=vs)
+    torch.cuda.synchronize()
+    o = out_to_f64(out)
+    rng = np.random.default_rng(wid)
+    gots, refs, extras = [], [], []
+    hv = lambda x: np.swapaxes(x, 1, 2) if w.layout == "bshd" else x
+    for b in range(w.batch):
+        for h in sorted(set([0, w.nheads - 1] + rng.integers(0, w.nheads, 2).tolist())):
+            rows = _sample_rows(w.seqlen, rng)
+            ro, _ = oracle.causal_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout)
+            gots.append(o[b, rows, h] if w.layout == "bshd" else o[b, h, rows])
+            refs.append(ro)
+            hk = h // (w.nheads // w.nheads_k)
+            extras.append(fp8_score_allowance(hv(rq)[b, h], hv(rk)[b, hk], hv(rv)[b, hk], w.softmax_scale, rows)
+                          if w.activation_like else np.zeros(len(rows)))
+    check_fp8(np.concatenate(gots), np.concatenate(refs), w.name, extra=np.concatenate(extras))
+
+
+def test_bitwise_deterministic():
+    w = WORKLOADS[3].resized(seqlen=2048)
+    q, k, v = generate(w)
+    tq, tk, tv = (bf16_pair(x)[0] for x in (q, k, v))
+    (q8, qs), (k8, ks), (v8, vs) = (zy.zyfa_fp8_quantize(x) for x in (tq, tk, tv))
+    first, flse = zy.zyfa_fwd(q8, k8, v8, return_lse=True, q_descale=qs, k_descale=ks, v_descale=vs)
+    a = torch.randn(2048, 2048, device="cuda")
+    for i in range(10):
+        if i % 2:
+            _ = a @ a
+        o, l = zy.zyfa_fwd(q8, k8, v8, return_lse=True, q_descale=qs, k_descale=ks, v_descale=vs)
+        torch.cuda.synchronize()
+        assert torch.equal(o, first) and torch.equal(l, flse), f"run {i} differs"
