@@ -26,6 +26,24 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X published dense MFMA peaks
 
+# name -> (workload number, dtype); workloads are defined in workloads/.
+CASES = {
+    "bf16_d192_s16384": (4, "bf16"),
+    "bf16_d128_gqa_s16384": (3, "bf16"),
+    "fp8_d128_gqa_s16384": (3, "fp8"),
+    "fp8_d192_s16384": (4, "fp8"),
+}
+HEADLINE = "bf16_d192_s16384"
+DESCRIPTIONS = {
+    "bf16_d192_s16384": "causal MLA-prefill form, bf16: batch 1, seqlen 16384, nheads 16 = nheads_k, d_qk 192, "
+                        "d_v 128, bhsd, q/k/v N(0,1)",
+    "bf16_d128_gqa_s16384": "causal GQA, bf16: batch 1, seqlen 16384, nheads 32, nheads_k 8, d 128, bshd, N(0,1)",
+    "fp8_d128_gqa_s16384": "causal GQA, fp8 e4m3 per-tensor pow2 descales: batch 1, seqlen 16384, nheads 32, "
+                           "nheads_k 8, d 128, bshd, N(0,1)",
+    "fp8_d192_s16384": "causal MLA-prefill form, fp8 e4m3: batch 1, seqlen 16384, nheads 16, d_qk 192, d_v 128, "
+                       "bhsd, N(0,1)",
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -34,6 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", default="", help="comma-separated subset of: " + ",".join(CASES))
     return ap.parse_args()
 
 
@@ -103,48 +122,33 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    results = {}
-
-    def stage(w):
-        q, k, v = generate(w)
-        return tuple(torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
-
-    # BF16, MLA-prefill shape at 16K (headline)
-    w4 = WORKLOADS[4]
-    q, k, v = stage(w4)
-    out = torch.empty(w4.shape("q")[:-1] + (w4.d_v,), dtype=torch.bfloat16, device=dev)
-    zy.zyfa_fwd(q, k, v, out, layout=w4.layout)
-    ms, _ = time_launches(lambda: zy.zyfa_fwd(q, k, v, out, layout=w4.layout), args.steps, args.warmup)
-    results["bf16_d192_s16384"] = (w4.flops(), ms)
-    del q, k, v, out
-
-    # BF16 on the GQA d=128 16K shape (context row)
-    w3 = WORKLOADS[3]
-    q, k, v = stage(w3)
-    out = torch.empty(w3.shape("q")[:-1] + (w3.d_v,), dtype=torch.bfloat16, device=dev)
-    ms3, _ = time_launches(lambda: zy.zyfa_fwd(q, k, v, out, layout=w3.layout), args.steps, args.warmup)
-    results["bf16_d128_gqa_s16384"] = (w3.flops(), ms3)
-
-    fp8 = {}
-    try:
-        q8, qs = zy.zyfa_fp8_quantize(q)
-        k8, ks = zy.zyfa_fp8_quantize(k)
-        v8, vs = zy.zyfa_fp8_quantize(v)
-        zy.zyfa_fwd(q8, k8, v8, out, layout=w3.layout, q_descale=qs, k_descale=ks, v_descale=vs)
+    cases = args.only.split(",") if args.only else list(CASES)
+    res = {}
+    for name in cases:
+        wid, dtype = CASES[name]
+        w = WORKLOADS[wid]
+        q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in generate(w))
+        out = torch.empty(w.shape("q")[:-1] + (w.d_v,), dtype=torch.bfloat16, device=dev)
+        if dtype == "bf16":
+            fn = lambda: zy.zyfa_fwd(q, k, v, out, layout=w.layout)
+        else:
+            (q8, qs), (k8, ks), (v8, vs) = (zy.zyfa_fp8_quantize(x) for x in (q, k, v))
+            fn = lambda: zy.zyfa_fwd(q8, k8, v8, out, layout=w.layout, q_descale=qs, k_descale=ks, v_descale=vs)
+            msq, _ = time_launches(lambda: [zy.zyfa_fp8_quantize(x, x8, xs) for x, x8, xs in
+                                            ((q, q8, qs), (k, k8, ks), (v, v8, vs))], args.steps, args.warmup)
+            res[name + "_quantize_qkv_ms"] = round(msq, 4)
+        fn()
         torch.cuda.synchronize()
-        msf, _ = time_launches(lambda: zy.zyfa_fwd(q8, k8, v8, out, layout=w3.layout, q_descale=qs,
-                                                   k_descale=ks, v_descale=vs), args.steps, args.warmup)
-        msq, _ = time_launches(lambda: (zy.zyfa_fp8_quantize(q, q8, qs), zy.zyfa_fp8_quantize(k, k8, ks),
-                                        zy.zyfa_fp8_quantize(v, v8, vs)), args.steps, args.warmup)
-        fp8 = {"fp8_d128_gqa_s16384_tflops": w3.flops() / (msf * 1e-3) / 1e12,
-               "fp8_d128_gqa_s16384_ms": msf, "fp8_quantize_qkv_ms": msq}
-    except zy.ZyfaError as e:
-        fp8 = {"fp8": f"not available: {e}"}
-    del q, k, v, out
+        ms, _ = time_launches(fn, args.steps, args.warmup)
+        tf = w.flops() / (ms * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 2), "ms": round(ms, 4),
+                     "pct_of_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2)}
+        del q, k, v, out
+        torch.cuda.empty_cache()
 
-    flops, ms = results["bf16_d192_s16384"]
-    tflops = flops / (ms * 1e-3) / 1e12
-    t3 = results["bf16_d128_gqa_s16384"][0] / (results["bf16_d128_gqa_s16384"][1] * 1e-3) / 1e12
+    head = HEADLINE if HEADLINE in res else cases[0]
+    tflops, ms = res[head]["tflops"], res[head]["ms"]
+    hdt = CASES[head][1]
     line = {
         "metric": "causal prefill attention TFLOP/s (bf16, fp8) at 16K tokens; % of MFMA peak",
         "value": round(tflops, 2),
@@ -156,18 +160,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": hdt,
         "data": "synthetic",
         "config": {
-            "workload": "causal MLA-prefill form: batch 1, seqlen 16384, nheads 16 = nheads_k, d_qk 192, d_v 128, "
-                        "bhsd, q/k/v N(0,1) bf16",
-            "global_batch": 1, "seq_len": 16384, "parallelism": "none (1 GPU)",
-            "pct_of_bf16_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2),
-            "bf16_d128_gqa_s16384_tflops": round(t3, 2),
-            **{k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in fp8.items()},
+            "workload": DESCRIPTIONS[head],
+            "global_batch": WORKLOADS[CASES[head][0]].batch, "seq_len": WORKLOADS[CASES[head][0]].seqlen,
+            "parallelism": "none (1 GPU)",
+            "cases": res,
         },
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS["bf16"],
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS["bf16"], 4), "traffic": None},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[hdt],
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS[hdt], 4), "traffic": None},
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

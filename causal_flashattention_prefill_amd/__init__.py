@@ -16,7 +16,9 @@ import ctypes
 import os
 from typing import Optional
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzyfa.so")
+# ZYFA_LIB selects another build of the same library (e.g. to compare two
+# builds on one machine); by default the in-tree libzyfa.so is loaded.
+LIB_PATH = os.environ.get("ZYFA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzyfa.so")
 
 LAYOUTS = {"bshd": 0, "bhsd": 1}
 DTYPE_BF16, DTYPE_FP8, DTYPE_FP32 = 0, 1, 2

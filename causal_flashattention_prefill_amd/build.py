@@ -26,6 +26,7 @@ HIPCC_FLAGS = [
     # packed fp32 instructions (v_pk_*_f32) are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    "-Wno-inline-asm",  # m0 is clobbered on purpose by the direct-to-LDS load asm
 ]
 
 

@@ -9,8 +9,8 @@
 //    (README, Kernel design: work distribution). Each wave owns 32 query
 //    rows (two 16-row groups) for the whole key loop.
 //  - Keys stream in 64-key tiles through a two-stage LDS ring filled by
-//    direct global-to-LDS loads; the loads of tile t+1 are issued before the
-//    MFMA work on tile t.
+//    direct global-to-LDS loads (buffer_load ... lds): the loads of tile t+1
+//    are issued before the MFMA work on tile t and waited for after it.
 //  - Scores are computed transposed, S^T = K Q^T, with K as the MFMA A
 //    operand (README, Kernel design: transposed scores), using
 //    v_mfma_f32_16x16x32_bf16. Lane (g, n) (g = lane/16, n = lane%16) then
@@ -20,13 +20,20 @@
 //  - O^T += V^T P^T with V^T read from LDS by ds_read_b64_tr_b16, which
 //    transposes 16-bit values during the read, so V is stored in LDS as it
 //    arrives from memory.
-//  - Online softmax in base 2 (log2(e) folded into the scale) with a lazy
-//    reference maximum: the reference moves only when some score passes it by
-//    kTau; one wave-wide ballot decides, and the rescale runs out of line
-//    (README, Kernel design: lazy rescaling).
-//  - The row sum is an fp32 sum of the unrounded probabilities, so that the
-//    LSE holds to ~1e-7 relative; P is rounded to bf16 (RNE) for the MFMA.
+//  - One barrier per key tile; the key loop is unrolled by the two ring
+//    stages so every LDS offset is an immediate.
+//  - Online softmax in base 2 (log2(e) folded into the scale, one FMA per
+//    score before the exponential) with a lazy reference maximum: it moves
+//    only when some score passes it by kTau; one wave-wide ballot decides,
+//    and the rescale runs out of line (README, Kernel design: lazy
+//    rescaling). The causal mask is applied on diagonal tiles only.
+//  - Row sums: with LSE requested, an fp32 sum of the unrounded
+//    probabilities (so the LSE holds to ~1e-7 relative); otherwise one MFMA
+//    of the bf16 P against ones per 32 keys, so the output is divided by the
+//    sum of exactly the rounded weights that multiply V.
 //  - Every conversion rounds to nearest even (README, Kernel design).
+#include <type_traits>
+
 #include "device_common.h"
 #include "zyfa_internal.h"
 
@@ -36,6 +43,7 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kTileQ = 256;
 constexpr int kTileK = 64;
+constexpr int kStages = 2;
 constexpr float kTau = 8.0f;           // lazy-rescale threshold, log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -43,7 +51,6 @@ template <int DQK, bool WITH_LSE>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnArgs a) {
   constexpr int DV = 128;
   constexpr int KCH = DQK / 8;                 // 16-byte chunks per K row
-  constexpr int VCH = DV / 8;                  // 16-byte chunks per V row
   constexpr int KPITCH = DQK * 2;              // bytes per K row in LDS
   constexpr int VPITCH = DV * 2;
   constexpr int KSWZ = (KCH % 16 == 0) ? 15 : 7;
@@ -55,7 +62,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   constexpr int VLD = VBYTES / 1024 / 8;
   static_assert(KLD * 8 * 1024 == KBYTES && VLD * 8 * 1024 == VBYTES, "tile split");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[kStages * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -64,6 +71,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   const int n = lane & 15;
   const int S = a.seqlen;
   const float sl2 = a.scale_log2;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   for (int it = 0; it < a.jobs_per_wg; ++it) {
     const int2 job = a.jobs[it * (int)gridDim.x + (int)blockIdx.x];
@@ -76,8 +84,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
     const char* kbase = (const char*)a.k.ptr + 2 * (b * a.k.stride_b + hk * a.k.stride_h);
     const char* vbase = (const char*)a.v.ptr + 2 * (b * a.v.stride_b + hk * a.v.stride_h);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, a.q_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, a.k_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, a.v_bytes);
+    const i32x4 rk = make_rsrc_words(kbase, a.k_bytes);
+    const i32x4 rv = make_rsrc_words(vbase, a.v_bytes);
     const int qrs = (int)(2 * a.q.stride_s);
     const int krs = (int)(2 * a.k.stride_s);
     const int vrs = (int)(2 * a.v.stride_s);
@@ -102,49 +110,48 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
           qf[qg][c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (qw0 + 16 * qg + n) * qrs + (32 * c + 8 * g) * 2));
 
       f32x4 o[2][8];
+      f32x4 lacc[2];
 #pragma unroll
-      for (int qg = 0; qg < 2; ++qg)
+      for (int qg = 0; qg < 2; ++qg) {
+        lacc[qg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       float mref[2] = {neg_inf(), neg_inf()};
       float lsum[2] = {0.f, 0.f};
 
-      // K/V tiles go straight from memory into LDS (buffer_load ... lds).
-      // Wave-instruction I fills bytes [1024 I, 1024 I + 1024) of a region;
-      // lane L's 16 bytes land at p = 1024 I + 16 L, which is row p / pitch,
-      // chunk slot (p % pitch) / 16, so the lane fetches the global chunk
-      // that belongs in that slot. K chunks are XOR-swizzled by row so the 16
-      // lanes that read one chunk column of 16 rows hit distinct banks; V
-      // chunks are swizzled by even values, keeping the 8-byte halves the
-      // transposing read needs intact.
-      auto issue_kv = [&](int kt, int st) {
-        char* ks = smem + st * STAGE;
+      // K/V tiles go straight from memory into LDS. Wave-instruction I fills
+      // bytes [1024 I, 1024 I + 1024) of a region; lane L's 16 bytes land at
+      // p = 1024 I + 16 L, which is row p / pitch, chunk slot (p % pitch) / 16,
+      // so the lane fetches the global chunk that belongs in that slot. K
+      // chunks are XOR-swizzled by row so the 16 lanes that read one chunk
+      // column of 16 rows hit distinct banks; V chunks are swizzled by even
+      // values, keeping the 8-byte halves the transposing read needs intact.
+      auto issue_kv = [&](int kt, char* stage) {
 #pragma unroll
         for (int u = 0; u < KLD; ++u) {
           const int I = wave * KLD + u;
           const int p = I * 1024 + lane * 16;
           const int row = p / KPITCH, x = ((p % KPITCH) >> 4) ^ (row & KSWZ);
-          buf_load16_lds(rk, (kt * kTileK + row) * krs + x * 16, ks + I * 1024);
+          dma16(rk, (kt * kTileK + row) * krs + x * 16, stage + I * 1024);
         }
 #pragma unroll
         for (int u = 0; u < VLD; ++u) {
           const int I = wave * VLD + u;
           const int p = I * 1024 + lane * 16;
           const int row = p / VPITCH, x = ((p % VPITCH) >> 4) ^ ((row & 7) << 1);
-          buf_load16_lds(rv, (kt * kTileK + row) * vrs + x * 16, ks + KBYTES + I * 1024);
+          dma16(rv, (kt * kTileK + row) * vrs + x * 16, stage + KBYTES + I * 1024);
         }
       };
 
-      issue_kv(0, 0);
-      wait_all_memory();
-      __syncthreads();
-
-      for (int kt = 0; kt < n_kt; ++kt) {
-        const int st = kt & 1;
-        if (kt + 1 < n_kt) issue_kv(kt + 1, st ^ 1);
+      // One key tile on ring stage ST: S^T = K Q^T, softmax, O^T += V^T P^T.
+      auto step = [&](auto st_c, int kt) {
+        constexpr int ST = decltype(st_c)::value;
+        char* const cur = smem + ST * STAGE;
+        char* const nxt = smem + (ST ^ 1) * STAGE;
+        const bool more = kt + 1 < n_kt;
+        if (more) issue_kv(kt + 1, nxt);
         if (kt <= kt_w) {
-          const char* ks = smem + st * STAGE;
-          const char* vs = ks + KBYTES;
           // ---- S^T = K Q^T
           f32x4 s[2][4];
 #pragma unroll
@@ -157,32 +164,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
             for (int kb = 0; kb < 4; ++kb) {
               const int row = 16 * kb + n;
               const int x = 4 * c + g;
-              const bf16x8 kf = lds_load<bf16x8>(ks + row * KPITCH + ((x ^ (row & KSWZ)) << 4));
+              const bf16x8 kf = lds_load<bf16x8>(cur + row * KPITCH + ((x ^ (row & KSWZ)) << 4));
 #pragma unroll
               for (int qg = 0; qg < 2; ++qg)
                 s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qg][c], s[qg][kb], 0, 0, 0);
             }
-          // ---- scale, causal mask (diagonal tiles only), lazy max
+          // ---- causal mask, on diagonal tiles only (kept a real branch)
           const int kbase = kt * kTileK;
-          const bool diag = kbase + kTileK - 1 > qw0;
+          if (__builtin_expect(kbase + kTileK - 1 > qw0, 0)) {
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg) {
+              const int q = qw0 + 16 * qg + n - kbase - 4 * g;
+#pragma unroll
+              for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (16 * kb + i > q) s[qg][kb][i] = neg_inf();
+            }
+          }
+          // ---- lazy max: a lane-local test and one ballot per tile
           float mx[2];
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) {
-            float m = neg_inf();
-            const int q = qw0 + 16 * qg + n;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                float v = s[qg][kb][i] * sl2;
-                if (diag && (kbase + 16 * kb + 4 * g + i > q)) v = neg_inf();
-                s[qg][kb][i] = v;
-                m = fmaxf(m, v);
-              }
-            mx[qg] = m;
+            float m = fmaxf(fmaxf(s[qg][0][0], s[qg][0][1]), s[qg][0][2]);
+            m = fmaxf(fmaxf(m, s[qg][0][3]), s[qg][1][0]);
+            m = fmaxf(fmaxf(m, s[qg][1][1]), s[qg][1][2]);
+            m = fmaxf(fmaxf(m, s[qg][1][3]), s[qg][2][0]);
+            m = fmaxf(fmaxf(m, s[qg][2][1]), s[qg][2][2]);
+            m = fmaxf(fmaxf(m, s[qg][2][3]), s[qg][3][0]);
+            m = fmaxf(fmaxf(m, s[qg][3][1]), s[qg][3][2]);
+            mx[qg] = fmaxf(m, s[qg][3][3]) * sl2;
           }
-          const bool need = (mx[0] > mref[0] + kTau) || (mx[1] > mref[1] + kTau);
-          if (wave_any(need)) {
+          if (__builtin_expect(wave_any((mx[0] > mref[0] + kTau) || (mx[1] > mref[1] + kTau)), 0)) {
+            // Keep this branch real: with f == 1 the multiplies are harmless,
+            // so the compiler would otherwise run them on every tile.
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg) {
               float rm = fmaxf(mx[qg], __shfl_xor(mx[qg], 16));
@@ -190,18 +207,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
               const float mn = fmaxf(mref[qg], rm);
               const float f = fast_exp2(mref[qg] - mn);
               lsum[qg] *= f;
+              lacc[qg] *= f;
 #pragma unroll
               for (int db = 0; db < 8; ++db) o[qg][db] *= f;
               mref[qg] = mn;
             }
           }
-          // ---- P = exp2(s - mref), fp32 row sum, RNE pack to bf16
-          // Operands are assembled as whole 32-bit words (two bf16 each):
-          // building them element by element from 16-bit values has been
-          // lowered incorrectly (every slot took the first element).
+          // ---- P = exp2(s * scale - m), RNE to bf16. Operands are assembled
+          // as whole 32-bit words: building them element by element from
+          // 16-bit values has been compiled incorrectly (every slot took
+          // element 0).
           bf16x8 pb[2][2];
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) {
+            const float nm = -mref[qg];
             float ls = 0.f;
             u32x4 w[2];
 #pragma unroll
@@ -209,28 +228,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
               f32x4 p;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                p[i] = fast_exp2(s[qg][kb][i] - mref[qg]);
-                ls += p[i];
+                p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, nm));
+                if (WITH_LSE) ls += p[i];
               }
               w[kb >> 1][2 * (kb & 1) + 0] = pack_bf16x2(p[0], p[1]);
               w[kb >> 1][2 * (kb & 1) + 1] = pack_bf16x2(p[2], p[3]);
             }
             pb[qg][0] = __builtin_bit_cast(bf16x8, w[0]);
             pb[qg][1] = __builtin_bit_cast(bf16x8, w[1]);
-            lsum[qg] += ls;
+            if (WITH_LSE) lsum[qg] += ls;
           }
-          // ---- O^T += V^T P^T
+          // ---- O^T += V^T P^T (and the row sum of the rounded P when no LSE)
 #pragma unroll
-          for (int db = 0; db < 8; ++db)
+          for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
+            for (int db = 0; db < 8; ++db) {
               u32x2 t[2];
 #pragma unroll
               for (int hf = 0; hf < 2; ++hf) {
                 const int row = 32 * kc + 16 * hf + 4 * g + (n >> 2);
-                const int dcol = 16 * db + 4 * (n & 3);
-                const int x = dcol >> 3;
-                const char* p = vs + row * VPITCH + ((x ^ ((row & 7) << 1)) << 4) + ((dcol >> 2) & 1) * 8;
+                const int x = 2 * db + ((n & 3) >> 1);
+                const char* p = cur + KBYTES + row * VPITCH + ((x ^ ((row & 7) << 1)) << 4) + (n & 1) * 8;
                 t[hf] = __builtin_bit_cast(u32x2, lds_read_tr16(p));
               }
               const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{t[0][0], t[0][1], t[1][0], t[1][1]});
@@ -238,17 +256,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
               for (int qg = 0; qg < 2; ++qg)
                 o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qg][kc], o[qg][db], 0, 0, 0);
             }
+          if (!WITH_LSE) {
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+              for (int kc = 0; kc < 2; ++kc)
+                lacc[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qg][kc], lacc[qg], 0, 0, 0);
+          }
         }
-        wait_all_memory();
+        if (more) wait_vm<0>();
         __syncthreads();
+      };
+
+      __syncthreads();   // the previous tile's last reads of the ring are done
+      issue_kv(0, smem);
+      wait_vm<0>();
+      __syncthreads();
+      for (int kt = 0; kt < n_kt; kt += 2) {
+        step(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
       }
 
       // ---- epilogue: O / l (RNE to bf16), LSE = ln2 * (m + log2 l)
       if (kt_w >= 0) {
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
-          float lt = lsum[qg] + __shfl_xor(lsum[qg], 16);
-          lt += __shfl_xor(lt, 32);
+          float lt;
+          if (WITH_LSE) {
+            lt = lsum[qg] + __shfl_xor(lsum[qg], 16);
+            lt += __shfl_xor(lt, 32);
+          } else {
+            lt = lacc[qg][0];
+          }
           const float inv = 1.0f / lt;
           const int q = qw0 + 16 * qg + n;
           if (q < S) {

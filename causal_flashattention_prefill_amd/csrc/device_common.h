@@ -47,6 +47,39 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, int off
 // direct-to-LDS loads) has completed.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Raw buffer resource as four scalar words (for inline assembly operands).
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, unsigned nbytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a & 0xFFFFFFFFull));
+  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r[3] = kBufferWord3;
+  return r;
+}
+
+// Direct global-to-LDS load issued as inline assembly, so the compiler does
+// not track it: otherwise it waits for every such load before any later LDS
+// read (it cannot tell which ring slot a read touches), which would expose
+// the full memory latency once per key tile. The caller orders these loads
+// with wait_vm() and barriers itself. Lane L's 16 bytes go to
+// lds_wave_base + 16 L (M0 holds the wave-uniform base); past the resource's
+// extent they are zero.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, int voff, const char* lds_wave_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) leaving the LDS and export counters alone (gfx9
+// encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <class T>
 __device__ __forceinline__ T lds_load(const char* p) {
   return *reinterpret_cast<const T*>(p);
