@@ -20,8 +20,8 @@
 //  - O^T += V^T P^T with V^T read from LDS by ds_read_b64_tr_b16, which
 //    transposes 16-bit values during the read, so V is stored in LDS as it
 //    arrives from memory.
-//  - One barrier per key tile; the key loop is unrolled by the two ring
-//    stages so every LDS offset is an immediate.
+//  - One barrier per key tile; at d_qk = 128 the key loop is unrolled by the
+//    two ring stages so every LDS offset is an immediate.
 //  - Online softmax in base 2 (log2(e) folded into the scale, one FMA per
 //    score before the exponential) with a lazy reference maximum: it moves
 //    only when some score passes it by kTau; one wave-wide ballot decides,
@@ -144,11 +144,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
         }
       };
 
-      // One key tile on ring stage ST: S^T = K Q^T, softmax, O^T += V^T P^T.
-      auto step = [&](auto st_c, int kt) {
-        constexpr int ST = decltype(st_c)::value;
-        char* const cur = smem + ST * STAGE;
-        char* const nxt = smem + (ST ^ 1) * STAGE;
+      // One key tile read from ring stage `cur` while the next streams into
+      // `nxt`: S^T = K Q^T, softmax, O^T += V^T P^T.
+      auto step = [&](char* const cur, char* const nxt, int kt) {
         const bool more = kt + 1 < n_kt;
         if (more) issue_kv(kt + 1, nxt);
         if (kt <= kt_w) {
@@ -272,9 +270,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       issue_kv(0, smem);
       wait_vm<0>();
       __syncthreads();
-      for (int kt = 0; kt < n_kt; kt += 2) {
-        step(std::integral_constant<int, 0>{}, kt);
-        if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
+      if (DQK == 128) {
+        // unrolled by the two stages: every LDS offset is an immediate
+        for (int kt = 0; kt < n_kt; kt += 2) {
+          step(smem, smem + STAGE, kt);
+          if (kt + 1 < n_kt) step(smem + STAGE, smem, kt + 1);
+        }
+      } else {
+        // d_qk = 192 keeps 48 registers of Q; a rolled loop leaves room
+        for (int kt = 0; kt < n_kt; ++kt) {
+          const int st = kt & 1;
+          step(smem + st * STAGE, smem + (st ^ 1) * STAGE, kt);
+        }
       }
 
       // ---- epilogue: O / l (RNE to bf16), LSE = ln2 * (m + log2 l)

@@ -9,7 +9,7 @@
 // Structure (shared with the BF16 kernel: persistent 8-wave workgroups, jobs
 // = pairs of 256-row query tiles, 32 query rows per wave, transposed scores):
 //  - Keys stream in 128-key tiles through a two-stage LDS ring filled by
-//    direct global-to-LDS loads.
+//    direct global-to-LDS loads issued one tile ahead.
 //  - S^T = K Q^T with v_mfma_scale_f32_16x16x128_f8f6f4 (neutral scales);
 //    the three descales and the softmax scale are folded into one base-2
 //    factor read from device memory at kernel start.
@@ -99,8 +99,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
     const char* kbase = (const char*)a.k.ptr + (b * a.k.stride_b + hk * a.k.stride_h);
     const char* vbase = (const char*)a.v.ptr + (b * a.v.stride_b + hk * a.v.stride_h);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, a.q_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, a.k_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, a.v_bytes);
+    const i32x4 rk = make_rsrc_words(kbase, a.k_bytes);
+    const i32x4 rv = make_rsrc_words(vbase, a.v_bytes);
     const int qrs = (int)a.q.stride_s;
     const int krs = (int)a.k.stride_s;
     const int vrs = (int)a.v.stride_s;
@@ -146,34 +146,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       //  K d 0..127:   row * 128 + ((c ^ ((row >> 1) & 7)) << 4)
       //  K d 128..191: row * 64  + ((c ^ ((row >> 2) & 3)) << 4)
       //  V:            row * 128 + ((c ^ ((row >> 1) & 7)) << 4)
-      auto issue_kv = [&](int kt, int st) {
-        char* base = smem + st * STAGE;
+      auto issue_kv = [&](int kt, char* base) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int I = wave * 2 + u;
           const int p = I * 1024 + lane * 16;
           const int row = p >> 7, x = ((p & 127) >> 4) ^ ((row >> 1) & 7);
-          buf_load16_lds(rk, (kt * kTileK + row) * krs + x * 16, base + I * 1024);
-          buf_load16_lds(rv, (kt * kTileK + row) * vrs + x * 16, base + KA_BYTES + KB_BYTES + I * 1024);
+          dma16(rk, (kt * kTileK + row) * krs + x * 16, base + I * 1024);
+          dma16(rv, (kt * kTileK + row) * vrs + x * 16, base + KA_BYTES + KB_BYTES + I * 1024);
         }
         if (D192) {
           const int p = wave * 1024 + lane * 16;
           const int row = p >> 6, x = ((p & 63) >> 4) ^ ((row >> 2) & 3);
-          buf_load16_lds(rk, (kt * kTileK + row) * krs + 128 + x * 16, base + KA_BYTES + wave * 1024);
+          dma16(rk, (kt * kTileK + row) * krs + 128 + x * 16, base + KA_BYTES + wave * 1024);
         }
       };
 
-      issue_kv(0, 0);
-      wait_all_memory();
-      __syncthreads();
-
-      for (int kt = 0; kt < n_kt; ++kt) {
-        const int st = kt & 1;
-        if (kt + 1 < n_kt) issue_kv(kt + 1, st ^ 1);
+      // One key tile read from ring stage `cur` while the next streams into `nxt`.
+      auto step = [&](char* const cur, char* const nxt, int kt) {
+        const bool more = kt + 1 < n_kt;
+        if (more) issue_kv(kt + 1, nxt);
         if (kt <= kt_w) {
-          const char* ka = smem + st * STAGE;
-          const char* kb2 = ka + KA_BYTES;
-          const char* vs = ka + KA_BYTES + KB_BYTES;
+          const char* ka = cur;
+          const char* kb2 = cur + KA_BYTES;
+          const char* vs = cur + KA_BYTES + KB_BYTES;
           // ---- S^T = K Q^T (8 blocks of 16 keys)
           f32x4 s[2][8];
 #pragma unroll
@@ -193,30 +189,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
               for (int qg = 0; qg < 2; ++qg) s[qg][kb] = mfma_fp8(kf2, qf2[qg], s[qg][kb], kE8M0One, kE8M0One);
             }
           }
-          // ---- scale, causal mask, lazy max
+          // ---- causal mask, on diagonal tiles only
           const int kbase = kt * kTileK;
-          const bool diag = kbase + kTileK - 1 > qw0;
-          float mx[2];
-#pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
-            float m = neg_inf();
-            const int q = qw0 + 16 * qg + n;
-#pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                float v = s[qg][kb][i] * sl2;
-                if (diag && (kbase + 16 * kb + 4 * g + i > q)) v = neg_inf();
-                s[qg][kb][i] = v;
-                m = fmaxf(m, v);
-              }
-            mx[qg] = m;
-          }
-          const bool need = (mx[0] > mref[0] + kTau) || (mx[1] > mref[1] + kTau);
-          if (wave_any(need)) {
+          if (__builtin_expect(kbase + kTileK - 1 > qw0, 0)) {
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg) {
-              float rm = fmaxf(mx[qg], __shfl_xor(mx[qg], 16));
+              const int q = qw0 + 16 * qg + n - kbase - 4 * g;
+#pragma unroll
+              for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (16 * kb + i > q) s[qg][kb][i] = neg_inf();
+            }
+          }
+          // ---- lane maxima of the raw scores per scale half (kb 0..3 and
+          // 4..7), lazy test and one ballot per tile
+          float m0[2], m1[2];
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            float a0 = fmaxf(fmaxf(s[qg][0][0], s[qg][0][1]), s[qg][0][2]);
+            float a1 = fmaxf(fmaxf(s[qg][4][0], s[qg][4][1]), s[qg][4][2]);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+              for (int i = (kb == 0 ? 3 : 0); i < 4; i += 2) {
+                if (i == 3) {
+                  a0 = fmaxf(a0, s[qg][kb][3]);
+                  a1 = fmaxf(a1, s[qg][kb + 4][3]);
+                } else {
+                  a0 = fmaxf(fmaxf(a0, s[qg][kb][i]), s[qg][kb][i + 1]);
+                  a1 = fmaxf(fmaxf(a1, s[qg][kb + 4][i]), s[qg][kb + 4][i + 1]);
+                }
+              }
+            }
+            m0[qg] = a0 * sl2;
+            m1[qg] = a1 * sl2;
+          }
+          const bool need = (fmaxf(m0[0], m1[0]) > mref[0] + kTau) || (fmaxf(m0[1], m1[1]) > mref[1] + kTau);
+          if (__builtin_expect(wave_any(need), 0)) {
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg) {
+              float rm = fmaxf(fmaxf(m0[qg], m1[qg]), __shfl_xor(fmaxf(m0[qg], m1[qg]), 16));
               rm = fmaxf(rm, __shfl_xor(rm, 32));
               const float mn = fmaxf(mref[qg], rm);
               const float f = fast_exp2(mref[qg] - mn);
@@ -231,17 +244,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
           int psc[2];
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) {
-            float h0 = 0.f, h1 = 0.f;   // largest p of blocks kb 0..3 and 4..7
-#pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(s[qg][kb][i] - mref[qg]);
-                s[qg][kb][i] = p;
-                if (kb < 4) h0 = fmaxf(h0, p); else h1 = fmaxf(h1, p);
-              }
-            // scale block of kb 0..3 is g/2, of kb 4..7 is 2 + g/2; each is
-            // shared with lane ^ 16 (the other half of the block)
+            const float nm = -mref[qg];
+            // largest p of each scale half, from the raw maxima; each half is
+            // shared with lane ^ 16 (the other half of the 32-key block)
+            float h0 = fast_exp2(m0[qg] + nm), h1 = fast_exp2(m1[qg] + nm);
             h0 = fmaxf(h0, __shfl_xor(h0, 16));
             h1 = fmaxf(h1, __shfl_xor(h1, 16));
             const float sc0 = pow2_floor(h0), sc1 = pow2_floor(h1);
@@ -251,8 +257,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
             const float mine = g == 0 ? sc0 : (g == 3 ? sc1 : other);
             psc[qg] = (int)(__builtin_bit_cast(unsigned, mine) >> 23);
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
-              pf[qg][kb] = (int)cvt4_fp8(s[qg][kb][0], s[qg][kb][1], s[qg][kb][2], s[qg][kb][3], kb < 4 ? sc0 : sc1);
+            for (int kb = 0; kb < 8; ++kb) {
+              f32x4 p;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, nm));
+              pf[qg][kb] = (int)cvt4_fp8(p[0], p[1], p[2], p[3], kb < 4 ? sc0 : sc1);
+            }
           }
           // ---- row sum of the rounded P on the matrix unit
 #pragma unroll
@@ -277,8 +287,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
             for (int qg = 0; qg < 2; ++qg) o[qg][db] = mfma_fp8(vf, pf[qg], o[qg][db], kE8M0One, psc[qg]);
           }
         }
-        wait_all_memory();
+        if (more) wait_vm<0>();
         __syncthreads();
+      };
+
+      __syncthreads();   // the previous tile's last reads of the ring are done
+      issue_kv(0, smem);
+      wait_vm<0>();
+      __syncthreads();
+      for (int kt = 0; kt < n_kt; ++kt) {
+        const int st = kt & 1;
+        step(smem + st * STAGE, smem + (st ^ 1) * STAGE, kt);
       }
 
       // ---- epilogue: O * dv / l (RNE to bf16), LSE = ln2 * (m + log2 l)
