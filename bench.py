@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="", help="comma-separated subset of: " + ",".join(CASES))
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -123,6 +125,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cases = args.only.split(",") if args.only else list(CASES)
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     res = {}
     for name in cases:
         wid, dtype = CASES[name]
