@@ -145,15 +145,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // 16-byte chunks XOR-swizzled by row:
       //  K d 0..127:   row * 128 + ((c ^ ((row >> 1) & 7)) << 4)
       //  K d 128..191: row * 64  + ((c ^ ((row >> 2) & 3)) << 4)
-      //  V:            row * 128 + ((c ^ ((row >> 1) & 7)) << 4)
+      //  V:            row * 128 + ((c ^ (((row >> 1) ^ (row >> 2)) & 7)) << 4)
+      // The V swizzle keeps the eight rows of each transposing read (rows 16
+      // apart among them) on distinct banks.
       auto issue_kv = [&](int kt, char* base) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int I = wave * 2 + u;
           const int p = I * 1024 + lane * 16;
-          const int row = p >> 7, x = ((p & 127) >> 4) ^ ((row >> 1) & 7);
-          dma16(rk, (kt * kTileK + row) * krs + x * 16, base + I * 1024);
-          dma16(rv, (kt * kTileK + row) * vrs + x * 16, base + KA_BYTES + KB_BYTES + I * 1024);
+          const int row = p >> 7, slot = (p & 127) >> 4;
+          dma16(rk, (kt * kTileK + row) * krs + (slot ^ ((row >> 1) & 7)) * 16, base + I * 1024);
+          dma16(rv, (kt * kTileK + row) * vrs + (slot ^ (((row >> 1) ^ (row >> 2)) & 7)) * 16,
+                base + KA_BYTES + KB_BYTES + I * 1024);
         }
         if (D192) {
           const int p = wave * 1024 + lane * 16;
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
               // 16db + 8hh .. +7
               const int r = n >> 1, hh = n & 1;
               const int row = 32 * t + 16 * (r >> 2) + 4 * g + (r & 3);
-              const char* p = vs + row * 128 + ((db ^ ((row >> 1) & 7)) << 4) + hh * 8;
+              const char* p = vs + row * 128 + ((db ^ (((row >> 1) ^ (row >> 2)) & 7)) << 4) + hh * 8;
               const i32x2 w = lds_read_tr8(p);
               vf[2 * t] = w[0];
               vf[2 * t + 1] = w[1];
