@@ -98,7 +98,7 @@ def test_job_table_covers_every_tile_once(B, S, H, Hk):
 
 def test_job_pairs_have_equal_work():
     tq, nw, jp, table = zy.zyfa_plan_jobs(1, 16384, 32, 8)
-    n = 16384 // tq
+    n = -(-16384 // tq)
     for bh, i in table.reshape(-1, 2):
         if bh >= 0:
             assert (i + 1) + (n - 1 - i + 1) == n + 1
@@ -107,8 +107,8 @@ def test_job_pairs_have_equal_work():
 def test_job_table_xcd_locality():
     # in each table row, the workgroups of one XCD (blockIdx % 8) hold
     # consecutive jobs, so at most two heads per XCD per row
-    tq, nw, jp, table = zy.zyfa_plan_jobs(1, 16384, 32, 8)
-    assert nw == 256 and jp == 4
+    tq, nw, jp, table = zy.zyfa_plan_jobs(1, 16384, 32, 8, dtype=zy.DTYPE_FP8)
+    assert tq == 256 and nw == 256 and jp == 4
     for r in range(jp):
         for x in range(8):
             heads = {int(table[r, w, 0]) for w in range(x, nw, 8)}
