@@ -55,7 +55,135 @@ def parse():
     ap.add_argument("--only", default="", help="comma-separated subset of: " + ",".join(CASES))
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference for HBM byte counters)")
+    ap.add_argument("--sustain-seconds", type=float, default=3.0,
+                    help="seconds of back-to-back headline launches before the sustained-clock reading (0: skip)")
     return ap.parse_args()
+
+
+# Sources that decide the code and launch shape of each attention kernel; a
+# stored counter reading is used only while their hash is unchanged.
+PKG = os.path.join(ROOT, "causal_flashattention_prefill_amd", "csrc")
+COMMON_SOURCES = ["device_common.h", "zyfa_internal.h", "api.cpp", "plan.cpp", "plan.h"]
+KERNEL_SOURCES = {"bf16": ["attn_bf16.hip"] + COMMON_SOURCES, "fp8": ["attn_fp8.hip"] + COMMON_SOURCES}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash(dtype: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[dtype]:
+        with open(os.path.join(PKG, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(name: str, dtype: str):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE
+    reading of this case, each divided by the factor the same counter showed
+    for a plain copy of known size; None when there is no reading or the
+    kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)[name]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash(dtype):
+        return None
+    return rec["fetch_kib"] * 1024 / rec["copy_fetch_factor"] + rec["write_kib"] * 1024 / rec["copy_write_factor"]
+
+
+class PowerClockSampler:
+    """Samples the GFX clock and socket power of the GPU behind cuda:0 with
+    amdsmi from a host thread; empty readings if amdsmi is unavailable."""
+
+    def __init__(self, period_s: float = 0.05):
+        import threading
+        self.period, self.clk, self.pw, self.err = period_s, [], [], None
+        self._stop = threading.Event()
+        self._thr = threading.Thread(target=self._run, daemon=True)
+        self._handle = None
+        try:
+            import amdsmi
+            import torch
+            amdsmi.amdsmi_init()
+            props = torch.cuda.get_device_properties(0)
+            want = (getattr(props, "pci_domain_id", 0), props.pci_bus_id, props.pci_device_id)
+            for hnd in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(hnd)  # "dddd:bb:dd.f"
+                dom, bus, devfn = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(devfn.split(".")[0], 16)) == want:
+                    self._handle = hnd
+            if self._handle is None:
+                self.err = "no amdsmi device matches cuda:0"
+            self._smi = amdsmi
+        except Exception as e:  # noqa: BLE001 - a missing reading is reported, not fatal
+            self.err = f"amdsmi unavailable: {e}"
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+        clk = m.get("current_gfxclk")
+        if not isinstance(clk, (int, float)):
+            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+            clk = sum(clks) / len(clks) if clks else None
+        pw = m.get("current_socket_power")
+        if not isinstance(pw, (int, float)):
+            pw = m.get("average_socket_power")
+        return clk, pw if isinstance(pw, (int, float)) else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                c, p = self._read()
+                if c is not None:
+                    self.clk.append(c)
+                if p is not None:
+                    self.pw.append(p)
+            except Exception as e:  # noqa: BLE001
+                self.err = f"amdsmi read failed: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._handle is not None:
+            self._thr.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thr.is_alive():
+            self._thr.join()
+
+
+def median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2] if xs else None
+
+
+def sustained(fn, flops: float, seconds: float):
+    """Back-to-back launches of fn for `seconds`, then 20 more timed with
+    events; GFX clock and socket power sampled over the last half of it."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    t_half = t_end - seconds / 2
+    n = 0
+    while time.perf_counter() < t_half:  # first half: heat up
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    with PowerClockSampler() as smp:
+        while time.perf_counter() < t_end:
+            fn()
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+        ms, _ = time_launches(fn, 20, 0)
+    rec = {"seconds": seconds, "launches": n + 20, "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "ms": round(ms, 4), "gfxclk_mhz": median(smp.clk), "socket_power_w": median(smp.pw),
+           "samples": len(smp.clk)}
+    if smp.err:
+        rec["note"] = smp.err
+    return rec
 
 
 def time_launches(fn, steps, warmup):
@@ -126,12 +254,17 @@ def main():
     torch.cuda.set_device(dev)
     cases = args.only.split(",") if args.only else list(CASES)
     if args.copy_mib:
+        # reference for the byte counters: a device-to-device copy of a
+        # source that has been written first
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        src.fill_(0x5A)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
     res = {}
+    sustain = None
     for name in cases:
         wid, dtype = CASES[name]
         w = WORKLOADS[wid]
@@ -149,8 +282,12 @@ def main():
         torch.cuda.synchronize()
         ms, _ = time_launches(fn, args.steps, args.warmup)
         tf = w.flops() / (ms * 1e-3) / 1e12
+        tr = stored_traffic(name, dtype)
         res[name] = {"tflops": round(tf, 2), "ms": round(ms, 4),
-                     "pct_of_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2)}
+                     "pct_of_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
+                     "hbm_traffic_bytes": None if tr is None else int(tr)}
+        if name == (HEADLINE if HEADLINE in cases else cases[0]) and args.sustain_seconds > 0:
+            sustain = sustained(fn, w.flops(), args.sustain_seconds)
         del q, k, v, out
         torch.cuda.empty_cache()
 
@@ -177,8 +314,11 @@ def main():
             "cases": res,
         },
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[hdt],
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS[hdt], 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS[hdt], 4),
+                     "traffic": res[head]["hbm_traffic_bytes"]},
     }
+    if sustain is not None:
+        line["sustained"] = sustain
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

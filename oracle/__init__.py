@@ -11,7 +11,9 @@ arithmetic (the bf16 and e4m3fn codecs, the power-of-two quantizer).
 Sources (cited by page title and section):
 - "ZYFA" README (GitHub page of Zyphra/zyfa): Usage (LSE, descales,
   padding), Supported configurations (formats, head dims, GQA), Accuracy
-  (fp64 attention on the same quantized inputs), Kernel design (rounding).
+  (fp64 attention on the same quantized inputs), Kernel design (rounding;
+  lazy rescaling, per-block scaling, lean P and the row sum for the FP8
+  probability rounding in fp8_p.py).
 
 Parity pins for every function live in tests/test_oracle_*.py and
 tests/golden/. No function here is "parity unpinned".
@@ -20,9 +22,10 @@ from .codecs import (bf16_round, bf16_decode, bf16_encode_bits, e4m3fn_decode,
                      e4m3fn_encode, E4M3FN_MAX)
 from .quantize import fp8_quantize_ref
 from .attention import causal_attention_ref, causal_probs_ref, causal_attention_rows_ref
+from .fp8_p import fp8_attention_rows_ref
 
 __all__ = [
     "bf16_round", "bf16_decode", "bf16_encode_bits", "e4m3fn_decode", "e4m3fn_encode",
     "E4M3FN_MAX", "fp8_quantize_ref", "causal_attention_ref", "causal_probs_ref",
-    "causal_attention_rows_ref",
+    "causal_attention_rows_ref", "fp8_attention_rows_ref",
 ]
