@@ -27,8 +27,11 @@ ZYFA_OK = 0
 STATUS = {
     "ZYFA_ERR_NULL": -1, "ZYFA_ERR_SHAPE": -2, "ZYFA_ERR_HEADDIM": -3, "ZYFA_ERR_GQA": -4,
     "ZYFA_ERR_DTYPE": -5, "ZYFA_ERR_LAYOUT": -6, "ZYFA_ERR_DESCALE": -7, "ZYFA_ERR_CAPTURE": -8,
-    "ZYFA_ERR_HIP": -9, "ZYFA_ERR_RANGE": -10, "ZYFA_ERR_ALIGN": -11,
+    "ZYFA_ERR_HIP": -9, "ZYFA_ERR_RANGE": -10, "ZYFA_ERR_ALIGN": -11, "ZYFA_ERR_PMODE": -12,
 }
+# FP8 probability modes (zyfa_p_mode): default = lean P below the diagonal at
+# d_qk 128, exact P at d_qk 192.
+P_MODES = {"default": 0, "exact": 1, "lean": 2}
 
 _lib = None
 _lib_err: Optional[str] = None
@@ -52,7 +55,7 @@ def lib() -> ctypes.CDLL:
     fwd_args = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp]
     L.zyfa_fwd.argtypes = fwd_args + [vp]
     L.zyfa_fwd.restype = i
-    L.zyfa_fwd_ex.argtypes = fwd_args + [f, vp]
+    L.zyfa_fwd_ex.argtypes = fwd_args + [f, i, vp]
     L.zyfa_fwd_ex.restype = i
     L.zyfa_prepare.argtypes = [i, i, i, i, i, i, i, i, i, vp]
     L.zyfa_prepare.restype = i
@@ -110,10 +113,12 @@ def _dims(q, k, v, layout: str):
 
 def zyfa_fwd(q, k, v, out=None, lse=None, *, layout: str = "bshd", return_lse: bool = False,
              q_descale=None, k_descale=None, v_descale=None, softmax_scale: Optional[float] = None,
-             stream=None):
+             p_mode: str = "default", stream=None):
     """Causal forward attention. q, k, v: contiguous CUDA tensors (bf16, or
-    float8_e4m3fn / uint8 codes with fp32 device descales). Returns out, or
-    (out, lse) when return_lse (or an lse tensor is passed)."""
+    float8_e4m3fn / uint8 codes with fp32 device descales). p_mode selects
+    the FP8 probability rounding ("default", "exact", "lean"; see
+    zyfa_p_mode in zyfa.h). Returns out, or (out, lse) when return_lse (or
+    an lse tensor is passed)."""
     import torch
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {list(LAYOUTS)}")
@@ -130,10 +135,13 @@ def zyfa_fwd(q, k, v, out=None, lse=None, *, layout: str = "bshd", return_lse: b
     L = lib()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S, H, Hk, dqk, dv, LAYOUTS[layout], dt,
             _ptr(q_descale), _ptr(k_descale), _ptr(v_descale))
-    if softmax_scale is None:
+    if p_mode not in P_MODES:
+        raise ValueError(f"p_mode must be one of {list(P_MODES)}")
+    if softmax_scale is None and p_mode == "default":
         rc = L.zyfa_fwd(*args, _stream(stream))
     else:
-        rc = L.zyfa_fwd_ex(*args, float(softmax_scale), _stream(stream))
+        rc = L.zyfa_fwd_ex(*args, 0.0 if softmax_scale is None else float(softmax_scale), P_MODES[p_mode],
+                           _stream(stream))
     _check(rc, "zyfa_fwd")
     return (out, lse) if lse is not None else out
 

@@ -112,9 +112,10 @@ void strides(int layout, int seqlen, int heads, int dim, long long* sb, long lon
 
 int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen,
              int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale,
-             const float* k_descale, const float* v_descale, float softmax_scale, void* stream_) {
+             const float* k_descale, const float* v_descale, float softmax_scale, int p_mode, void* stream_) {
   int rc = check_shape(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype);
   if (rc) return rc;
+  if (p_mode != ZYFA_P_DEFAULT && p_mode != ZYFA_P_EXACT && p_mode != ZYFA_P_LEAN) return ZYFA_ERR_PMODE;
   if (!q || !k || !v || !out) return ZYFA_ERR_NULL;
   if (dtype == ZYFA_DTYPE_FP8_E4M3FN && (!q_descale || !k_descale || !v_descale)) return ZYFA_ERR_DESCALE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
@@ -168,7 +169,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   if (dtype == ZYFA_DTYPE_BF16)
     e = launch_attn_bf16(a, d_qk, lse != nullptr, plan->num_wgs, stream);
   else
-    e = launch_attn_fp8(a, d_qk, lse != nullptr, plan->num_wgs, stream);
+    e = launch_attn_fp8(a, d_qk, lse != nullptr,
+                        p_mode == ZYFA_P_LEAN || (p_mode == ZYFA_P_DEFAULT && d_qk == 128), plan->num_wgs, stream);
   return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
 }
 
@@ -183,14 +185,14 @@ int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale, const float* k_descale,
              const float* v_descale, void* stream) {
   return fwd_impl(q, k, v, out, lse, batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype, q_descale, k_descale,
-                  v_descale, 0.f, stream);
+                  v_descale, 0.f, ZYFA_P_DEFAULT, stream);
 }
 
 int zyfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen,
                 int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale,
-                const float* k_descale, const float* v_descale, float softmax_scale, void* stream) {
+                const float* k_descale, const float* v_descale, float softmax_scale, int p_mode, void* stream) {
   return fwd_impl(q, k, v, out, lse, batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype, q_descale, k_descale,
-                  v_descale, softmax_scale, stream);
+                  v_descale, softmax_scale, p_mode, stream);
 }
 
 int zyfa_prepare(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype,
@@ -243,6 +245,7 @@ const char* zyfa_status_string(int status) {
     case ZYFA_ERR_HIP: return "a HIP runtime call failed";
     case ZYFA_ERR_RANGE: return "a (batch, head) slice is too large for 32-bit offsets";
     case ZYFA_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
+    case ZYFA_ERR_PMODE: return "unknown FP8 probability mode";
     default: return "unknown status";
   }
 }

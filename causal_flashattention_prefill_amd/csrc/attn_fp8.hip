@@ -13,19 +13,32 @@
 //  - S^T = K Q^T with v_mfma_scale_f32_16x16x128_f8f6f4 (neutral scales);
 //    the three descales and the softmax scale are folded into one base-2
 //    factor read from device memory at kernel start.
-//  - P is exact: p = exp2(s - m_ref), then per-block power-of-two scaling
-//    (README, Kernel design: per-block scaling): each 32-key block of a query
-//    row (the scale block of the scaled MFMA) is divided by 2^floor(log2 of
-//    its largest p) while rounding to e4m3fn (v_cvt_scalef32_pk_fp8_f32,
-//    RNE), so the block's largest value lands in [1, 2) and stays normal.
-//    The PV MFMA multiplies the same power of two back in through its B-scale
-//    operand at no extra cost.
+//  - Per-block power-of-two scaling (README, Kernel design: per-block
+//    scaling): each 32-key block of a query row (the scale block of the
+//    scaled MFMA) gets e_b = floor(block max - m_ref) in base-2 units, so its
+//    largest probability divided by 2^e_b lies in [1, 2) and stays normal;
+//    the PV MFMA multiplies 2^e_b back in through its B-scale operand.
+//  - Exact P: p = exp2(s - m_ref) rounded to e4m3fn as p / 2^e_b
+//    (v_cvt_scalef32_pk_fp8_f32, RNE).
+//  - Lean P (README, Kernel design: lean P): the e4m3fn code of a positive
+//    value grows by 8 per doubling, so the code of 2^y is written directly as
+//    RNE(8 y + C), clamped to 0..255 by v_cvt_pk_u8_f32 (one FMA and one
+//    conversion per score instead of an exponential and an FP8 conversion).
+//    C = 56 + 8 log2(2 ln^2 2) makes the piecewise-linear value unbiased.
+//    Lean P is used on key tiles below the diagonal; the diagonal tile, which
+//    holds every key of the rows with fewest keys, keeps exact P.
 //  - The row sum is one extra MFMA of the rounded, scaled P against a block
 //    of ones (README, Kernel design: row sum on the matrix unit), so the
 //    denominator is the sum of exactly the values that multiply V.
 //  - V^T is read from LDS with ds_read_b64_tr_b8 (transposes bytes during
 //    the read), so V is stored as it arrives.
-//  - Lazy rescale of the running maximum with one wave ballot, as in BF16.
+//  - Lazy rescale (README, Kernel design: lazy rescaling): a row's reference
+//    moves to the tile maximum only when that exceeds it by more than kTau;
+//    one wave ballot decides whether any row of the wave moves.
+//  - K rows are written to LDS with key bits [5:4] and [3:2] swapped, so the
+//    score layout of the MFMA puts key 16g + 4c + i (and 64 + ...) in lane
+//    group g: the MFMA k index of P equals the key's offset in the tile and
+//    each E8M0 scale block is 32 consecutive keys.
 //  - d_qk = 192 adds one MFMA per score block over d 128..191 with the
 //    remaining half of the K dimension zero.
 //
@@ -46,6 +59,14 @@ constexpr int kTileK = 128;
 constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kE8M0One = 127;           // E8M0 scale 2^0
+// Lean-P constant 56 + 8 log2(2 ln(2)^2).
+constexpr float kLeanC = 55.539734f;
+
+// 16-byte chunk swizzle of V row r: bits 1..2 and 4 of r.
+__device__ __forceinline__ int vsw(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
+
+// Key held by LDS row r of a K tile: bits [5:4] and [3:2] of r swapped.
+__device__ __forceinline__ int kswap(int r) { return (r & ~0x3C) | ((r & 0x30) >> 2) | ((r & 0x0C) << 2); }
 
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
@@ -65,7 +86,7 @@ __device__ __forceinline__ unsigned cvt4_fp8(float a, float b, float c, float d,
   return __builtin_bit_cast(unsigned, w);
 }
 
-template <int DQK, bool WITH_LSE>
+template <int DQK, bool WITH_LSE, bool LEAN>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArgs a) {
   constexpr int DV = 128;
   constexpr bool D192 = DQK == 192;
@@ -141,27 +162,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       }
       float mref[2] = {neg_inf(), neg_inf()};
 
-      // Direct global-to-LDS tile loads (see the BF16 kernel); LDS layouts,
-      // 16-byte chunks XOR-swizzled by row:
+      // Direct global-to-LDS tile loads (see the BF16 kernel); K row r of the
+      // LDS tile holds key kswap(r), V row r holds key r; 16-byte chunks
+      // XOR-swizzled by row:
       //  K d 0..127:   row * 128 + ((c ^ ((row >> 1) & 7)) << 4)
       //  K d 128..191: row * 64  + ((c ^ ((row >> 2) & 3)) << 4)
-      //  V:            row * 128 + ((c ^ (((row >> 1) ^ (row >> 2)) & 7)) << 4)
-      // The V swizzle keeps the eight rows of each transposing read (rows 16
-      // apart among them) on distinct banks.
+      //  V:            row * 128 + ((c ^ vsw(row)) << 4)
+      // The V swizzle puts the sixteen rows that a half-wave of each
+      // transposing read touches (8 consecutive keys in each of two lane
+      // groups) on distinct banks, and does not depend on the read index t.
       auto issue_kv = [&](int kt, char* base) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int I = wave * 2 + u;
           const int p = I * 1024 + lane * 16;
           const int row = p >> 7, slot = (p & 127) >> 4;
-          dma16(rk, (kt * kTileK + row) * krs + (slot ^ ((row >> 1) & 7)) * 16, base + I * 1024);
-          dma16(rv, (kt * kTileK + row) * vrs + (slot ^ (((row >> 1) ^ (row >> 2)) & 7)) * 16,
+          dma16(rk, (kt * kTileK + kswap(row)) * krs + (slot ^ ((row >> 1) & 7)) * 16, base + I * 1024);
+          dma16(rv, (kt * kTileK + row) * vrs + (slot ^ vsw(row)) * 16,
                 base + KA_BYTES + KB_BYTES + I * 1024);
         }
         if (D192) {
           const int p = wave * 1024 + lane * 16;
           const int row = p >> 6, x = ((p & 63) >> 4) ^ ((row >> 2) & 3);
-          dma16(rk, (kt * kTileK + row) * krs + 128 + x * 16, base + KA_BYTES + wave * 1024);
+          dma16(rk, (kt * kTileK + kswap(row)) * krs + 128 + x * 16, base + KA_BYTES + wave * 1024);
         }
       };
 
@@ -192,21 +215,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
               for (int qg = 0; qg < 2; ++qg) s[qg][kb] = mfma_fp8(kf2, qf2[qg], s[qg][kb], kE8M0One, kE8M0One);
             }
           }
-          // ---- causal mask, on diagonal tiles only
+          // ---- causal mask, on the diagonal tile only; score (kb, i) of lane
+          // group g is key 64 (kb / 4) + 16 g + 4 (kb % 4) + i of the tile
           const int kbase = kt * kTileK;
-          if (__builtin_expect(kbase + kTileK - 1 > qw0, 0)) {
+          const bool diag = kbase + kTileK - 1 > qw0;
+          if (__builtin_expect(diag, 0)) {
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg) {
-              const int q = qw0 + 16 * qg + n - kbase - 4 * g;
+              const int q = qw0 + 16 * qg + n - kbase - 16 * g;
 #pragma unroll
               for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                  if (16 * kb + i > q) s[qg][kb][i] = neg_inf();
+                  if (64 * (kb >> 2) + 4 * (kb & 3) + i > q) s[qg][kb][i] = neg_inf();
             }
           }
-          // ---- lane maxima of the raw scores per scale half (kb 0..3 and
-          // 4..7), lazy test and one ballot per tile
+          // ---- lane maxima of the raw scores per scale half (kb 0..3: keys
+          // 16g..16g+15, kb 4..7: keys 64+16g..), lazy test and one ballot
+          // per tile
           float m0[2], m1[2];
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) {
@@ -234,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
             for (int qg = 0; qg < 2; ++qg) {
               float rm = fmaxf(fmaxf(m0[qg], m1[qg]), __shfl_xor(fmaxf(m0[qg], m1[qg]), 16));
               rm = fmaxf(rm, __shfl_xor(rm, 32));
-              const float mn = fmaxf(mref[qg], rm);
+              const float mn = rm > mref[qg] + kTau ? rm : mref[qg];
               const float f = fast_exp2(mref[qg] - mn);
               lacc[qg] *= f;
 #pragma unroll
@@ -242,29 +268,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
               mref[qg] = mn;
             }
           }
-          // ---- exact P, per-block power-of-two scale, RNE to e4m3fn
+          // ---- P codes and per-block exponents
           i32x8 pf[2];
           int psc[2];
+          const bool lean = LEAN && !diag;
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) {
-            const float nm = -mref[qg];
-            // largest p of each scale half, from the raw maxima; each half is
-            // shared with lane ^ 16 (the other half of the 32-key block)
-            float h0 = fast_exp2(m0[qg] + nm), h1 = fast_exp2(m1[qg] + nm);
-            h0 = fmaxf(h0, __shfl_xor(h0, 16));
-            h1 = fmaxf(h1, __shfl_xor(h1, 16));
-            const float sc0 = pow2_floor(h0), sc1 = pow2_floor(h1);
-            // lane 16*b + n supplies the scale of block b: groups 1 and 2
-            // swap the maxima they do not hold themselves
-            const float other = __shfl_xor((g & 1) ? sc1 : sc0, 48);
-            const float mine = g == 0 ? sc0 : (g == 3 ? sc1 : other);
-            psc[qg] = (int)(__builtin_bit_cast(unsigned, mine) >> 23);
+            // block maxima: the 32-key block of half 0 (1) is held by lane
+            // groups g and g ^ 1
+            const float b0 = fmaxf(m0[qg], __shfl_xor(m0[qg], 16));
+            const float b1 = fmaxf(m1[qg], __shfl_xor(m1[qg], 16));
+            const float e0 = fmaxf(floorf(b0 - mref[qg]), -126.0f);
+            const float e1 = fmaxf(floorf(b1 - mref[qg]), -126.0f);
+            // lane 16 b + n supplies the scale of block b: groups 1 and 2
+            // swap the exponents they do not hold themselves
+            const float other = __shfl_xor((g & 1) ? e1 : e0, 48);
+            const float mine = g == 0 ? e0 : (g == 3 ? e1 : other);
+            psc[qg] = (int)mine + 127;
+            if (lean) {
+              const float c8 = 8.0f * sl2;
+              const float o0 = kLeanC - 8.0f * (mref[qg] + e0);
+              const float o1 = kLeanC - 8.0f * (mref[qg] + e1);
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) {
-              f32x4 p;
+              for (int kb = 0; kb < 8; ++kb) {
+                const float o = kb < 4 ? o0 : o1;
+                unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[qg][kb][0], c8, o), 0, 0u);
+                w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[qg][kb][1], c8, o), 1, w);
+                w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[qg][kb][2], c8, o), 2, w);
+                w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[qg][kb][3], c8, o), 3, w);
+                pf[qg][kb] = (int)w;
+              }
+            } else {
+              const float nm = -mref[qg];
+              const float sc0 = __builtin_bit_cast(float, (unsigned)((int)e0 + 127) << 23);
+              const float sc1 = __builtin_bit_cast(float, (unsigned)((int)e1 + 127) << 23);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, nm));
-              pf[qg][kb] = (int)cvt4_fp8(p[0], p[1], p[2], p[3], kb < 4 ? sc0 : sc1);
+              for (int kb = 0; kb < 8; ++kb) {
+                f32x4 p;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, nm));
+                pf[qg][kb] = (int)cvt4_fp8(p[0], p[1], p[2], p[3], kb < 4 ? sc0 : sc1);
+              }
             }
           }
           // ---- row sum of the rounded P on the matrix unit
@@ -276,12 +320,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
             i32x8 vf;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              // rows of this 8-key read: byte e of lane group g is key
-              // 32t + 16*(e/4) + 4g + e%4; lane 2r+hh supplies row r, columns
+              // byte 8t + r of lane group g is key 64 (t / 2) + 16 g +
+              // 8 (t % 2) + r; lane 2r + hh supplies that row, columns
               // 16db + 8hh .. +7
               const int r = n >> 1, hh = n & 1;
-              const int row = 32 * t + 16 * (r >> 2) + 4 * g + (r & 3);
-              const char* p = vs + row * 128 + ((db ^ (((row >> 1) ^ (row >> 2)) & 7)) << 4) + hh * 8;
+              const int row = 64 * (t >> 1) + 16 * g + 8 * (t & 1) + r;
+              const char* p = vs + row * 128 + ((db ^ vsw(row)) << 4) + hh * 8;
               const i32x2 w = lds_read_tr8(p);
               vf[2 * t] = w[0];
               vf[2 * t + 1] = w[1];
@@ -329,14 +373,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
 
 }  // namespace
 
-hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, int grid, hipStream_t s) {
+template <int DQK, bool LEAN>
+static void launch_fp8(const AttnArgs& a, bool with_lse, dim3 gd, dim3 bd, hipStream_t s) {
+  if (with_lse) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, true, LEAN>), gd, bd, 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, false, LEAN>), gd, bd, 0, s, a);
+}
+
+hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean, int grid, hipStream_t s) {
   const dim3 gd(grid), bd(kThreads);
   if (d_qk == 128) {
-    if (with_lse) hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false>), gd, bd, 0, s, a);
+    if (lean) launch_fp8<128, true>(a, with_lse, gd, bd, s);
+    else launch_fp8<128, false>(a, with_lse, gd, bd, s);
   } else {
-    if (with_lse) hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, false>), gd, bd, 0, s, a);
+    if (lean) launch_fp8<192, true>(a, with_lse, gd, bd, s);
+    else launch_fp8<192, false>(a, with_lse, gd, bd, s);
   }
   return hipGetLastError();
 }

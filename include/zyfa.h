@@ -37,7 +37,8 @@ enum zyfa_status {
   ZYFA_ERR_CAPTURE = -8,   /* a per-shape plan must be built while the stream is capturing */
   ZYFA_ERR_HIP = -9,       /* a HIP runtime call failed (launch, allocation, copy) */
   ZYFA_ERR_RANGE = -10,    /* one (batch, head) slice spans more than 2^31 bytes */
-  ZYFA_ERR_ALIGN = -11     /* a tensor pointer is not 16-byte aligned */
+  ZYFA_ERR_ALIGN = -11,    /* a tensor pointer is not 16-byte aligned */
+  ZYFA_ERR_PMODE = -12     /* unknown FP8 probability mode */
 };
 
 enum zyfa_layout {
@@ -81,14 +82,35 @@ int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              const float* q_descale, const float* k_descale, const float* v_descale,
              void* stream);
 
+/*
+ * How the FP8 kernels turn scores into e4m3fn probabilities ("ZYFA" README,
+ * Kernel design: lean P, per-block scaling). Every mode rounds the
+ * probabilities of each 32-key block relative to a power of two, multiplies
+ * V by the rounded values and divides by their sum (README, Accuracy).
+ *  ZYFA_P_DEFAULT  lean P below the diagonal at d_qk = 128, exact P at
+ *                  d_qk = 192 (the README's choice per head dim).
+ *  ZYFA_P_EXACT    exact P: e4m3fn RNE of exp2 of the base-2 score.
+ *  ZYFA_P_LEAN     lean P on key tiles below the diagonal tile: the code of
+ *                  2^y is RNE(8 y + 56 + 8 log2(2 ln^2 2)) read as an
+ *                  integer (interpolates 2^y linearly between powers of two,
+ *                  unbiased on average); the diagonal tile keeps exact P.
+ * BF16 calls ignore the mode.
+ */
+enum zyfa_p_mode {
+  ZYFA_P_DEFAULT = 0,
+  ZYFA_P_EXACT = 1,
+  ZYFA_P_LEAN = 2
+};
+
 /* zyfa_fwd with an explicit softmax scale (flash-attn's softmax_scale
- * argument, README: Differences from flash-attn); softmax_scale <= 0 selects
- * 1/sqrt(d_qk). */
+ * argument, README: Differences from flash-attn; softmax_scale <= 0 selects
+ * 1/sqrt(d_qk)) and an FP8 probability mode (enum zyfa_p_mode; any other
+ * value returns ZYFA_ERR_PMODE). */
 int zyfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
                 int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v,
                 int layout, int dtype,
                 const float* q_descale, const float* k_descale, const float* v_descale,
-                float softmax_scale, void* stream);
+                float softmax_scale, int p_mode, void* stream);
 
 /*
  * zyfa_prepare - build (or find) the per-shape plan ahead of time so that a

@@ -103,3 +103,33 @@ def fp8_score_allowance(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: f
     e = FP8_MFMA_REL * scale * np.log2(np.e) * mag.max(axis=1)
     vmax = np.abs(vh[:nk]).max()
     return (np.exp2(2 * e) - 1.0) * vmax
+
+
+# Tight check against the oracle that rounds the probabilities as the
+# selected FP8 mode does. What still differs is the score: the kernel's FP8
+# MFMA sums in fp32 with its own rounding (bounded by 2^-15.7 sum|ab| on
+# N(0, 1) data), so a code whose 8 y + C (lean) or 2^y (exact) lies that
+# close to a rounding boundary can land one code step (at most 2^(1/8), 9%)
+# away from the oracle's, and the lazy reference can move on the other side
+# of its threshold. Single flips dominate the max; the mean stays tiny.
+FP8_ROUND_MAX = 2e-2
+FP8_ROUND_MEAN = 2e-4
+FP8_ROUND_LSE_MAX = 1e-2
+FP8_ROUND_LSE_MEAN = 1e-4
+
+
+def check_fp8_rounding(out, ref_out, lse, ref_lse, what=""):
+    d = np.abs(out - ref_out)
+    bound = FP8_ROUND_MAX + BF16_OUT_REL_ROUND * np.abs(ref_out)
+    worst = np.unravel_index(np.argmax(d - bound), d.shape)
+    stats = f"{what}: max|dout|={d.max():.3e} mean={d.mean():.3e}"
+    if lse is not None:
+        dl = np.abs(lse - ref_lse)
+        stats += f" max|dLSE|={dl.max():.3e} mean={dl.mean():.3e}"
+    print(stats, flush=True)
+    assert np.all(np.isfinite(out)), what + ": non-finite output"
+    assert np.all(d <= bound), f"{stats} worst at {worst} (ref {ref_out[worst]:.4f} got {out[worst]:.4f})"
+    assert d.mean() <= FP8_ROUND_MEAN, stats
+    if lse is not None:
+        assert np.all(np.isfinite(lse)), what + ": non-finite lse"
+        assert dl.max() <= FP8_ROUND_LSE_MAX and dl.mean() <= FP8_ROUND_LSE_MEAN, stats

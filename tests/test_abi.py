@@ -52,6 +52,13 @@ def test_fwd_argument_errors(kw, status):
     assert _fwd(**kw) == zy.STATUS[status]
 
 
+@pytest.mark.parametrize("p_mode", [-1, 3, 100])
+def test_fwd_ex_rejects_unknown_p_mode(p_mode):
+    L = zy.lib()
+    rc = L.zyfa_fwd_ex(16, 16, 16, 16, None, 1, 128, 4, 2, 128, 128, 0, 1, 16, 16, 16, 0.0, p_mode, None)
+    assert rc == zy.STATUS["ZYFA_ERR_PMODE"]
+
+
 def test_quantize_argument_errors():
     L = zy.lib()
     assert L.zyfa_fp8_quantize(16, 5, 10, 16, 16, None) == zy.STATUS["ZYFA_ERR_DTYPE"]

@@ -1,13 +1,15 @@
 """GPU parity of the FP8 path: the quantizer bit for bit against the oracle's,
-and FP8 attention against the float64 oracle run on the oracle's own
-dequantized inputs (through the C ABI)."""
+and FP8 attention (through the C ABI) against two float64 oracles on the
+oracle's own dequantized inputs: exact softmax attention (the accuracy
+gate), and attention with the probabilities rounded the way the selected
+FP8 mode rounds them (a tight check that the kernel computes that mode)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from workloads import WORKLOADS, Workload, generate
-from parity import bf16_pair, check_fp8, fp8_score_allowance, out_to_f64
+from parity import bf16_pair, check_fp8, check_fp8_rounding, fp8_score_allowance, out_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -69,11 +71,20 @@ def _allowance(rq, rk, rv, w):
     return np.swapaxes(al, 1, 2) if w.layout == "bshd" else al
 
 
-def run_case(w: Workload, seed=None, with_lse=False):
+def oracle_p_mode(p_mode: str, d_qk: int) -> str:
+    """The oracle's rounding mode for a library p_mode (zyfa_p_mode)."""
+    if p_mode == "exact" or (p_mode == "default" and d_qk == 192):
+        return "exact"
+    return "lean_offdiag"
+
+
+def run_case(w: Workload, seed=None, with_lse=False, p_mode="default"):
     q, k, v = generate(w, seed)
-    print(f"case fp8 {w.name} B{w.batch} S{w.seqlen} H{w.nheads}/{w.nheads_k} d{w.d_qk} {w.layout}", flush=True)
+    print(f"case fp8 {w.name} B{w.batch} S{w.seqlen} H{w.nheads}/{w.nheads_k} d{w.d_qk} {w.layout} {p_mode}",
+          flush=True)
     (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
-    res = zy.zyfa_fwd(q8, k8, v8, layout=w.layout, return_lse=with_lse, q_descale=qs, k_descale=ks, v_descale=vs)
+    res = zy.zyfa_fwd(q8, k8, v8, layout=w.layout, return_lse=with_lse, q_descale=qs, k_descale=ks, v_descale=vs,
+                      p_mode=p_mode)
     torch.cuda.synchronize()
     out, lse = res if with_lse else (res, None)
     ref_out, ref_lse = oracle.causal_attention_ref(rq, rk, rv, layout=w.layout)
@@ -102,6 +113,42 @@ def test_small_shapes(B, S, H, Hk, dqk, layout):
     run_case(w, with_lse=True)
 
 
+@pytest.mark.parametrize("p_mode", ["exact", "lean"])
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_modes_meet_the_gate(p_mode, dqk):
+    w = Workload("mode_fp8", 1, 1100, 4, 2, dqk, 128, "bshd", ("fp8",), False, False, 77 + dqk)
+    run_case(w, with_lse=True, p_mode=p_mode)
+
+
+@pytest.mark.parametrize("p_mode", ["default", "exact", "lean"])
+@pytest.mark.parametrize("B,S,H,Hk,dqk,layout", [
+    (1, 700, 4, 2, 128, "bshd"),
+    (2, 389, 2, 1, 128, "bhsd"),
+    (1, 520, 2, 2, 192, "bhsd"),
+])
+def test_rounding_matches_fp8_oracle(p_mode, B, S, H, Hk, dqk, layout):
+    w = Workload("round_fp8", B, S, H, Hk, dqk, 128, layout, ("fp8",), False, False, 3000 + S)
+    q, k, v = generate(w)
+    print(f"case fp8 rounding {p_mode} B{B} S{S} H{H}/{Hk} d{dqk} {layout}", flush=True)
+    (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
+    out, lse = zy.zyfa_fwd(q8, k8, v8, layout=layout, return_lse=True, q_descale=qs, k_descale=ks, v_descale=vs,
+                           p_mode=p_mode)
+    torch.cuda.synchronize()
+    o, l = out_to_f64(out), lse.cpu().numpy().astype(np.float64)
+    rows = np.arange(S)
+    gots, glse, refs, rlse = [], [], [], []
+    for b in range(B):
+        for h in range(H):
+            ro, rl = oracle.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=layout,
+                                                   p_mode=oracle_p_mode(p_mode, dqk))
+            gots.append(o[b, :, h] if layout == "bshd" else o[b, h])
+            glse.append(l[b, h])
+            refs.append(ro)
+            rlse.append(rl)
+    check_fp8_rounding(np.concatenate(gots), np.concatenate(refs), np.concatenate(glse), np.concatenate(rlse),
+                       f"{p_mode} d{dqk} S{S}")
+
+
 def test_activation_like_small():
     run_case(WORKLOADS[5].resized(batch=1, seqlen=1536, name="act_small_fp8"))
 
@@ -123,7 +170,7 @@ def test_full_size_sampled_rows(wid):
     torch.cuda.synchronize()
     o = out_to_f64(out)
     rng = np.random.default_rng(wid)
-    gots, refs, extras = [], [], []
+    gots, refs, extras, rrefs = [], [], [], []
     hv = lambda x: np.swapaxes(x, 1, 2) if w.layout == "bshd" else x
     for b in range(w.batch):
         for h in sorted(set([0, w.nheads - 1] + rng.integers(0, w.nheads, 2).tolist())):
@@ -131,10 +178,16 @@ def test_full_size_sampled_rows(wid):
             ro, _ = oracle.causal_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout)
             gots.append(o[b, rows, h] if w.layout == "bshd" else o[b, h, rows])
             refs.append(ro)
+            if not w.activation_like:
+                rr, _ = oracle.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout,
+                                                      p_mode=oracle_p_mode("default", w.d_qk))
+                rrefs.append(rr)
             hk = h // (w.nheads // w.nheads_k)
             extras.append(fp8_score_allowance(hv(rq)[b, h], hv(rk)[b, hk], hv(rv)[b, hk], w.softmax_scale, rows)
                           if w.activation_like else np.zeros(len(rows)))
     check_fp8(np.concatenate(gots), np.concatenate(refs), w.name, extra=np.concatenate(extras))
+    if rrefs:
+        check_fp8_rounding(np.concatenate(gots), np.concatenate(rrefs), None, None, w.name + " rounding")
 
 
 def test_bitwise_deterministic():
