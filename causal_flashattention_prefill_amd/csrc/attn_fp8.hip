@@ -25,8 +25,10 @@
 //    RNE(8 y + C), clamped to 0..255 by v_cvt_pk_u8_f32 (one FMA and one
 //    conversion per score instead of an exponential and an FP8 conversion).
 //    C = 56 + 8 log2(2 ln^2 2) makes the piecewise-linear value unbiased.
-//    Lean P is used on key tiles below the diagonal; the diagonal tile, which
-//    holds every key of the rows with fewest keys, keeps exact P.
+//    Lean P is used on key tiles that lie wholly before the workgroup's
+//    256-row query tile; the key tiles that overlap the query tile keep exact
+//    P, so the rows with the fewest keys (query tile 0) are exact throughout.
+//    The choice is uniform over the workgroup.
 //  - The row sum is one extra MFMA of the rounded, scaled P against a block
 //    of ones (README, Kernel design: row sum on the matrix unit), so the
 //    denominator is the sum of exactly the values that multiply V.
@@ -59,6 +61,9 @@ constexpr int kTileK = 128;
 constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kE8M0One = 127;           // E8M0 scale 2^0
+// sched_group_barrier instruction classes.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 // Lean-P constant 56 + 8 log2(2 ln(2)^2).
 constexpr float kLeanC = 55.539734f;
 
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
           // ---- P codes and per-block exponents
           i32x8 pf[2];
           int psc[2];
-          const bool lean = LEAN && !diag;
+          const bool lean = LEAN && kbase + kTileK <= q0;
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) {
             // block maxima: the 32-key block of half 0 (1) is held by lane
@@ -314,24 +319,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
           // ---- row sum of the rounded P on the matrix unit
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) lacc[qg] = mfma_fp8(ones, pf[qg], lacc[qg], kE8M0One, psc[qg]);
-          // ---- O^T += V^T P^T
-#pragma unroll
-          for (int db = 0; db < 8; ++db) {
+          // ---- O^T += V^T P^T; V fragments are read two 16-column blocks
+          // ahead of their MFMAs, so the LDS latency hides behind the
+          // matrix work
+          auto v_frag = [&](int db) {
             i32x8 vf;
+            const int r = n >> 1, hh = n & 1;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               // byte 8t + r of lane group g is key 64 (t / 2) + 16 g +
               // 8 (t % 2) + r; lane 2r + hh supplies that row, columns
               // 16db + 8hh .. +7
-              const int r = n >> 1, hh = n & 1;
               const int row = 64 * (t >> 1) + 16 * g + 8 * (t & 1) + r;
-              const char* p = vs + row * 128 + ((db ^ vsw(row)) << 4) + hh * 8;
-              const i32x2 w = lds_read_tr8(p);
+              const i32x2 w = lds_read_tr8(vs + row * 128 + ((db ^ vsw(row)) << 4) + hh * 8);
               vf[2 * t] = w[0];
               vf[2 * t + 1] = w[1];
             }
+            return vf;
+          };
+          i32x8 vfb[2] = {v_frag(0), v_frag(1)};
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
 #pragma unroll
-            for (int qg = 0; qg < 2; ++qg) o[qg][db] = mfma_fp8(vf, pf[qg], o[qg][db], kE8M0One, psc[qg]);
+          for (int db = 0; db < 8; ++db) {
+            const i32x8 cur = vfb[db & 1];
+            if (db + 2 < 8) vfb[db & 1] = v_frag(db + 2);
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg) o[qg][db] = mfma_fp8(cur, pf[qg], o[qg][db], kE8M0One, psc[qg]);
+            if (db + 2 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
           }
         }
         if (more) wait_vm<0>();

@@ -115,6 +115,36 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// Bit casts of scalars passed by value (a bit cast applied directly to an
+// element of an ext_vector has been compiled as a cast of element 0).
+__device__ __forceinline__ float as_f32(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned as_u32(float f) { return __builtin_bit_cast(unsigned, f); }
+
+// v_permlane16_swap_b32 with both operands x: the first result holds rows
+// (16-lane groups) 0, 0, 2, 2 of x and the second rows 1, 1, 3, 3, so their
+// maximum is max(x[l], x[l ^ 16]) in every lane l.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  const unsigned a = r[0], b = r[1];
+  return fmaxf(as_f32(a), as_f32(b));
+}
+
+// v_permlane32_swap_b32 with both operands x: max(x[l], x[l ^ 32]).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  const unsigned a = r[0], b = r[1];
+  return fmaxf(as_f32(a), as_f32(b));
+}
+
+// v_permlane32_swap_b32 of (x, y): returns {lanes 0..31 of x then lanes
+// 0..31 of y, lanes 32..63 of x then lanes 32..63 of y}.
+__device__ __forceinline__ void swap32(float x, float y, float* lo, float* hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(y), false, false);
+  const unsigned a = r[0], b = r[1];
+  *lo = as_f32(a);
+  *hi = as_f32(b);
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 }  // namespace zyfa

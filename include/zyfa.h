@@ -87,13 +87,16 @@ int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  * Kernel design: lean P, per-block scaling). Every mode rounds the
  * probabilities of each 32-key block relative to a power of two, multiplies
  * V by the rounded values and divides by their sum (README, Accuracy).
- *  ZYFA_P_DEFAULT  lean P below the diagonal at d_qk = 128, exact P at
- *                  d_qk = 192 (the README's choice per head dim).
+ *  ZYFA_P_DEFAULT  ZYFA_P_LEAN at d_qk = 128, ZYFA_P_EXACT at d_qk = 192
+ *                  (the README's choice per head dim).
  *  ZYFA_P_EXACT    exact P: e4m3fn RNE of exp2 of the base-2 score.
- *  ZYFA_P_LEAN     lean P on key tiles below the diagonal tile: the code of
- *                  2^y is RNE(8 y + 56 + 8 log2(2 ln^2 2)) read as an
- *                  integer (interpolates 2^y linearly between powers of two,
- *                  unbiased on average); the diagonal tile keeps exact P.
+ *  ZYFA_P_LEAN     lean P for keys below the query's own 256-row tile
+ *                  (keys j < 256 floor(i / 256) of row i): the code of 2^y
+ *                  is RNE(8 y + 56 + 8 log2(2 ln^2 2)) read as an integer
+ *                  (interpolates 2^y linearly between powers of two,
+ *                  unbiased on average); keys from that tile on, which
+ *                  include every key of the rows with fewest keys, keep
+ *                  exact P.
  * BF16 calls ignore the mode.
  */
 enum zyfa_p_mode {

@@ -32,8 +32,12 @@ For query row i (keys j <= i), with x_j = softmax_scale * log2(e) *
      8 log2(2 ln(2)^2) = 55.54 instead of 56 makes the piecewise-linear
      value 2^floor(y) (1 + frac(y)) unbiased: its mean ratio to 2^y over a
      uniform frac(y) is 1 / (2 ln(2)^2));
-   - lean P off the diagonal ("lean_offdiag"): lean P for keys of tiles
-     before the one holding key i, exact P for the tile holding key i.
+   - lean P off the diagonal query tile ("lean_offdiag"): the query rows
+     are tiled in QUERY_TILE = 256 rows; keys of the key tiles that hold the
+     rows of row i's own query tile (key tile t >= 2 * floor(i / 256)) get
+     exact P, which covers every key of the rows with the fewest keys; the
+     key tiles before them get lean P. (Which tiles keep exact P is this
+     implementation's choice; the README uses lean P throughout at d = 128.)
 4. The key's weight is w_j = value(c_j) * 2^(e_b + m), with m the reference
    when its tile was visited. O_i = sum_j w_j v_j / sum_j w_j and
    LSE_i = ln(sum_j w_j).
@@ -52,6 +56,7 @@ from .attention import _split, kv_head
 from .codecs import e4m3fn_decode, e4m3fn_encode
 
 KEY_TILE = 128
+QUERY_TILE = 256
 BLOCK = 32
 TAU = 8.0
 LOG2E = 1.4426950408889634073599246810019
@@ -71,7 +76,7 @@ def exact_code(y) -> np.ndarray:
 
 
 def row_weights(x: np.ndarray, i: int, p_mode: str, *, key_tile: int = KEY_TILE, block: int = BLOCK,
-                tau: float = TAU):
+                tau: float = TAU, query_tile: int = QUERY_TILE):
     """Weights of keys 0..i of one row (x holds their base-2 scores), divided
     by 2^m_final, and m_final. Returns (w, m_final)."""
     if p_mode not in P_MODES:
@@ -85,6 +90,7 @@ def row_weights(x: np.ndarray, i: int, p_mode: str, *, key_tile: int = KEY_TILE,
     exps = np.zeros(n)     # e_b + m_t per key
     codes = np.zeros(n, dtype=np.int64)
     diag_tile = i // key_tile
+    exact_from = (i // query_tile) * query_tile // key_tile
     for t in range(diag_tile + 1):
         lo, hi = t * key_tile, min((t + 1) * key_tile, n)
         mt = x[lo:hi].max()
@@ -94,7 +100,7 @@ def row_weights(x: np.ndarray, i: int, p_mode: str, *, key_tile: int = KEY_TILE,
             b1 = min(b0 + block, hi)
             e_b = max(math.floor(x[b0:b1].max() - m), -126)
             y = x[b0:b1] - m - e_b
-            lean = p_mode == "lean" or (p_mode == "lean_offdiag" and t < diag_tile)
+            lean = p_mode == "lean" or (p_mode == "lean_offdiag" and t < exact_from)
             codes[b0:b1] = lean_code(y) if lean else exact_code(y)
             exps[b0:b1] = e_b + m
     m_final = m

@@ -105,16 +105,22 @@ def test_subnormal_and_underflow_weights():
     assert np.array_equal(_row([0.0, -7.0, -6.5], 2, "lean"), [1.0, 0.0, 2.0 ** -7])
 
 
-def test_diagonal_tile_is_exact_in_lean_offdiag():
-    # row 128: key 0 (tile 0) and key 128 (tile 1, the diagonal tile), both
+def test_query_tile_is_exact_in_lean_offdiag():
+    # row 384 lies in query tile 1 (rows 256..511): key tiles 2 and 3 (keys
+    # 256..) take exact P, key tiles 0 and 1 lean P; all four marked keys are
     # half a binade below the reference
-    x = np.full(129, -300.0)
-    x[0], x[1], x[128] = 0.0, -0.5, -0.5
-    w = _row(x, 128, "lean_offdiag")
-    assert w[0] == 1.0 and w[1] == 0.75               # lean, off the diagonal
-    assert w[128] == 1.375 * 2.0 ** -1                # exact: block e_b = -1, RNE(2^0.5)
-    w = _row(x, 128, "lean")
-    assert w[128] == 1.5 * 2.0 ** -1
+    x = np.full(385, -300.0)
+    x[0] = 0.0
+    x[[1, 200, 300, 384]] = -0.5
+    w = _row(x, 384, "lean_offdiag")
+    assert w[0] == 1.0 and w[1] == 0.75                 # lean, key tile 0
+    assert w[200] == 1.5 * 2.0 ** -1                    # lean, key tile 1 (block e_b = -1)
+    assert w[300] == 1.375 * 2.0 ** -1                  # exact, key tile 2: RNE(2^0.5)
+    assert w[384] == 1.375 * 2.0 ** -1                  # exact, key tile 3
+    w = _row(x, 384, "lean")
+    assert w[300] == 1.5 * 2.0 ** -1 and w[384] == 1.5 * 2.0 ** -1
+    # row 255 lies in query tile 0: every key is exact
+    assert np.array_equal(_row(x[:256], 255, "lean_offdiag"), _row(x[:256], 255, "exact"))
 
 
 def test_lazy_reference():
@@ -145,9 +151,9 @@ def test_row0_and_constant_keys(p_mode):
     np.testing.assert_allclose(o, prefix, rtol=0, atol=1e-12)
 
 
-def test_lean_offdiag_equals_exact_within_first_tile():
+def test_lean_offdiag_equals_exact_within_first_query_tile():
     rng = np.random.default_rng(5)
-    S, d = 128, 16
+    S, d = 256, 16
     q, k, v = (rng.standard_normal((1, S, 1, d)) for _ in range(3))
     rows = np.arange(S)
     a = fp8_p.fp8_attention_rows_ref(q, k, v, 0, 0, rows, p_mode="exact")
