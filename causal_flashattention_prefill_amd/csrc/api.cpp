@@ -10,7 +10,7 @@
 #include <tuple>
 #include <vector>
 
-#include "../../include/zyfa.h"
+#include "zyfa.h"
 #include "plan.h"
 #include "zyfa_internal.h"
 
@@ -146,6 +146,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   a.nheads_k = nheads_k;
   a.n_qtiles = plan->n_qtiles;
   a.jobs_per_wg = plan->jobs_per_wg;
+  a.num_wgs = plan->num_wgs;
   a.jobs = plan->jobs;
   const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)d_qk);
   a.scale_log2 = (float)(scale * 1.4426950408889634);

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform values live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
   const int n = lane & 15;
   const int S = a.seqlen;
@@ -74,7 +75,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   for (int it = 0; it < a.jobs_per_wg; ++it) {
-    const int2 job = a.jobs[it * (int)gridDim.x + (int)blockIdx.x];
+    const int2 jv = a.jobs[it * (int)gridDim.x + (int)blockIdx.x];
+    const int2 job = {__builtin_amdgcn_readfirstlane(jv.x), __builtin_amdgcn_readfirstlane(jv.y)};
     if (job.x < 0) break;
     const int b = job.x / a.nheads;
     const int h = job.x - b * a.nheads;

@@ -58,6 +58,7 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kTileQ = 256;
 constexpr int kTileK = 128;
+constexpr int kSlots = 4;             // K and V ring depth
 constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kE8M0One = 127;           // E8M0 scale 2^0
@@ -66,6 +67,7 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 // Lean-P constant 56 + 8 log2(2 ln(2)^2).
 constexpr float kLeanC = 55.539734f;
+constexpr float kInv65535 = 1.0f / 65535.0f;
 
 // 16-byte chunk swizzle of V row r: bits 1..2 and 4 of r.
 __device__ __forceinline__ int vsw(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
@@ -73,8 +75,26 @@ __device__ __forceinline__ int vsw(int r) { return ((r >> 1) & 3) | ((r >> 2) & 
 // Key held by LDS row r of a K tile: bits [5:4] and [3:2] of r swapped.
 __device__ __forceinline__ int kswap(int r) { return (r & ~0x3C) | ((r & 0x30) >> 2) | ((r & 0x0C) << 2); }
 
+// x = -inf where key offset ko > q (the causal mask). One compare into VCC
+// and one select per score; written as assembly so that the compiler does
+// not compute all compares first into scalar register pairs (which it then
+// spills).
+__device__ __forceinline__ float mask_above(float x, int ko, int q, float ninf) {
+  asm volatile("v_cmp_gt_i32_e32 vcc, %1, %2\n\tv_cndmask_b32_e32 %0, %0, %3, vcc"
+               : "+v"(x)
+               : "s"(ko), "v"(q), "v"(ninf)
+               : "vcc");
+  return x;
+}
+
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// a * b rounded to fp32 on its own: never fused with a following add.
+__device__ __forceinline__ float mul_nofma(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
 }
 
 // Largest power of two <= x for x > 0 (exponent field only), at least 2^-126.
@@ -95,28 +115,43 @@ template <int DQK, bool WITH_LSE, bool LEAN>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArgs a) {
   constexpr int DV = 128;
   constexpr bool D192 = DQK == 192;
-  constexpr int KA_BYTES = kTileK * 128;       // K region for d 0..127
+  constexpr int KA_BYTES = kTileK * 128;            // K region for d 0..127
   constexpr int KB_BYTES = D192 ? kTileK * 64 : 0;  // K region for d 128..191
-  constexpr int V_BYTES = kTileK * DV;
-  constexpr int STAGE = KA_BYTES + KB_BYTES + V_BYTES;
-  static_assert(KA_BYTES == 16 * 1024 && V_BYTES == 16 * 1024 && (!D192 || KB_BYTES == 8 * 1024), "tile split");
+  constexpr int K_SLOT = KA_BYTES + KB_BYTES;
+  constexpr int V_SLOT = kTileK * DV;
+  static_assert(KA_BYTES == 16 * 1024 && V_SLOT == 16 * 1024 && (!D192 || KB_BYTES == 8 * 1024), "tile split");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[kSlots * (K_SLOT + V_SLOT)];
+  char* const kring = smem;
+  char* const vring = smem + kSlots * K_SLOT;
 
-  const int tid = threadIdx.x;
+  // work-item and group ids from the hardware registers directly (the
+  // device-library accessors are not inlined into a kernel compiled with
+  // IEEE mode off, and a call would spill every live register)
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+  const int wg = (int)__builtin_amdgcn_workgroup_id_x();
   const int lane = tid & 63;
+  // wave-uniform values live in scalar registers
   const int wave = tid >> 6;
   const int g = lane >> 4;
   const int n = lane & 15;
+  // Waves w and w + 4 share a SIMD. Waves 4..7 (the lead group, which also
+  // holds the query rows with more keys) run half a key tile ahead of waves
+  // 0..3 (the lag group).
+  const bool lead = wave >= 4;
   const int S = a.seqlen;
   // Scores in base-2 units: S_codes * (softmax_scale * log2 e * dq * dk).
   const float sl2 = a.scale_log2 * a.q_descale[0] * a.k_descale[0];
+  const float c8s = 8.0f * sl2 * kInv65535;
+  // ds_bpermute source of the lane's E8M0 scale: lane groups 1 and 2 swap
+  const int psc_addr = 4 * (((g == 1) || (g == 2)) ? (lane ^ 48) : lane);
   const float dvs = a.v_descale[0];
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3fn 1.0
 
   for (int it = 0; it < a.jobs_per_wg; ++it) {
-    const int2 job = a.jobs[it * (int)gridDim.x + (int)blockIdx.x];
+    const int2 jv = a.jobs[it * a.num_wgs + wg];
+    const int2 job = {__builtin_amdgcn_readfirstlane(jv.x), __builtin_amdgcn_readfirstlane(jv.y)};
     if (job.x < 0) break;
     const int b = job.x / a.nheads;
     const int h = job.x - b * a.nheads;
@@ -125,8 +160,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
     const char* kbase = (const char*)a.k.ptr + (b * a.k.stride_b + hk * a.k.stride_h);
     const char* vbase = (const char*)a.v.ptr + (b * a.v.stride_b + hk * a.v.stride_h);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, a.q_bytes);
-    const i32x4 rk = make_rsrc_words(kbase, a.k_bytes);
-    const i32x4 rv = make_rsrc_words(vbase, a.v_bytes);
     const int qrs = (int)a.q.stride_s;
     const int krs = (int)a.k.stride_s;
     const int vrs = (int)a.v.stride_s;
@@ -140,7 +173,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       const int qw0 = q0 + wave * 32;
       const int qend = min(q0 + kTileQ, S);
       const int n_kt = (qend - 1) / kTileK + 1;
+      // this wave's last key tile (the one holding its diagonal), -1 if the
+      // wave has no rows
       const int kt_w = (qw0 < S) ? min((qw0 + 31) / kTileK, n_kt - 1) : -1;
+      // key tiles from K0 on overlap this query tile: exact P and (on the
+      // diagonal) the causal mask; tiles before K0 take lean P (with LEAN)
+      const int K0 = q0 / kTileK;
 
       // Q fragments (B operand): lane (g, n) holds q[row n][16g..16g+15] and
       // q[row n][64+16g..]; for d 192 also q[row n][128+16g..] (upper half 0).
@@ -166,201 +204,282 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       float mref[2] = {neg_inf(), neg_inf()};
+      // lazy-rescale threshold in raw score units, (m + tau) / sl2, and the
+      // lean-P offset (C - 8 m) / 65535 of each query group
+      float thr[2] = {neg_inf(), neg_inf()};
+      float lcs[2] = {0.f, 0.f};
+      // scores of the tile in flight (made by a matrix cluster, turned into P
+      // codes by the next vector cluster), the P codes and the E8M0 exponent
+      // this lane supplies to the PV MFMA
+      f32x4 s[2][8];
+      i32x8 pf[2];
+      int psc[2];
 
-      // Direct global-to-LDS tile loads (see the BF16 kernel); K row r of the
-      // LDS tile holds key kswap(r), V row r holds key r; 16-byte chunks
-      // XOR-swizzled by row:
+      // Direct global-to-LDS tile loads; K row r of a slot holds key
+      // kswap(r), V row r holds key r; 16-byte chunks XOR-swizzled by row:
       //  K d 0..127:   row * 128 + ((c ^ ((row >> 1) & 7)) << 4)
       //  K d 128..191: row * 64  + ((c ^ ((row >> 2) & 3)) << 4)
       //  V:            row * 128 + ((c ^ vsw(row)) << 4)
       // The V swizzle puts the sixteen rows that a half-wave of each
       // transposing read touches (8 consecutive keys in each of two lane
-      // groups) on distinct banks, and does not depend on the read index t.
-      auto issue_kv = [&](int kt, char* base) {
+      // groups) on distinct banks.
+      // Per-lane byte offsets of the tile loads (fixed for the job); the
+      // tile's own offset goes into the buffer resource, whose extent still
+      // ends at the slice end, so rows past seqlen read as zeros.
+      int kvo[3], vvo[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int I = wave * 2 + u;
-          const int p = I * 1024 + lane * 16;
-          const int row = p >> 7, slot = (p & 127) >> 4;
-          dma16(rk, (kt * kTileK + kswap(row)) * krs + (slot ^ ((row >> 1) & 7)) * 16, base + I * 1024);
-          dma16(rv, (kt * kTileK + row) * vrs + (slot ^ vsw(row)) * 16,
-                base + KA_BYTES + KB_BYTES + I * 1024);
-        }
-        if (D192) {
-          const int p = wave * 1024 + lane * 16;
-          const int row = p >> 6, x = ((p & 63) >> 4) ^ ((row >> 2) & 3);
-          dma16(rk, (kt * kTileK + kswap(row)) * krs + 128 + x * 16, base + KA_BYTES + wave * 1024);
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int p = (wave * 2 + u) * 1024 + lane * 16;
+        const int row = p >> 7, slot = (p & 127) >> 4;
+        kvo[u] = kswap(row) * krs + (slot ^ ((row >> 1) & 7)) * 16;
+        vvo[u] = row * vrs + (slot ^ vsw(row)) * 16;
+      }
+      if (D192) {
+        const int p = wave * 1024 + lane * 16;
+        const int row = p >> 6, x = ((p & 63) >> 4) ^ ((row >> 2) & 3);
+        kvo[2] = kswap(row) * krs + 128 + x * 16;
+      }
+      auto tile_rsrc = [&](const char* base, unsigned nbytes, int stride, int kt) {
+        const unsigned off = (unsigned)(kt * kTileK * stride);
+        return make_rsrc_words(base + off, nbytes > off ? nbytes - off : 0u);
+      };
+      auto issue_k = [&](int kt) {
+        char* base = kring + (kt % kSlots) * K_SLOT;
+        const i32x4 r = tile_rsrc(kbase, a.k_bytes, krs, kt);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) dma16(r, kvo[u], base + (wave * 2 + u) * 1024);
+        if (D192) dma16(r, kvo[2], base + KA_BYTES + wave * 1024);
+      };
+      auto issue_v = [&](int kt) {
+        char* base = vring + (kt % kSlots) * V_SLOT;
+        const i32x4 r = tile_rsrc(vbase, a.v_bytes, vrs, kt);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) dma16(r, vvo[u], base + (wave * 2 + u) * 1024);
       };
 
-      // One key tile read from ring stage `cur` while the next streams into `nxt`.
-      auto step = [&](char* const cur, char* const nxt, int kt) {
-        const bool more = kt + 1 < n_kt;
-        if (more) issue_kv(kt + 1, nxt);
-        if (kt <= kt_w) {
-          const char* ka = cur;
-          const char* kb2 = cur + KA_BYTES;
-          const char* vs = cur + KA_BYTES + KB_BYTES;
-          // ---- S^T = K Q^T (8 blocks of 16 keys)
-          f32x4 s[2][8];
+      // V^T fragment of 16-column block db: byte 8t + r of lane group g is
+      // key 64 (t / 2) + 16 g + 8 (t % 2) + r; lane 2r + hh supplies that
+      // row, columns 16 db + 8 hh .. +7.
+      auto v_frag = [&](const char* vs, int db) {
+        i32x8 vf;
+        const int r = n >> 1, hh = n & 1;
 #pragma unroll
-          for (int kb = 0; kb < 8; ++kb) {
-            const int row = 16 * kb + n;
-            const int sw = (row >> 1) & 7;
-            const u32x4 lo = lds_load<u32x4>(ka + row * 128 + ((g ^ sw) << 4));
-            const u32x4 hi = lds_load<u32x4>(ka + row * 128 + (((4 + g) ^ sw) << 4));
-            const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-#pragma unroll
-            for (int qg = 0; qg < 2; ++qg)
-              s[qg][kb] = mfma_fp8(kf, qf[qg], f32x4{0.f, 0.f, 0.f, 0.f}, kE8M0One, kE8M0One);
-            if (D192) {
-              const u32x4 x = lds_load<u32x4>(kb2 + row * 64 + ((g ^ ((row >> 2) & 3)) << 4));
-              const i32x8 kf2 = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
-#pragma unroll
-              for (int qg = 0; qg < 2; ++qg) s[qg][kb] = mfma_fp8(kf2, qf2[qg], s[qg][kb], kE8M0One, kE8M0One);
-            }
-          }
-          // ---- causal mask, on the diagonal tile only; score (kb, i) of lane
-          // group g is key 64 (kb / 4) + 16 g + 4 (kb % 4) + i of the tile
-          const int kbase = kt * kTileK;
-          const bool diag = kbase + kTileK - 1 > qw0;
-          if (__builtin_expect(diag, 0)) {
-#pragma unroll
-            for (int qg = 0; qg < 2; ++qg) {
-              const int q = qw0 + 16 * qg + n - kbase - 16 * g;
-#pragma unroll
-              for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (64 * (kb >> 2) + 4 * (kb & 3) + i > q) s[qg][kb][i] = neg_inf();
-            }
-          }
-          // ---- lane maxima of the raw scores per scale half (kb 0..3: keys
-          // 16g..16g+15, kb 4..7: keys 64+16g..), lazy test and one ballot
-          // per tile
-          float m0[2], m1[2];
-#pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
-            float a0 = fmaxf(fmaxf(s[qg][0][0], s[qg][0][1]), s[qg][0][2]);
-            float a1 = fmaxf(fmaxf(s[qg][4][0], s[qg][4][1]), s[qg][4][2]);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-              for (int i = (kb == 0 ? 3 : 0); i < 4; i += 2) {
-                if (i == 3) {
-                  a0 = fmaxf(a0, s[qg][kb][3]);
-                  a1 = fmaxf(a1, s[qg][kb + 4][3]);
-                } else {
-                  a0 = fmaxf(fmaxf(a0, s[qg][kb][i]), s[qg][kb][i + 1]);
-                  a1 = fmaxf(fmaxf(a1, s[qg][kb + 4][i]), s[qg][kb + 4][i + 1]);
-                }
-              }
-            }
-            m0[qg] = a0 * sl2;
-            m1[qg] = a1 * sl2;
-          }
-          const bool need = (fmaxf(m0[0], m1[0]) > mref[0] + kTau) || (fmaxf(m0[1], m1[1]) > mref[1] + kTau);
-          if (__builtin_expect(wave_any(need), 0)) {
-#pragma unroll
-            for (int qg = 0; qg < 2; ++qg) {
-              float rm = fmaxf(fmaxf(m0[qg], m1[qg]), __shfl_xor(fmaxf(m0[qg], m1[qg]), 16));
-              rm = fmaxf(rm, __shfl_xor(rm, 32));
-              const float mn = rm > mref[qg] + kTau ? rm : mref[qg];
-              const float f = fast_exp2(mref[qg] - mn);
-              lacc[qg] *= f;
-#pragma unroll
-              for (int db = 0; db < 8; ++db) o[qg][db] *= f;
-              mref[qg] = mn;
-            }
-          }
-          // ---- P codes and per-block exponents
-          i32x8 pf[2];
-          int psc[2];
-          const bool lean = LEAN && kbase + kTileK <= q0;
-#pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
-            // block maxima: the 32-key block of half 0 (1) is held by lane
-            // groups g and g ^ 1
-            const float b0 = fmaxf(m0[qg], __shfl_xor(m0[qg], 16));
-            const float b1 = fmaxf(m1[qg], __shfl_xor(m1[qg], 16));
-            const float e0 = fmaxf(floorf(b0 - mref[qg]), -126.0f);
-            const float e1 = fmaxf(floorf(b1 - mref[qg]), -126.0f);
-            // lane 16 b + n supplies the scale of block b: groups 1 and 2
-            // swap the exponents they do not hold themselves
-            const float other = __shfl_xor((g & 1) ? e1 : e0, 48);
-            const float mine = g == 0 ? e0 : (g == 3 ? e1 : other);
-            psc[qg] = (int)mine + 127;
-            if (lean) {
-              const float c8 = 8.0f * sl2;
-              const float o0 = kLeanC - 8.0f * (mref[qg] + e0);
-              const float o1 = kLeanC - 8.0f * (mref[qg] + e1);
-#pragma unroll
-              for (int kb = 0; kb < 8; ++kb) {
-                const float o = kb < 4 ? o0 : o1;
-                unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[qg][kb][0], c8, o), 0, 0u);
-                w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[qg][kb][1], c8, o), 1, w);
-                w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[qg][kb][2], c8, o), 2, w);
-                w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[qg][kb][3], c8, o), 3, w);
-                pf[qg][kb] = (int)w;
-              }
-            } else {
-              const float nm = -mref[qg];
-              const float sc0 = __builtin_bit_cast(float, (unsigned)((int)e0 + 127) << 23);
-              const float sc1 = __builtin_bit_cast(float, (unsigned)((int)e1 + 127) << 23);
-#pragma unroll
-              for (int kb = 0; kb < 8; ++kb) {
-                f32x4 p;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, nm));
-                pf[qg][kb] = (int)cvt4_fp8(p[0], p[1], p[2], p[3], kb < 4 ? sc0 : sc1);
-              }
-            }
-          }
-          // ---- row sum of the rounded P on the matrix unit
+        for (int t = 0; t < 4; ++t) {
+          const int row = 64 * (t >> 1) + 16 * g + 8 * (t & 1) + r;
+          const i32x2 w = lds_read_tr8(vs + row * 128 + ((db ^ vsw(row)) << 4) + hh * 8);
+          vf[2 * t] = w[0];
+          vf[2 * t + 1] = w[1];
+        }
+        return vf;
+      };
+
+      // K fragments of 16-key block kb (A operand): lane (g, n) holds key
+      // row 16 kb + n, d 16g..16g+15 and 64+16g.. (and, for d 192, d
+      // 128+16g.. with the upper half zero).
+      struct KFrag {
+        i32x8 a, b;
+      };
+      auto k_frag = [&](const char* ka, int kb) {
+        KFrag f;
+        const int row = 16 * kb + n;
+        const int sw = (row >> 1) & 7;
+        const u32x4 lo = lds_load<u32x4>(ka + row * 128 + ((g ^ sw) << 4));
+        const u32x4 hi = lds_load<u32x4>(ka + row * 128 + (((4 + g) ^ sw) << 4));
+        f.a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        if (D192) {
+          const u32x4 x = lds_load<u32x4>(ka + KA_BYTES + row * 64 + ((g ^ ((row >> 2) & 3)) << 4));
+          f.b = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+        }
+        return f;
+      };
+
+      // Matrix cluster of tile t: O^T += V^T P^T and the row sum for tile
+      // t - 1 (P codes from the previous vector cluster), then the scores
+      // S^T = K Q^T of tile t.
+      auto matrix_cluster = [&](int t) {
+        __builtin_amdgcn_s_setprio(1);
+        const bool pv = t >= 1 && t - 1 <= kt_w;
+        if (pv) {
+          const char* vs = vring + ((t - 1) % kSlots) * V_SLOT;
+          i32x8 vfb[2] = {v_frag(vs, 0), v_frag(vs, 1)};
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) lacc[qg] = mfma_fp8(ones, pf[qg], lacc[qg], kE8M0One, psc[qg]);
-          // ---- O^T += V^T P^T; V fragments are read two 16-column blocks
-          // ahead of their MFMAs, so the LDS latency hides behind the
-          // matrix work
-          auto v_frag = [&](int db) {
-            i32x8 vf;
-            const int r = n >> 1, hh = n & 1;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              // byte 8t + r of lane group g is key 64 (t / 2) + 16 g +
-              // 8 (t % 2) + r; lane 2r + hh supplies that row, columns
-              // 16db + 8hh .. +7
-              const int row = 64 * (t >> 1) + 16 * g + 8 * (t & 1) + r;
-              const i32x2 w = lds_read_tr8(vs + row * 128 + ((db ^ vsw(row)) << 4) + hh * 8);
-              vf[2 * t] = w[0];
-              vf[2 * t + 1] = w[1];
-            }
-            return vf;
-          };
-          i32x8 vfb[2] = {v_frag(0), v_frag(1)};
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
             const i32x8 cur = vfb[db & 1];
-            if (db + 2 < 8) vfb[db & 1] = v_frag(db + 2);
+            if (db + 2 < 8) vfb[db & 1] = v_frag(vs, db + 2);
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg) o[qg][db] = mfma_fp8(cur, pf[qg], o[qg][db], kE8M0One, psc[qg]);
             if (db + 2 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
           }
         }
-        if (more) wait_vm<0>();
-        __syncthreads();
+        if (t <= kt_w) {
+          const char* ka = kring + (t % kSlots) * K_SLOT;
+          // K fragments are read two 16-key blocks ahead of their MFMAs
+          KFrag kfb[2] = {k_frag(ka, 0), k_frag(ka, 1)};
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 ? 6 : 4, 0);
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            const KFrag cur = kfb[kb & 1];
+            if (kb + 2 < 8) kfb[kb & 1] = k_frag(ka, kb + 2);
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg)
+              s[qg][kb] = mfma_fp8(cur.a, qf[qg], f32x4{0.f, 0.f, 0.f, 0.f}, kE8M0One, kE8M0One);
+            if (D192) {
+#pragma unroll
+              for (int qg = 0; qg < 2; ++qg) s[qg][kb] = mfma_fp8(cur.b, qf2[qg], s[qg][kb], kE8M0One, kE8M0One);
+            }
+            if (kb + 2 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 ? 3 : 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, D192 ? 4 : 2, 0);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
       };
 
-      __syncthreads();   // the previous tile's last reads of the ring are done
-      issue_kv(0, smem);
+      // Vector cluster of tile t: causal mask (diagonal tile), maxima, lazy
+      // rescale, block exponents and P codes. Cross-lane exchanges go
+      // through the LDS unit (ds_swizzle, ds_bpermute), which is idle here,
+      // so they take no vector-ALU issue slots.
+      auto vector_cluster = [&](int t) {
+        if (t > kt_w) return;
+        const int kt0 = t * kTileK;
+        // ---- causal mask, on the diagonal tile only; score (kb, i) of lane
+        // group g is key 64 (kb / 4) + 16 g + 4 (kb % 4) + i of the tile
+        if (__builtin_expect(kt0 + kTileK - 1 > qw0, 0)) {
+          const float ninf = neg_inf();
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            const int q = qw0 + 16 * qg + n - kt0 - 16 * g;
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) s[qg][kb][i] = mask_above(s[qg][kb][i], 64 * (kb >> 2) + 4 * (kb & 3) + i, q, ninf);
+          }
+        }
+        // ---- lane maxima of the raw scores per scale half (kb 0..3: keys
+        // 16g..16g+15, kb 4..7: keys 64+16g..), then the maxima of the
+        // 32-key scale blocks (held by lane groups g and g ^ 1)
+        float x0[2], x1[2], b0[2], b1[2];
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+          float y0 = fmaxf(fmaxf(s[qg][0][0], s[qg][0][1]), s[qg][0][2]);
+          float y1 = fmaxf(fmaxf(s[qg][4][0], s[qg][4][1]), s[qg][4][2]);
+#pragma unroll
+          for (int j = 3; j < 15; j += 2) {
+            y0 = fmaxf(fmaxf(y0, s[qg][j >> 2][j & 3]), s[qg][(j + 1) >> 2][(j + 1) & 3]);
+            y1 = fmaxf(fmaxf(y1, s[qg][4 + (j >> 2)][j & 3]), s[qg][4 + ((j + 1) >> 2)][(j + 1) & 3]);
+          }
+          x0[qg] = fmaxf(y0, s[qg][3][3]);
+          x1[qg] = fmaxf(y1, s[qg][7][3]);
+          b0[qg] = fmaxf(x0[qg], swap16(x0[qg]));
+          b1[qg] = fmaxf(x1[qg], swap16(x1[qg]));
+        }
+        // ---- lazy test in raw score units, one ballot per tile
+        const bool need = (fmaxf(x0[0], x1[0]) > thr[0]) || (fmaxf(x0[1], x1[1]) > thr[1]);
+        if (__builtin_expect(wave_any(need), 0)) {
+          // keep the rescale a real branch (with f == 1 it is harmless, so
+          // the compiler would otherwise run it on every tile)
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            const float rm = max_xor32(fmaxf(b0[qg], b1[qg])) * sl2;
+            const float mn = rm > mref[qg] + kTau ? rm : mref[qg];
+            const float f = fast_exp2(mref[qg] - mn);
+            lacc[qg] *= f;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[qg][db] *= f;
+            mref[qg] = mn;
+            thr[qg] = (mn + kTau) / sl2;
+            lcs[qg] = (kLeanC - 8.0f * mn) * kInv65535;
+          }
+        }
+        // ---- block exponents e_b = floor(block max - m) (base 2, >= -126)
+        // and P codes
+        const bool lean = LEAN && t < K0;
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+          // the block maximum is rounded to fp32 before m is subtracted,
+          // exactly as m itself was (a fused multiply-subtract would give
+          // e_b = -1 instead of 0 for the block that holds the maximum
+          // whenever the product rounds up)
+          const float e0 = fmaxf(floorf(mul_nofma(b0[qg], sl2) - mref[qg]), -126.0f);
+          const float e1 = fmaxf(floorf(mul_nofma(b1[qg], sl2) - mref[qg]), -126.0f);
+          // lane 16 b + n supplies the scale of block b; group g holds
+          // blocks g / 2 (half 0) and 2 + g / 2 (half 1), so groups 1 and 2
+          // fetch theirs from each other
+          const float es = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                         psc_addr, __builtin_bit_cast(int, (g & 1) ? e1 : e0)));
+          if (lean) {
+            // code = RNE(8 y + C) with y = s sl2 - m - e_b, clamped at 0:
+            // v_cvt_pknorm_u16_f32 rounds (8 y + C) / 65535 * 65535 and
+            // clamps, two scores per instruction
+            const float o0 = __builtin_fmaf(e0, -8.0f * kInv65535, lcs[qg]);
+            const float o1 = __builtin_fmaf(e1, -8.0f * kInv65535, lcs[qg]);
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+              const float off = kb < 4 ? o0 : o1;
+              const u16x2 lo = __builtin_amdgcn_cvt_pknorm_u16(__builtin_fmaf(s[qg][kb][0], c8s, off),
+                                                               __builtin_fmaf(s[qg][kb][1], c8s, off));
+              const u16x2 hi = __builtin_amdgcn_cvt_pknorm_u16(__builtin_fmaf(s[qg][kb][2], c8s, off),
+                                                               __builtin_fmaf(s[qg][kb][3], c8s, off));
+              pf[qg][kb] = (int)__builtin_amdgcn_perm(__builtin_bit_cast(unsigned, hi), __builtin_bit_cast(unsigned, lo),
+                                                      0x06040200u);
+            }
+          } else {
+            const float nm = -mref[qg];
+            const float sc0 = __builtin_ldexpf(1.0f, (int)e0);
+            const float sc1 = __builtin_ldexpf(1.0f, (int)e1);
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+              f32x4 p;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, nm));
+              pf[qg][kb] = (int)cvt4_fp8(p[0], p[1], p[2], p[3], kb < 4 ? sc0 : sc1);
+            }
+          }
+          psc[qg] = (int)es + 127;
+        }
+      };
+
+      // Ping-pong over intervals closed by one barrier each. In interval i
+      // the lead group runs the vector cluster of tile i - 1 and then the
+      // matrix cluster of tile i; the lag group runs the matrix cluster of
+      // tile i - 1 and then its vector cluster. On every SIMD one wave is in
+      // a matrix cluster while the other computes a softmax. Interval i
+      // reads K(i - 1), K(i), V(i - 2) and V(i - 1). At its end each wave
+      // issues its share of K(i + 2) and V(i + 1) into the slots last read
+      // in interval i - 1 (four-slot rings), and waits for the loads issued
+      // one interval earlier (K(i + 1), V(i), read from interval i + 1 on):
+      // issued at the end, the loads fill the time a wave waits at the
+      // barrier, and each load has a whole interval to arrive. (Issued in a
+      // burst at the start of an interval they queue in the address unit
+      // and stall every wave.) The lag group's last tile (its PV) ends in
+      // interval kt_w + 2, the lead's in kt_w + 1.
+      const int lag_last = min(K0, n_kt - 1);
+      const int n_int = max(n_kt + 1, lag_last + 3);
+      __syncthreads();   // the previous query tile's last reads of the rings are done
+      issue_k(0);
+      if (n_kt > 1) issue_k(1);
+      issue_v(0);
       wait_vm<0>();
       __syncthreads();
-      for (int kt = 0; kt < n_kt; ++kt) {
-        const int st = kt & 1;
-        step(smem + st * STAGE, smem + (st ^ 1) * STAGE, kt);
+      for (int i = 0; i < n_int; ++i) {
+        if (lead) {
+          if (i >= 1) vector_cluster(i - 1);
+          matrix_cluster(i);
+        } else if (i >= 1) {
+          matrix_cluster(i - 1);
+          vector_cluster(i - 1);
+        }
+        if (i + 2 < n_kt) issue_k(i + 2);
+        if (i + 1 < n_kt) issue_v(i + 1);
+        if (i + 2 < n_kt) wait_vm<D192 ? 5 : 4>();
+        else if (i + 1 < n_kt) wait_vm<2>();
+        else wait_vm<0>();
+        __syncthreads();
       }
 
       // ---- epilogue: O * dv / l (RNE to bf16), LSE = ln2 * (m + log2 l)

@@ -16,6 +16,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
@@ -72,6 +73,15 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, int voff, const char* l
                : "memory", "m0");
 }
 
+// dma16 without the compiler memory barrier: LDS reads may be scheduled
+// across it. Only for loads into a ring slot that no LDS read between the
+// surrounding barriers touches.
+__device__ __forceinline__ void dma16_unordered(const i32x4& rsrc, int voff, const char* lds_wave_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc) : "m0");
+}
+
 // s_waitcnt vmcnt(N) leaving the LDS and export counters alone (gfx9
 // encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
@@ -119,6 +129,12 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // element of an ext_vector has been compiled as a cast of element 0).
 __device__ __forceinline__ float as_f32(unsigned u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ unsigned as_u32(float f) { return __builtin_bit_cast(unsigned, f); }
+
+// x of lane l ^ 16 (ds_swizzle in bit-mask mode, xor mask 16): runs on the
+// LDS unit without touching memory, so it takes no vector-ALU issue slot.
+__device__ __forceinline__ float swap16(float x) {
+  return as_f32((unsigned)__builtin_amdgcn_ds_swizzle((int)as_u32(x), 0x401F));
+}
 
 // v_permlane16_swap_b32 with both operands x: the first result holds rows
 // (16-lane groups) 0, 0, 2, 2 of x and the second rows 1, 1, 3, 3, so their

@@ -21,6 +21,7 @@ struct AttnArgs {
   int batch, seqlen, nheads, nheads_k;
   int n_qtiles;               // query tiles per (batch, head)
   int jobs_per_wg;
+  int num_wgs;                // workgroups of the launch (the job table's row length)
   const int2* jobs;           // [jobs_per_wg][gridDim.x]
   float scale_log2;           // softmax_scale * log2(e)
   const float* q_descale;     // fp8 only
