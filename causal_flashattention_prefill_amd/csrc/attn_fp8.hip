@@ -118,6 +118,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   constexpr int KA_BYTES = kTileK * 128;            // K region for d 0..127
   constexpr int KB_BYTES = D192 ? kTileK * 64 : 0;  // K region for d 128..191
   constexpr int K_SLOT = KA_BYTES + KB_BYTES;
+  // LDS fragment prefetch distance of the matrix cluster (16-key or
+  // 16-column blocks); d 192 has fewer registers to spare
+  constexpr int kPf = D192 ? 1 : 2;
   constexpr int V_SLOT = kTileK * DV;
   static_assert(KA_BYTES == 16 * 1024 && V_SLOT == 16 * 1024 && (!D192 || KB_BYTES == 8 * 1024), "tile split");
 
@@ -181,8 +184,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       const int K0 = q0 / kTileK;
 
       // Q fragments (B operand): lane (g, n) holds q[row n][16g..16g+15] and
-      // q[row n][64+16g..]; for d 192 also q[row n][128+16g..] (upper half 0).
-      i32x8 qf[2], qf2[2];
+      // q[row n][64+16g..]; for d 192 also q[row n][128+8g..+7] and
+      // q[row n][160+8g..+7], the B operands of two 16x16x32 FP8 MFMAs over
+      // d 128..191.
+      i32x8 qf[2];
+      long qx[2][2];
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg) {
         const int off = (qw0 + 16 * qg + n) * qrs;
@@ -190,8 +196,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         const u32x4 hi = buf_load16(rq, off + 64 + 16 * g);
         qf[qg] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         if (D192) {
-          const u32x4 x = buf_load16(rq, off + 128 + 16 * g);
-          qf2[qg] = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+          qx[qg][0] = __builtin_bit_cast(long, buf_load8(rq, off + 128 + 8 * g));
+          qx[qg][1] = __builtin_bit_cast(long, buf_load8(rq, off + 160 + 8 * g));
         }
       }
 
@@ -275,9 +281,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
 
       // K fragments of 16-key block kb (A operand): lane (g, n) holds key
       // row 16 kb + n, d 16g..16g+15 and 64+16g.. (and, for d 192, d
-      // 128+16g.. with the upper half zero).
+      // 128+8g..+7 and 160+8g..+7).
       struct KFrag {
-        i32x8 a, b;
+        i32x8 a;
+        long b0, b1;
       };
       auto k_frag = [&](const char* ka, int kb) {
         KFrag f;
@@ -287,8 +294,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         const u32x4 hi = lds_load<u32x4>(ka + row * 128 + (((4 + g) ^ sw) << 4));
         f.a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         if (D192) {
-          const u32x4 x = lds_load<u32x4>(ka + KA_BYTES + row * 64 + ((g ^ ((row >> 2) & 3)) << 4));
-          f.b = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+          // 64-byte rows, 16-byte chunks swizzled by (row >> 2) & 3: d
+          // 128+8g.. is half g & 1 of chunk g >> 1, d 160+8g.. of chunk
+          // 2 + (g >> 1)
+          const char* kr = ka + KA_BYTES + row * 64 + (g & 1) * 8;
+          const int sw2 = (row >> 2) & 3;
+          f.b0 = __builtin_bit_cast(long, lds_load<u32x2>(kr + (((g >> 1) ^ sw2) << 4)));
+          f.b1 = __builtin_bit_cast(long, lds_load<u32x2>(kr + (((2 + (g >> 1)) ^ sw2) << 4)));
         }
         return f;
       };
@@ -301,39 +313,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         const bool pv = t >= 1 && t - 1 <= kt_w;
         if (pv) {
           const char* vs = vring + ((t - 1) % kSlots) * V_SLOT;
-          i32x8 vfb[2] = {v_frag(vs, 0), v_frag(vs, 1)};
+          i32x8 vfb[2];
+          vfb[0] = v_frag(vs, 0);
+          if (kPf == 2) vfb[1] = v_frag(vs, 1);
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) lacc[qg] = mfma_fp8(ones, pf[qg], lacc[qg], kE8M0One, psc[qg]);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * kPf, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
-            const i32x8 cur = vfb[db & 1];
-            if (db + 2 < 8) vfb[db & 1] = v_frag(vs, db + 2);
+            const i32x8 cur = vfb[db % kPf];
+            if (db + kPf < 8) vfb[db % kPf] = v_frag(vs, db + kPf);
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg) o[qg][db] = mfma_fp8(cur, pf[qg], o[qg][db], kE8M0One, psc[qg]);
-            if (db + 2 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+            if (db + kPf < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
           }
         }
         if (t <= kt_w) {
           const char* ka = kring + (t % kSlots) * K_SLOT;
           // K fragments are read two 16-key blocks ahead of their MFMAs
-          KFrag kfb[2] = {k_frag(ka, 0), k_frag(ka, 1)};
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 ? 6 : 4, 0);
+          KFrag kfb[2];
+          kfb[0] = k_frag(ka, 0);
+          if (kPf == 2) kfb[1] = k_frag(ka, 1);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (D192 ? 4 : 2) * kPf, 0);
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) {
-            const KFrag cur = kfb[kb & 1];
-            if (kb + 2 < 8) kfb[kb & 1] = k_frag(ka, kb + 2);
+            const KFrag cur = kfb[kb % kPf];
+            if (kb + kPf < 8) kfb[kb % kPf] = k_frag(ka, kb + kPf);
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg)
               s[qg][kb] = mfma_fp8(cur.a, qf[qg], f32x4{0.f, 0.f, 0.f, 0.f}, kE8M0One, kE8M0One);
             if (D192) {
 #pragma unroll
-              for (int qg = 0; qg < 2; ++qg) s[qg][kb] = mfma_fp8(cur.b, qf2[qg], s[qg][kb], kE8M0One, kE8M0One);
+              for (int qg = 0; qg < 2; ++qg) {
+                s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur.b0, qx[qg][0], s[qg][kb], 0, 0, 0);
+                s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur.b1, qx[qg][1], s[qg][kb], 0, 0, 0);
+              }
             }
-            if (kb + 2 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 ? 3 : 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, D192 ? 4 : 2, 0);
+            if (kb + kPf < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 ? 4 : 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, D192 ? 6 : 2, 0);
           }
         }
         __builtin_amdgcn_s_setprio(0);

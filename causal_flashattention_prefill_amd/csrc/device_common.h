@@ -36,6 +36,11 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// 8-byte load at a byte offset; zeros past the resource's extent.
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
 // Direct global-to-LDS load (buffer_load_dwordx4 ... lds): lane L of the
 // wave writes its 16 bytes to lds_wave_base + 16 * L. lds_wave_base must be
 // the same for the whole wave. Past the resource's extent the bytes are zero.
