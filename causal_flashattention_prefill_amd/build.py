@@ -21,6 +21,7 @@ SOURCES = ["api.cpp", "plan.cpp", "attn_bf16.hip", "attn_fp8.hip", "fp8_quantize
 # a matrix-instruction result costs an extra canonicalising instruction.
 EXTRA_FLAGS = {
     "attn_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 BUILD_DIR = os.path.join(HERE, "_build")
 

@@ -64,7 +64,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
 
   __shared__ __attribute__((aligned(16))) char smem[kStages * STAGE];
 
-  const int tid = threadIdx.x;
+  // work-item and group ids from the hardware registers directly (the
+  // device-library accessors are not inlined into a kernel compiled with
+  // IEEE mode off, and a call would spill every live register)
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+  const int wg = (int)__builtin_amdgcn_workgroup_id_x();
   const int lane = tid & 63;
   // wave-uniform values live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -75,7 +79,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   for (int it = 0; it < a.jobs_per_wg; ++it) {
-    const int2 jv = a.jobs[it * (int)gridDim.x + (int)blockIdx.x];
+    const int2 jv = a.jobs[it * a.num_wgs + wg];
     const int2 job = {__builtin_amdgcn_readfirstlane(jv.x), __builtin_amdgcn_readfirstlane(jv.y)};
     if (job.x < 0) break;
     const int b = job.x / a.nheads;
@@ -202,8 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg) {
-              float rm = fmaxf(mx[qg], __shfl_xor(mx[qg], 16));
-              rm = fmaxf(rm, __shfl_xor(rm, 32));
+              const float rm = max_xor32(max_xor16(mx[qg]));
               const float mn = fmaxf(mref[qg], rm);
               const float f = fast_exp2(mref[qg] - mn);
               lsum[qg] *= f;
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
         for (int qg = 0; qg < 2; ++qg) {
           float lt;
           if (WITH_LSE) {
-            lt = lsum[qg] + __shfl_xor(lsum[qg], 16);
+            lt = lsum[qg] + swap16(lsum[qg]);
             lt += __shfl_xor(lt, 32);
           } else {
             lt = lacc[qg][0];
