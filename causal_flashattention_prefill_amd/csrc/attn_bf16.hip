@@ -100,7 +100,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
     const int tB = a.n_qtiles - 1 - job.y;
     const int ntiles = (tA == tB) ? 1 : 2;
     for (int tt = 0; tt < ntiles; ++tt) {
-      const int qt = tt == 0 ? tA : tB;
+      // the longer tile first: the workgroups of one chiplet then stream the
+      // same keys at the same time for longer, so K and V stay in its L2
+      const int qt = tt == 0 ? tB : tA;
       const int q0 = qt * kTileQ;
       const int qw0 = q0 + wave * 32;
       const int qend = min(q0 + kTileQ, S);
