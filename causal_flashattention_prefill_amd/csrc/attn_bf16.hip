@@ -152,11 +152,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
         }
       };
 
-      // One key tile read from ring stage `cur` while the next streams into
-      // `nxt`: S^T = K Q^T, softmax, O^T += V^T P^T.
-      auto step = [&](char* const cur, char* const nxt, int kt) {
-        const bool more = kt + 1 < n_kt;
-        if (more) issue_kv(kt + 1, nxt);
+      // Key tiles are visited in ascending order for the first (longer)
+      // query tile of the pair and in descending order for the second. A
+      // pair's tiles together span the same number of key tiles for every
+      // pair, so the workgroups of a chiplet that have moved on to their
+      // second tiles all read the same key tile at the same time and share
+      // it in L2.
+      const bool rev = tt == 1;
+      auto tile_of = [&](int j) { return rev ? n_kt - 1 - j : j; };
+      // Step j: key tile tile_of(j) is read from ring stage `cur` while the
+      // next streams into `nxt`: S^T = K Q^T, softmax, O^T += V^T P^T.
+      auto step = [&](char* const cur, char* const nxt, int j) {
+        const int kt = tile_of(j);
+        const bool more = j + 1 < n_kt;
+        if (more) issue_kv(tile_of(j + 1), nxt);
         if (kt <= kt_w) {
           // ---- S^T = K Q^T
           f32x4 s[2][4];
@@ -274,20 +283,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       };
 
       __syncthreads();   // the previous tile's last reads of the ring are done
-      issue_kv(0, smem);
+      issue_kv(tile_of(0), smem);
       wait_vm<0>();
       __syncthreads();
       if (DQK == 128) {
         // unrolled by the two stages: every LDS offset is an immediate
-        for (int kt = 0; kt < n_kt; kt += 2) {
-          step(smem, smem + STAGE, kt);
-          if (kt + 1 < n_kt) step(smem + STAGE, smem, kt + 1);
+        for (int j = 0; j < n_kt; j += 2) {
+          step(smem, smem + STAGE, j);
+          if (j + 1 < n_kt) step(smem + STAGE, smem, j + 1);
         }
       } else {
         // d_qk = 192 keeps 48 registers of Q; a rolled loop leaves room
-        for (int kt = 0; kt < n_kt; ++kt) {
-          const int st = kt & 1;
-          step(smem + st * STAGE, smem + (st ^ 1) * STAGE, kt);
+        for (int j = 0; j < n_kt; ++j) {
+          const int st = j & 1;
+          step(smem + st * STAGE, smem + (st ^ 1) * STAGE, j);
         }
       }
 
