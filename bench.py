@@ -69,11 +69,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash(dtype: str) -> str:
+    """Hash of the kernel sources with comments and blank space removed, so
+    that a comment edit keeps a stored reading valid and a code edit does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[dtype]:
-        with open(os.path.join(PKG, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(PKG, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(f.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 

@@ -8,8 +8,13 @@
 //
 // Structure (shared with the BF16 kernel: persistent 8-wave workgroups, jobs
 // = pairs of 256-row query tiles, 32 query rows per wave, transposed scores):
-//  - Keys stream in 128-key tiles through a two-stage LDS ring filled by
-//    direct global-to-LDS loads issued one tile ahead.
+//  - Keys stream in 128-key tiles through four-slot K and V rings in LDS,
+//    filled by direct global-to-LDS loads two tiles (K) and one tile (V)
+//    ahead of use.
+//  - Ping-pong (README, Kernel design: ping-pong schedule): the two waves
+//    that share a SIMD run half a tile apart, so while one issues the
+//    matrix instructions of a tile the other runs the vector work of its
+//    own; one barrier per interval keeps the groups in step.
 //  - S^T = K Q^T with v_mfma_scale_f32_16x16x128_f8f6f4 (neutral scales);
 //    the three descales and the softmax scale are folded into one base-2
 //    factor read from device memory at kernel start.
@@ -22,8 +27,9 @@
 //    (v_cvt_scalef32_pk_fp8_f32, RNE).
 //  - Lean P (README, Kernel design: lean P): the e4m3fn code of a positive
 //    value grows by 8 per doubling, so the code of 2^y is written directly as
-//    RNE(8 y + C), clamped to 0..255 by v_cvt_pk_u8_f32 (one FMA and one
-//    conversion per score instead of an exponential and an FP8 conversion).
+//    RNE(8 y + C), clamped to 0..255 (one FMA per score and one packing
+//    conversion per two scores instead of an exponential and an FP8
+//    conversion).
 //    C = 56 + 8 log2(2 ln^2 2) makes the piecewise-linear value unbiased.
 //    Lean P is used on key tiles that lie wholly before the workgroup's
 //    256-row query tile; the key tiles that overlap the query tile keep exact
@@ -41,8 +47,8 @@
 //    score layout of the MFMA puts key 16g + 4c + i (and 64 + ...) in lane
 //    group g: the MFMA k index of P equals the key's offset in the tile and
 //    each E8M0 scale block is 32 consecutive keys.
-//  - d_qk = 192 adds one MFMA per score block over d 128..191 with the
-//    remaining half of the K dimension zero.
+//  - d_qk = 192 adds d 128..191 to every score block through two
+//    v_mfma_f32_16x16x32_fp8_fp8 (8-byte operands, no zero padding).
 //
 // Fragment layout of the 16x16x128 FP8 MFMA (lane = 16*g + r, g = lane/16):
 // A (16 x 128): lane holds row r, bytes 0..15 = k 16g..16g+15 and bytes
