@@ -8,9 +8,14 @@
 //  - A job is a pair of 256-row query tiles (i, n-1-i) of one (batch, head)
 //    (README, Kernel design: work distribution). Each wave owns 32 query
 //    rows (two 16-row groups) for the whole key loop.
-//  - Keys stream in 64-key tiles through a two-stage LDS ring filled by
-//    direct global-to-LDS loads (buffer_load ... lds): the loads of tile t+1
-//    are issued before the MFMA work on tile t and waited for after it.
+//  - Keys stream in 64-key tiles through four-slot K and V rings in LDS,
+//    filled by direct global-to-LDS loads (buffer_load ... lds) two tiles
+//    (K) and one tile (V) ahead of use, all issued by the lag wave group.
+//  - Ping-pong (README, Kernel design: ping-pong schedule; the post
+//    "Attention at the Power Cap", two wave groups half a tile apart): the
+//    two waves that share a SIMD run half a tile apart, so while one issues
+//    the matrix instructions of a tile the other computes the softmax of
+//    its own; one barrier per interval keeps the groups in step.
 //  - Scores are computed transposed, S^T = K Q^T, with K as the MFMA A
 //    operand (README, Kernel design: transposed scores), using
 //    v_mfma_f32_16x16x32_bf16. Lane (g, n) (g = lane/16, n = lane%16) then
@@ -20,8 +25,6 @@
 //  - O^T += V^T P^T with V^T read from LDS by ds_read_b64_tr_b16, which
 //    transposes 16-bit values during the read, so V is stored in LDS as it
 //    arrives from memory.
-//  - One barrier per key tile; at d_qk = 128 the key loop is unrolled by the
-//    two ring stages so every LDS offset is an immediate.
 //  - Online softmax in base 2 (log2(e) folded into the scale, one FMA per
 //    score before the exponential) with a lazy reference maximum: it moves
 //    only when some score passes it by kTau; one wave-wide ballot decides,
@@ -32,8 +35,6 @@
 //    of the bf16 P against ones per 32 keys, so the output is divided by the
 //    sum of exactly the rounded weights that multiply V.
 //  - Every conversion rounds to nearest even (README, Kernel design).
-#include <type_traits>
-
 #include "device_common.h"
 #include "zyfa_internal.h"
 
@@ -43,7 +44,7 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kTileQ = 256;
 constexpr int kTileK = 64;
-constexpr int kStages = 2;
+constexpr int kSlots = 4;              // K and V ring depth
 constexpr float kTau = 8.0f;           // lazy-rescale threshold, log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -54,15 +55,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   constexpr int KPITCH = DQK * 2;              // bytes per K row in LDS
   constexpr int VPITCH = DV * 2;
   constexpr int KSWZ = (KCH % 16 == 0) ? 15 : 7;
-  constexpr int KBYTES = kTileK * KPITCH;
-  constexpr int VBYTES = kTileK * VPITCH;
-  constexpr int STAGE = KBYTES + VBYTES;
+  constexpr int K_SLOT = kTileK * KPITCH;
+  constexpr int V_SLOT = kTileK * VPITCH;
   constexpr int NC = DQK / 32;                 // MFMA k-steps over d_qk
-  constexpr int KLD = KBYTES / 1024 / 8;       // 1 KiB direct-to-LDS loads per wave per tile
-  constexpr int VLD = VBYTES / 1024 / 8;
-  static_assert(KLD * 8 * 1024 == KBYTES && VLD * 8 * 1024 == VBYTES, "tile split");
+  constexpr int KLD = K_SLOT / 1024 / 8;       // 1 KiB direct-to-LDS loads per wave per tile
+  constexpr int VLD = V_SLOT / 1024 / 8;
+  static_assert(KLD * 8 * 1024 == K_SLOT && VLD * 8 * 1024 == V_SLOT, "tile split");
+  // LDS fragment prefetch distance of the matrix cluster
+  constexpr int kPfV = 4;
+  constexpr int kPfK = 4;
 
-  __shared__ __attribute__((aligned(16))) char smem[kStages * STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[kSlots * (K_SLOT + V_SLOT)];
+  char* const kring = smem;
+  char* const vring = smem + kSlots * K_SLOT;
 
   // work-item and group ids from the hardware registers directly (the
   // device-library accessors are not inlined into a kernel compiled with
@@ -71,9 +76,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   const int wg = (int)__builtin_amdgcn_workgroup_id_x();
   const int lane = tid & 63;
   // wave-uniform values live in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = tid >> 6;
   const int g = lane >> 4;
   const int n = lane & 15;
+  // Waves w and w + 4 share a SIMD. Waves 4..7 (the lead group, which also
+  // holds the query rows with more keys) run half a key tile ahead of waves
+  // 0..3 (the lag group).
+  const bool lead = wave >= 4;
+  // The wave's index within its group, as a scalar: the load addresses
+  // built from it then stay in scalar registers (built from the per-lane
+  // wave index, each load needs vector address arithmetic and a
+  // readfirstlane, and the extra live registers spilled at d_qk = 192).
+  const int wq = __builtin_amdgcn_readfirstlane(wave & 3);
   const int S = a.seqlen;
   const float sl2 = a.scale_log2;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
@@ -90,11 +104,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
     const char* kbase = (const char*)a.k.ptr + 2 * (b * a.k.stride_b + hk * a.k.stride_h);
     const char* vbase = (const char*)a.v.ptr + 2 * (b * a.v.stride_b + hk * a.v.stride_h);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, a.q_bytes);
-    const i32x4 rk = make_rsrc_words(kbase, a.k_bytes);
-    const i32x4 rv = make_rsrc_words(vbase, a.v_bytes);
     const int qrs = (int)(2 * a.q.stride_s);
     const int krs = (int)(2 * a.k.stride_s);
     const int vrs = (int)(2 * a.v.stride_s);
+
+    // Per-lane byte offsets of the direct-to-LDS tile loads (fixed for the
+    // job; the offset of the tile, or of its upper half, goes into the
+    // buffer resource, whose extent still ends at the slice end, so rows
+    // past seqlen read as zeros). The lag group loads every tile: wave wq of
+    // it fills instructions I = wq * n + u (n = KLD or VLD) of each 32-row
+    // half. Instruction I fills bytes [1024 I, 1024 I + 1024) of the half;
+    // lane L's 16 bytes land at p = 1024 I + 16 L, which is row p / pitch,
+    // chunk slot (p % pitch) / 16, so the lane fetches the global chunk that
+    // belongs in that slot (the same offsets serve both halves, 32 rows
+    // apart being a multiple of every swizzle period). K chunks are XOR-swizzled by row so the 16 lanes
+    // that read one chunk column of 16 rows hit distinct banks; V chunks are
+    // swizzled by even values, keeping the 8-byte halves the transposing
+    // read needs intact.
+    int kvo[KLD], vvo[VLD];
+#pragma unroll
+    for (int u = 0; u < KLD; ++u) {
+      const int p = (wq * KLD + u) * 1024 + lane * 16;
+      const int row = p / KPITCH, x = ((p % KPITCH) >> 4) ^ (row & KSWZ);
+      kvo[u] = row * krs + x * 16;
+    }
+#pragma unroll
+    for (int u = 0; u < VLD; ++u) {
+      const int p = (wq * VLD + u) * 1024 + lane * 16;
+      const int row = p / VPITCH, x = ((p % VPITCH) >> 4) ^ ((row & 7) << 1);
+      vvo[u] = row * vrs + x * 16;
+    }
+    auto tile_rsrc = [&](const char* base, unsigned nbytes, int stride, int kt, int half) {
+      const unsigned off = (unsigned)((kt * kTileK + 32 * half) * stride);
+      return make_rsrc_words(base + off, nbytes > off ? nbytes - off : 0u);
+    };
 
     const int tA = job.y;
     const int tB = a.n_qtiles - 1 - job.y;
@@ -107,7 +150,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       const int qw0 = q0 + wave * 32;
       const int qend = min(q0 + kTileQ, S);
       const int n_kt = (qend - 1) / kTileK + 1;
+      // this wave's last key tile (the one holding its diagonal), -1 if the
+      // wave has no rows
       const int kt_w = (qw0 < S) ? min((qw0 + 31) / kTileK, n_kt - 1) : -1;
+
+      // Key tiles are visited in ascending order for the first (longer)
+      // query tile of the pair and in descending order for the second. A
+      // pair's tiles together span the same number of key tiles for every
+      // pair, so the workgroups of a chiplet that have moved on to their
+      // second tiles all read the same key tile at the same time and share
+      // it in L2. Position j of the visit order is key tile tile_of(j); ring
+      // slots follow the position.
+      const bool rev = tt == 1;
+      auto tile_of = [&](int j) { return rev ? n_kt - 1 - j : j; };
+      // whether position j holds a key tile with keys for this wave's rows
+      auto has = [&](int j) { return j < n_kt && tile_of(j) <= kt_w; };
 
       // Q fragments, MFMA B operand: lane (g, n) holds q[row n][32c + 8g .. +7].
       bf16x8 qf[2][NC];
@@ -126,178 +183,219 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
         for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       float mref[2] = {neg_inf(), neg_inf()};
+      // lazy-rescale threshold in raw score units, (m + tau) / sl2
+      float thr[2] = {neg_inf(), neg_inf()};
       float lsum[2] = {0.f, 0.f};
+      // scores of the tile in flight (made by a matrix cluster, turned into
+      // P by the next vector cluster) and the bf16 P (made by a vector
+      // cluster, multiplied into V by the next matrix cluster)
+      f32x4 s[2][4];
+      bf16x8 pb[2][2];
 
-      // K/V tiles go straight from memory into LDS. Wave-instruction I fills
-      // bytes [1024 I, 1024 I + 1024) of a region; lane L's 16 bytes land at
-      // p = 1024 I + 16 L, which is row p / pitch, chunk slot (p % pitch) / 16,
-      // so the lane fetches the global chunk that belongs in that slot. K
-      // chunks are XOR-swizzled by row so the 16 lanes that read one chunk
-      // column of 16 rows hit distinct banks; V chunks are swizzled by even
-      // values, keeping the 8-byte halves the transposing read needs intact.
-      auto issue_kv = [&](int kt, char* stage) {
+      auto issue_k = [&](int j) {
 #pragma unroll
-        for (int u = 0; u < KLD; ++u) {
-          const int I = wave * KLD + u;
-          const int p = I * 1024 + lane * 16;
-          const int row = p / KPITCH, x = ((p % KPITCH) >> 4) ^ (row & KSWZ);
-          dma16(rk, (kt * kTileK + row) * krs + x * 16, stage + I * 1024);
+        for (int hs = 0; hs < 2; ++hs) {
+          char* base = kring + (j % kSlots) * K_SLOT + hs * (K_SLOT / 2);
+          const i32x4 r = tile_rsrc(kbase, a.k_bytes, krs, tile_of(j), hs);
+#pragma unroll
+          for (int u = 0; u < KLD; ++u) dma16(r, kvo[u], base + (wq * KLD + u) * 1024);
         }
+      };
+      auto issue_v = [&](int j) {
 #pragma unroll
-        for (int u = 0; u < VLD; ++u) {
-          const int I = wave * VLD + u;
-          const int p = I * 1024 + lane * 16;
-          const int row = p / VPITCH, x = ((p % VPITCH) >> 4) ^ ((row & 7) << 1);
-          dma16(rv, (kt * kTileK + row) * vrs + x * 16, stage + KBYTES + I * 1024);
+        for (int hs = 0; hs < 2; ++hs) {
+          char* base = vring + (j % kSlots) * V_SLOT + hs * (V_SLOT / 2);
+          const i32x4 r = tile_rsrc(vbase, a.v_bytes, vrs, tile_of(j), hs);
+#pragma unroll
+          for (int u = 0; u < VLD; ++u) dma16(r, vvo[u], base + (wq * VLD + u) * 1024);
         }
       };
 
-      // Key tiles are visited in ascending order for the first (longer)
-      // query tile of the pair and in descending order for the second. A
-      // pair's tiles together span the same number of key tiles for every
-      // pair, so the workgroups of a chiplet that have moved on to their
-      // second tiles all read the same key tile at the same time and share
-      // it in L2.
-      const bool rev = tt == 1;
-      auto tile_of = [&](int j) { return rev ? n_kt - 1 - j : j; };
-      // Step j: key tile tile_of(j) is read from ring stage `cur` while the
-      // next streams into `nxt`: S^T = K Q^T, softmax, O^T += V^T P^T.
-      auto step = [&](char* const cur, char* const nxt, int j) {
-        const int kt = tile_of(j);
-        const bool more = j + 1 < n_kt;
-        if (more) issue_kv(tile_of(j + 1), nxt);
-        if (kt <= kt_w) {
-          // ---- S^T = K Q^T
-          f32x4 s[2][4];
+      // V^T fragment idx = 8 kc + db (keys 32 kc .., columns 16 db ..), A
+      // operand of O^T += V^T P^T: two transposing reads of 4 x 16 blocks.
+      auto v_frag = [&](const char* vs, int idx) {
+        const int kc = idx >> 3, db = idx & 7;
+        u32x2 t[2];
 #pragma unroll
-          for (int qg = 0; qg < 2; ++qg)
+        for (int hf = 0; hf < 2; ++hf) {
+          const int row = 32 * kc + 16 * hf + 4 * g + (n >> 2);
+          const int x = 2 * db + ((n & 3) >> 1);
+          t[hf] = __builtin_bit_cast(u32x2, lds_read_tr16(vs + row * VPITCH + ((x ^ ((row & 7) << 1)) << 4) + (n & 1) * 8));
+        }
+        return __builtin_bit_cast(bf16x8, u32x4{t[0][0], t[0][1], t[1][0], t[1][1]});
+      };
+      // K fragment idx = 4 c + kb (key rows 16 kb + n, d 32 c + 8 g ..), A
+      // operand of S^T = K Q^T.
+      auto k_frag = [&](const char* ks, int idx) {
+        const int c = idx >> 2, kb = idx & 3;
+        const int row = 16 * kb + n;
+        const int x = 4 * c + g;
+        return lds_load<bf16x8>(ks + row * KPITCH + ((x ^ (row & KSWZ)) << 4));
+      };
+
+      // Matrix cluster at position j: O^T += V^T P^T and the row sum for
+      // position j - 1 (P from the previous vector cluster), then the scores
+      // S^T = K Q^T at position j.
+      auto matrix_cluster = [&](int j) {
+        __builtin_amdgcn_s_setprio(1);
+        if (j >= 1 && has(j - 1)) {
+          const char* vs = vring + ((j - 1) % kSlots) * V_SLOT;
+          bf16x8 vfb[kPfV];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) s[qg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-              const int row = 16 * kb + n;
-              const int x = 4 * c + g;
-              const bf16x8 kf = lds_load<bf16x8>(cur + row * KPITCH + ((x ^ (row & KSWZ)) << 4));
-#pragma unroll
-              for (int qg = 0; qg < 2; ++qg)
-                s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qg][c], s[qg][kb], 0, 0, 0);
-            }
-          // ---- causal mask, on diagonal tiles only (kept a real branch)
-          const int kbase = kt * kTileK;
-          if (__builtin_expect(kbase + kTileK - 1 > qw0, 0)) {
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int qg = 0; qg < 2; ++qg) {
-              const int q = qw0 + 16 * qg + n - kbase - 4 * g;
-#pragma unroll
-              for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (16 * kb + i > q) s[qg][kb][i] = neg_inf();
-            }
-          }
-          // ---- lazy max: a lane-local test and one ballot per tile
-          float mx[2];
-#pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
-            float m = fmaxf(fmaxf(s[qg][0][0], s[qg][0][1]), s[qg][0][2]);
-            m = fmaxf(fmaxf(m, s[qg][0][3]), s[qg][1][0]);
-            m = fmaxf(fmaxf(m, s[qg][1][1]), s[qg][1][2]);
-            m = fmaxf(fmaxf(m, s[qg][1][3]), s[qg][2][0]);
-            m = fmaxf(fmaxf(m, s[qg][2][1]), s[qg][2][2]);
-            m = fmaxf(fmaxf(m, s[qg][2][3]), s[qg][3][0]);
-            m = fmaxf(fmaxf(m, s[qg][3][1]), s[qg][3][2]);
-            mx[qg] = fmaxf(m, s[qg][3][3]) * sl2;
-          }
-          if (__builtin_expect(wave_any((mx[0] > mref[0] + kTau) || (mx[1] > mref[1] + kTau)), 0)) {
-            // Keep this branch real: with f == 1 the multiplies are harmless,
-            // so the compiler would otherwise run them on every tile.
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int qg = 0; qg < 2; ++qg) {
-              const float rm = max_xor32(max_xor16(mx[qg]));
-              const float mn = fmaxf(mref[qg], rm);
-              const float f = fast_exp2(mref[qg] - mn);
-              lsum[qg] *= f;
-              lacc[qg] *= f;
-#pragma unroll
-              for (int db = 0; db < 8; ++db) o[qg][db] *= f;
-              mref[qg] = mn;
-            }
-          }
-          // ---- P = exp2(s * scale - m), RNE to bf16. Operands are assembled
-          // as whole 32-bit words: building them element by element from
-          // 16-bit values has been compiled incorrectly (every slot took
-          // element 0).
-          bf16x8 pb[2][2];
-#pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
-            const float nm = -mref[qg];
-            float ls = 0.f;
-            u32x4 w[2];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-              f32x4 p;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, nm));
-                if (WITH_LSE) ls += p[i];
-              }
-              w[kb >> 1][2 * (kb & 1) + 0] = pack_bf16x2(p[0], p[1]);
-              w[kb >> 1][2 * (kb & 1) + 1] = pack_bf16x2(p[2], p[3]);
-            }
-            pb[qg][0] = __builtin_bit_cast(bf16x8, w[0]);
-            pb[qg][1] = __builtin_bit_cast(bf16x8, w[1]);
-            if (WITH_LSE) lsum[qg] += ls;
-          }
-          // ---- O^T += V^T P^T (and the row sum of the rounded P when no LSE)
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int db = 0; db < 8; ++db) {
-              u32x2 t[2];
-#pragma unroll
-              for (int hf = 0; hf < 2; ++hf) {
-                const int row = 32 * kc + 16 * hf + 4 * g + (n >> 2);
-                const int x = 2 * db + ((n & 3) >> 1);
-                const char* p = cur + KBYTES + row * VPITCH + ((x ^ ((row & 7) << 1)) << 4) + (n & 1) * 8;
-                t[hf] = __builtin_bit_cast(u32x2, lds_read_tr16(p));
-              }
-              const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{t[0][0], t[0][1], t[1][0], t[1][1]});
-#pragma unroll
-              for (int qg = 0; qg < 2; ++qg)
-                o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qg][kc], o[qg][db], 0, 0, 0);
-            }
+          for (int u = 0; u < kPfV; ++u) vfb[u] = v_frag(vs, u);
           if (!WITH_LSE) {
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
               for (int kc = 0; kc < 2; ++kc)
                 lacc[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qg][kc], lacc[qg], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPfV, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+          }
+#pragma unroll
+          for (int idx = 0; idx < 16; ++idx) {
+            const bf16x8 cur = vfb[idx % kPfV];
+            if (idx + kPfV < 16) vfb[idx % kPfV] = v_frag(vs, idx + kPfV);
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg)
+              o[qg][idx & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pb[qg][idx >> 3], o[qg][idx & 7], 0, 0, 0);
+            if (idx + kPfV < 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
           }
         }
-        if (more) wait_vm<0>();
-        __syncthreads();
+        if (has(j)) {
+          const char* ks = kring + (j % kSlots) * K_SLOT;
+          bf16x8 kfb[kPfK];
+#pragma unroll
+          for (int u = 0; u < kPfK; ++u) kfb[u] = k_frag(ks, u);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPfK, 0);
+#pragma unroll
+          for (int idx = 0; idx < 4 * NC; ++idx) {
+            const bf16x8 cur = kfb[idx % kPfK];
+            if (idx + kPfK < 4 * NC) kfb[idx % kPfK] = k_frag(ks, idx + kPfK);
+            const int c = idx >> 2, kb = idx & 3;
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg)
+              s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[qg][c], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[qg][kb], 0, 0, 0);
+            if (idx + kPfK < 4 * NC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
       };
 
-      __syncthreads();   // the previous tile's last reads of the ring are done
-      issue_kv(tile_of(0), smem);
+      // Vector cluster at position j: causal mask (diagonal tiles), lane
+      // maxima, lazy rescale, P = exp2(s * scale - m) rounded to bf16, and
+      // the fp32 row sum when the LSE is requested.
+      auto vector_cluster = [&](int j) {
+        if (!has(j)) return;
+        const int kt0 = tile_of(j) * kTileK;
+        // ---- causal mask, on diagonal tiles only; score (kb, i) of lane
+        // group g is key 16 kb + 4 g + i of the tile
+        if (__builtin_expect(kt0 + kTileK - 1 > qw0, 0)) {
+          const float ninf = neg_inf();
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            const int q = qw0 + 16 * qg + n - kt0 - 4 * g;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) s[qg][kb][i] = mask_above(s[qg][kb][i], 16 * kb + i, q, ninf);
+          }
+        }
+        // ---- lazy max: lane maxima of the raw scores, one ballot per tile
+        float x[2];
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+          float m = fmaxf(fmaxf(s[qg][0][0], s[qg][0][1]), s[qg][0][2]);
+#pragma unroll
+          for (int e = 3; e < 15; e += 2)
+            m = fmaxf(fmaxf(m, s[qg][e >> 2][e & 3]), s[qg][(e + 1) >> 2][(e + 1) & 3]);
+          x[qg] = fmaxf(m, s[qg][3][3]);
+        }
+        if (__builtin_expect(wave_any((x[0] > thr[0]) || (x[1] > thr[1])), 0)) {
+          // Keep this branch real: with f == 1 the multiplies are harmless,
+          // so the compiler would otherwise run them on every tile.
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            const float rm = max_xor32(max_xor16(x[qg])) * sl2;
+            const float mn = fmaxf(mref[qg], rm);
+            const float f = fast_exp2(mref[qg] - mn);
+            lsum[qg] *= f;
+            lacc[qg] *= f;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[qg][db] *= f;
+            mref[qg] = mn;
+            thr[qg] = (mn + kTau) / sl2;
+          }
+        }
+        // ---- P = exp2(s * scale - m), RNE to bf16. Operands are assembled
+        // as whole 32-bit words: building them element by element from
+        // 16-bit values has been compiled incorrectly (every slot took
+        // element 0).
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+          const float nm = -mref[qg];
+          float ls = 0.f;
+          u32x4 w[2];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            f32x4 p;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, nm));
+              if (WITH_LSE) ls += p[i];
+            }
+            w[kb >> 1][2 * (kb & 1) + 0] = pack_bf16x2(p[0], p[1]);
+            w[kb >> 1][2 * (kb & 1) + 1] = pack_bf16x2(p[2], p[3]);
+          }
+          pb[qg][0] = __builtin_bit_cast(bf16x8, w[0]);
+          pb[qg][1] = __builtin_bit_cast(bf16x8, w[1]);
+          if (WITH_LSE) lsum[qg] += ls;
+        }
+      };
+
+      // Ping-pong over intervals closed by one barrier each. In interval i
+      // the lead group runs the vector cluster of position i - 1 and then
+      // the matrix cluster of position i; the lag group runs the matrix
+      // cluster of position i - 1 and then its vector cluster. On every SIMD
+      // one wave is in a matrix cluster while the other computes a softmax.
+      // Interval i reads K(i - 1), K(i), V(i - 2) and V(i - 1). Between its
+      // two clusters each lag wave issues its share of K(i + 2) and V(i + 1)
+      // into the slots last read in interval i - 1 (four-slot rings); before
+      // the barrier it waits for the loads issued one interval earlier
+      // (K(i + 1), V(i), read from interval i + 1 on). The lead group issues
+      // no loads: it carries the longer chain of the interval (its softmax
+      // and then its matrix cluster, while the lag group's softmax runs
+      // beside that matrix cluster), and a wave that issues direct-to-LDS
+      // loads is held until the address unit has accepted them. The last position with work for the lag group
+      // is n_kt - 1 in descending order and its last key tile in ascending
+      // order; its PV runs two intervals later.
+      const int lag_last = rev ? n_kt - 1 : min((q0 + 127) / kTileK, n_kt - 1);
+      const int n_int = max(n_kt + 1, lag_last + 3);
+      __syncthreads();   // the previous query tile's last reads of the rings are done
+      if (!lead) {
+        issue_k(0);
+        if (n_kt > 1) issue_k(1);
+        issue_v(0);
+      }
       wait_vm<0>();
       __syncthreads();
-      if (DQK == 128) {
-        // unrolled by the two stages: every LDS offset is an immediate
-        for (int j = 0; j < n_kt; j += 2) {
-          step(smem, smem + STAGE, j);
-          if (j + 1 < n_kt) step(smem + STAGE, smem, j + 1);
+      for (int i = 0; i < n_int; ++i) {
+        if (lead) {
+          if (i >= 1) vector_cluster(i - 1);
+          matrix_cluster(i);
+        } else {
+          if (i >= 1) matrix_cluster(i - 1);
+          if (i + 2 < n_kt) issue_k(i + 2);
+          if (i + 1 < n_kt) issue_v(i + 1);
+          if (i >= 1) vector_cluster(i - 1);
+          if (i + 2 < n_kt) wait_vm<2 * (KLD + VLD)>();
+          else if (i + 1 < n_kt) wait_vm<2 * VLD>();
+          else wait_vm<0>();
         }
-      } else {
-        // d_qk = 192 keeps 48 registers of Q; a rolled loop leaves room
-        for (int j = 0; j < n_kt; ++j) {
-          const int st = j & 1;
-          step(smem + st * STAGE, smem + (st ^ 1) * STAGE, j);
-        }
+        __syncthreads();
       }
 
       // ---- epilogue: O / l (RNE to bf16), LSE = ln2 * (m + log2 l)

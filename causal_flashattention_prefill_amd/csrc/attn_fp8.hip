@@ -10,7 +10,7 @@
 // = pairs of 256-row query tiles, 32 query rows per wave, transposed scores):
 //  - Keys stream in 128-key tiles through four-slot K and V rings in LDS,
 //    filled by direct global-to-LDS loads two tiles (K) and one tile (V)
-//    ahead of use.
+//    ahead of use, all issued by the lag wave group.
 //  - Ping-pong (README, Kernel design: ping-pong schedule): the two waves
 //    that share a SIMD run half a tile apart, so while one issues the
 //    matrix instructions of a tile the other runs the vector work of its
@@ -68,9 +68,6 @@ constexpr int kSlots = 4;             // K and V ring depth
 constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kE8M0One = 127;           // E8M0 scale 2^0
-// sched_group_barrier instruction classes.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
 // Lean-P constant 56 + 8 log2(2 ln(2)^2).
 constexpr float kLeanC = 55.539734f;
 constexpr float kInv65535 = 1.0f / 65535.0f;
@@ -80,18 +77,6 @@ __device__ __forceinline__ int vsw(int r) { return ((r >> 1) & 3) | ((r >> 2) & 
 
 // Key held by LDS row r of a K tile: bits [5:4] and [3:2] of r swapped.
 __device__ __forceinline__ int kswap(int r) { return (r & ~0x3C) | ((r & 0x30) >> 2) | ((r & 0x0C) << 2); }
-
-// x = -inf where key offset ko > q (the causal mask). One compare into VCC
-// and one select per score; written as assembly so that the compiler does
-// not compute all compares first into scalar register pairs (which it then
-// spills).
-__device__ __forceinline__ float mask_above(float x, int ko, int q, float ninf) {
-  asm volatile("v_cmp_gt_i32_e32 vcc, %1, %2\n\tv_cndmask_b32_e32 %0, %0, %3, vcc"
-               : "+v"(x)
-               : "s"(ko), "v"(q), "v"(ninf)
-               : "vcc");
-  return x;
-}
 
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
@@ -148,6 +133,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   // holds the query rows with more keys) run half a key tile ahead of waves
   // 0..3 (the lag group).
   const bool lead = wave >= 4;
+  // The wave's index within its group, as a scalar, so the load
+  // addresses built from it stay in scalar registers.
+  const int wsc = __builtin_amdgcn_readfirstlane(wave & 3);
   const int S = a.seqlen;
   // Scores in base-2 units: S_codes * (softmax_scale * log2 e * dq * dk).
   const float sl2 = a.scale_log2 * a.q_descale[0] * a.k_descale[0];
@@ -238,37 +226,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // transposing read touches (8 consecutive keys in each of two lane
       // groups) on distinct banks.
       // Per-lane byte offsets of the tile loads (fixed for the job); the
-      // tile's own offset goes into the buffer resource, whose extent still
-      // ends at the slice end, so rows past seqlen read as zeros.
+      // offset of the tile, or of its upper 64-row half, goes into the
+      // buffer resource, whose extent still ends at the slice end, so rows
+      // past seqlen read as zeros. The lag group loads every tile, wave wsc
+      // of it instructions 2 wsc, 2 wsc + 1 (and wsc for d 128..191) of each
+      // half; the same offsets serve both halves (64 rows apart is a
+      // multiple of every swizzle period and kswap keeps bit 6).
       int kvo[3], vvo[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int p = (wave * 2 + u) * 1024 + lane * 16;
+        const int p = (wsc * 2 + u) * 1024 + lane * 16;
         const int row = p >> 7, slot = (p & 127) >> 4;
         kvo[u] = kswap(row) * krs + (slot ^ ((row >> 1) & 7)) * 16;
         vvo[u] = row * vrs + (slot ^ vsw(row)) * 16;
       }
       if (D192) {
-        const int p = wave * 1024 + lane * 16;
+        const int p = wsc * 1024 + lane * 16;
         const int row = p >> 6, x = ((p & 63) >> 4) ^ ((row >> 2) & 3);
         kvo[2] = kswap(row) * krs + 128 + x * 16;
       }
-      auto tile_rsrc = [&](const char* base, unsigned nbytes, int stride, int kt) {
-        const unsigned off = (unsigned)(kt * kTileK * stride);
+      auto tile_rsrc = [&](const char* base, unsigned nbytes, int stride, int kt, int hs) {
+        const unsigned off = (unsigned)((kt * kTileK + 64 * hs) * stride);
         return make_rsrc_words(base + off, nbytes > off ? nbytes - off : 0u);
       };
       auto issue_k = [&](int kt) {
-        char* base = kring + (kt % kSlots) * K_SLOT;
-        const i32x4 r = tile_rsrc(kbase, a.k_bytes, krs, kt);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) dma16(r, kvo[u], base + (wave * 2 + u) * 1024);
-        if (D192) dma16(r, kvo[2], base + KA_BYTES + wave * 1024);
+        for (int hs = 0; hs < 2; ++hs) {
+          char* base = kring + (kt % kSlots) * K_SLOT;
+          const i32x4 r = tile_rsrc(kbase, a.k_bytes, krs, kt, hs);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) dma16(r, kvo[u], base + hs * (KA_BYTES / 2) + (wsc * 2 + u) * 1024);
+          if (D192) dma16(r, kvo[2], base + KA_BYTES + hs * (KB_BYTES / 2) + wsc * 1024);
+        }
       };
       auto issue_v = [&](int kt) {
-        char* base = vring + (kt % kSlots) * V_SLOT;
-        const i32x4 r = tile_rsrc(vbase, a.v_bytes, vrs, kt);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) dma16(r, vvo[u], base + (wave * 2 + u) * 1024);
+        for (int hs = 0; hs < 2; ++hs) {
+          char* base = vring + (kt % kSlots) * V_SLOT;
+          const i32x4 r = tile_rsrc(vbase, a.v_bytes, vrs, kt, hs);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) dma16(r, vvo[u], base + hs * (V_SLOT / 2) + (wsc * 2 + u) * 1024);
+        }
       };
 
       // V^T fragment of 16-column block db: byte 8t + r of lane group g is
@@ -476,36 +474,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // matrix cluster of tile i; the lag group runs the matrix cluster of
       // tile i - 1 and then its vector cluster. On every SIMD one wave is in
       // a matrix cluster while the other computes a softmax. Interval i
-      // reads K(i - 1), K(i), V(i - 2) and V(i - 1). At its end each wave
-      // issues its share of K(i + 2) and V(i + 1) into the slots last read
-      // in interval i - 1 (four-slot rings), and waits for the loads issued
-      // one interval earlier (K(i + 1), V(i), read from interval i + 1 on):
-      // issued at the end, the loads fill the time a wave waits at the
-      // barrier, and each load has a whole interval to arrive. (Issued in a
-      // burst at the start of an interval they queue in the address unit
-      // and stall every wave.) The lag group's last tile (its PV) ends in
-      // interval kt_w + 2, the lead's in kt_w + 1.
+      // reads K(i - 1), K(i), V(i - 2) and V(i - 1). Between its two
+      // clusters each lag wave issues its share of K(i + 2) and V(i + 1)
+      // into the slots last read in interval i - 1 (four-slot rings); before
+      // the barrier it waits for the loads issued one interval earlier
+      // (K(i + 1), V(i), read from interval i + 1 on). The lead group issues
+      // no loads: a wave that issues direct-to-LDS loads is held until the
+      // address unit accepts them, and the lead's softmax-then-matrix chain
+      // is the longer one. (Issued in a burst by all waves at the start of
+      // an interval the loads queue in the address unit and stall every
+      // wave.) The lag group's last tile (its PV) ends in interval
+      // kt_w + 2, the lead's in kt_w + 1.
       const int lag_last = min(K0, n_kt - 1);
       const int n_int = max(n_kt + 1, lag_last + 3);
       __syncthreads();   // the previous query tile's last reads of the rings are done
-      issue_k(0);
-      if (n_kt > 1) issue_k(1);
-      issue_v(0);
+      if (!lead) {
+        issue_k(0);
+        if (n_kt > 1) issue_k(1);
+        issue_v(0);
+      }
       wait_vm<0>();
       __syncthreads();
       for (int i = 0; i < n_int; ++i) {
         if (lead) {
           if (i >= 1) vector_cluster(i - 1);
           matrix_cluster(i);
-        } else if (i >= 1) {
-          matrix_cluster(i - 1);
-          vector_cluster(i - 1);
+        } else {
+          if (i >= 1) matrix_cluster(i - 1);
+          if (i + 2 < n_kt) issue_k(i + 2);
+          if (i + 1 < n_kt) issue_v(i + 1);
+          if (i >= 1) vector_cluster(i - 1);
+          if (i + 2 < n_kt) wait_vm<D192 ? 10 : 8>();
+          else if (i + 1 < n_kt) wait_vm<4>();
+          else wait_vm<0>();
         }
-        if (i + 2 < n_kt) issue_k(i + 2);
-        if (i + 1 < n_kt) issue_v(i + 1);
-        if (i + 2 < n_kt) wait_vm<D192 ? 5 : 4>();
-        else if (i + 1 < n_kt) wait_vm<2>();
-        else wait_vm<0>();
         __syncthreads();
       }
 

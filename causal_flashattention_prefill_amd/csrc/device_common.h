@@ -41,18 +41,6 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
 
-// Direct global-to-LDS load (buffer_load_dwordx4 ... lds): lane L of the
-// wave writes its 16 bytes to lds_wave_base + 16 * L. lds_wave_base must be
-// the same for the whole wave. Past the resource's extent the bytes are zero.
-__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, int off, char* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0,
-                                           0, 0);
-}
-
-// Wait until every outstanding memory operation of this wave (including
-// direct-to-LDS loads) has completed.
-__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
-
 // Raw buffer resource as four scalar words (for inline assembly operands).
 __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, unsigned nbytes) {
   const unsigned long long a = reinterpret_cast<unsigned long long>(base);
@@ -78,15 +66,6 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, int voff, const char* l
                : "memory", "m0");
 }
 
-// dma16 without the compiler memory barrier: LDS reads may be scheduled
-// across it. Only for loads into a ring slot that no LDS read between the
-// surrounding barriers touches.
-__device__ __forceinline__ void dma16_unordered(const i32x4& rsrc, int voff, const char* lds_wave_base) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc) : "m0");
-}
-
 // s_waitcnt vmcnt(N) leaving the LDS and export counters alone (gfx9
 // encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
@@ -98,10 +77,6 @@ __device__ __forceinline__ void wait_vm() {
 template <class T>
 __device__ __forceinline__ T lds_load(const char* p) {
   return *reinterpret_cast<const T*>(p);
-}
-template <class T>
-__device__ __forceinline__ void lds_store(char* p, const T& v) {
-  *reinterpret_cast<T*>(p) = v;
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, the lanes' 8-byte reads
@@ -157,15 +132,22 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(as_f32(a), as_f32(b));
 }
 
-// v_permlane32_swap_b32 of (x, y): returns {lanes 0..31 of x then lanes
-// 0..31 of y, lanes 32..63 of x then lanes 32..63 of y}.
-__device__ __forceinline__ void swap32(float x, float y, float* lo, float* hi) {
-  const auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(y), false, false);
-  const unsigned a = r[0], b = r[1];
-  *lo = as_f32(a);
-  *hi = as_f32(b);
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// x = -inf where key offset ko > q (the causal mask). One compare into VCC
+// and one select per score; written as assembly so that the compiler does
+// not compute all compares first into scalar register pairs (which it then
+// spills).
+__device__ __forceinline__ float mask_above(float x, int ko, int q, float ninf) {
+  asm volatile("v_cmp_gt_i32_e32 vcc, %1, %2\n\tv_cndmask_b32_e32 %0, %0, %3, vcc"
+               : "+v"(x)
+               : "s"(ko), "v"(q), "v"(ninf)
+               : "vcc");
+  return x;
 }
 
-__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+// sched_group_barrier instruction classes.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 }  // namespace zyfa
