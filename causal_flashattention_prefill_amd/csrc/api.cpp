@@ -153,18 +153,14 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   a.q_descale = q_descale;
   a.k_descale = k_descale;
   a.v_descale = v_descale;
-  // Byte extent of one (batch, head) slice from its base: rows past seqlen
-  // fall outside it and read as zero. Offsets up to the padded length must
-  // fit in 31 bits.
-  const long long s_pad = (long long)plan->n_qtiles * plan->tile_q;
-  auto extent = [&](long long ss, int dim) { return ((long long)(seqlen - 1) * ss + dim) * esz; };
-  auto reach = [&](long long ss, int dim) { return ((s_pad + 128) * ss + dim) * esz; };
+  // The kernels address each wave's query rows and each half key tile (at
+  // most 64 rows) through a buffer resource of its own with a 64-bit base,
+  // so only 64 rows of a tensor must fit in 31 bits of byte offset; tensors
+  // and (batch, head) slices may span more than 4 GiB.
+  auto local = [&](long long ss, int dim) { return (64 * ss + dim) * esz; };
   const long long lim = 0x7FFFFFFFll;
-  if (reach(a.q.stride_s, d_qk) > lim || reach(a.k.stride_s, d_qk) > lim || reach(a.v.stride_s, d_v) > lim)
+  if (local(a.q.stride_s, d_qk) > lim || local(a.k.stride_s, d_qk) > lim || local(a.v.stride_s, d_v) > lim)
     return ZYFA_ERR_RANGE;
-  a.q_bytes = (unsigned)extent(a.q.stride_s, d_qk);
-  a.k_bytes = (unsigned)extent(a.k.stride_s, d_qk);
-  a.v_bytes = (unsigned)extent(a.v.stride_s, d_v);
 
   hipError_t e;
   if (dtype == ZYFA_DTYPE_BF16)
@@ -244,7 +240,7 @@ const char* zyfa_status_string(int status) {
     case ZYFA_ERR_DESCALE: return "FP8 inputs need q, k and v descale pointers";
     case ZYFA_ERR_CAPTURE: return "the plan for this shape must be built (zyfa_prepare) before graph capture";
     case ZYFA_ERR_HIP: return "a HIP runtime call failed";
-    case ZYFA_ERR_RANGE: return "a (batch, head) slice is too large for 32-bit offsets";
+    case ZYFA_ERR_RANGE: return "the row stride is too large: 64 rows must span at most 2^31 bytes";
     case ZYFA_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case ZYFA_ERR_PMODE: return "unknown FP8 probability mode";
     default: return "unknown status";

@@ -88,6 +88,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   // wave index, each load needs vector address arithmetic and a
   // readfirstlane, and the extra live registers spilled at d_qk = 192).
   const int wq = __builtin_amdgcn_readfirstlane(wave & 3);
+  const int ws = __builtin_amdgcn_readfirstlane(wave);
   const int S = a.seqlen;
   const float sl2 = a.scale_log2;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
@@ -103,7 +104,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
     const char* qbase = (const char*)a.q.ptr + 2 * (b * a.q.stride_b + h * a.q.stride_h);
     const char* kbase = (const char*)a.k.ptr + 2 * (b * a.k.stride_b + hk * a.k.stride_h);
     const char* vbase = (const char*)a.v.ptr + 2 * (b * a.v.stride_b + hk * a.v.stride_h);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, a.q_bytes);
     const int qrs = (int)(2 * a.q.stride_s);
     const int krs = (int)(2 * a.k.stride_s);
     const int vrs = (int)(2 * a.v.stride_s);
@@ -134,9 +134,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       const int row = p / VPITCH, x = ((p % VPITCH) >> 4) ^ ((row & 7) << 1);
       vvo[u] = row * vrs + x * 16;
     }
-    auto tile_rsrc = [&](const char* base, unsigned nbytes, int stride, int kt, int half) {
-      const unsigned off = (unsigned)((kt * kTileK + 32 * half) * stride);
-      return make_rsrc_words(base + off, nbytes > off ? nbytes - off : 0u);
+    // resource at rows 32 half .. of key tile kt
+    auto tile_rsrc = [&](const char* base, int stride, int row_bytes, int kt, int half) {
+      const int r0 = kt * kTileK + 32 * half;
+      return make_rsrc_words(base + (unsigned long long)r0 * (unsigned)stride,
+                             rows_extent(min(S - r0, 32), stride, row_bytes));
     };
 
     const int tA = job.y;
@@ -166,13 +168,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       // whether position j holds a key tile with keys for this wave's rows
       auto has = [&](int j) { return j < n_kt && tile_of(j) <= kt_w; };
 
-      // Q fragments, MFMA B operand: lane (g, n) holds q[row n][32c + 8g .. +7].
+      // Q fragments, MFMA B operand: lane (g, n) holds q[row n][32c + 8g .. +7],
+      // read through a resource based at the wave's first row.
+      const int qr0 = q0 + 32 * ws;
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (unsigned long long)qr0 * (unsigned)qrs,
+                                                  rows_extent(min(S - qr0, 32), qrs, 2 * DQK));
       bf16x8 qf[2][NC];
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          qf[qg][c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (qw0 + 16 * qg + n) * qrs + (32 * c + 8 * g) * 2));
+          qf[qg][c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (16 * qg + n) * qrs + (32 * c + 8 * g) * 2));
 
       f32x4 o[2][8];
       f32x4 lacc[2];
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
           char* base = kring + (j % kSlots) * K_SLOT + hs * (K_SLOT / 2);
-          const i32x4 r = tile_rsrc(kbase, a.k_bytes, krs, tile_of(j), hs);
+          const i32x4 r = tile_rsrc(kbase, krs, 2 * DQK, tile_of(j), hs);
 #pragma unroll
           for (int u = 0; u < KLD; ++u) dma16(r, kvo[u], base + (wq * KLD + u) * 1024);
         }
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
           char* base = vring + (j % kSlots) * V_SLOT + hs * (V_SLOT / 2);
-          const i32x4 r = tile_rsrc(vbase, a.v_bytes, vrs, tile_of(j), hs);
+          const i32x4 r = tile_rsrc(vbase, vrs, 2 * DV, tile_of(j), hs);
 #pragma unroll
           for (int u = 0; u < VLD; ++u) dma16(r, vvo[u], base + (wq * VLD + u) * 1024);
         }

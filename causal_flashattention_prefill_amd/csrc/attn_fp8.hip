@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   // The wave's index within its group, as a scalar, so the load
   // addresses built from it stay in scalar registers.
   const int wsc = __builtin_amdgcn_readfirstlane(wave & 3);
+  const int ws = __builtin_amdgcn_readfirstlane(wave);
   const int S = a.seqlen;
   // Scores in base-2 units: S_codes * (softmax_scale * log2 e * dq * dk).
   const float sl2 = a.scale_log2 * a.q_descale[0] * a.k_descale[0];
@@ -156,7 +157,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
     const char* qbase = (const char*)a.q.ptr + (b * a.q.stride_b + h * a.q.stride_h);
     const char* kbase = (const char*)a.k.ptr + (b * a.k.stride_b + hk * a.k.stride_h);
     const char* vbase = (const char*)a.v.ptr + (b * a.v.stride_b + hk * a.v.stride_h);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, a.q_bytes);
     const int qrs = (int)a.q.stride_s;
     const int krs = (int)a.k.stride_s;
     const int vrs = (int)a.v.stride_s;
@@ -182,12 +182,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // Q fragments (B operand): lane (g, n) holds q[row n][16g..16g+15] and
       // q[row n][64+16g..]; for d 192 also q[row n][128+8g..+7] and
       // q[row n][160+8g..+7], the B operands of two 16x16x32 FP8 MFMAs over
-      // d 128..191.
+      // d 128..191. They are read through a resource based at the wave's
+      // first row.
+      const int qr0 = q0 + 32 * ws;
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (unsigned long long)qr0 * (unsigned)qrs,
+                                                  rows_extent(min(S - qr0, 32), qrs, DQK));
       i32x8 qf[2];
       long qx[2][2];
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg) {
-        const int off = (qw0 + 16 * qg + n) * qrs;
+        const int off = (16 * qg + n) * qrs;
         const u32x4 lo = buf_load16(rq, off + 16 * g);
         const u32x4 hi = buf_load16(rq, off + 64 + 16 * g);
         qf[qg] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -245,15 +249,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         const int row = p >> 6, x = ((p & 63) >> 4) ^ ((row >> 2) & 3);
         kvo[2] = kswap(row) * krs + 128 + x * 16;
       }
-      auto tile_rsrc = [&](const char* base, unsigned nbytes, int stride, int kt, int hs) {
-        const unsigned off = (unsigned)((kt * kTileK + 64 * hs) * stride);
-        return make_rsrc_words(base + off, nbytes > off ? nbytes - off : 0u);
+      // resource at rows 64 hs .. of key tile kt
+      auto tile_rsrc = [&](const char* base, int stride, int row_bytes, int kt, int hs) {
+        const int r0 = kt * kTileK + 64 * hs;
+        return make_rsrc_words(base + (unsigned long long)r0 * (unsigned)stride,
+                               rows_extent(min(S - r0, 64), stride, row_bytes));
       };
       auto issue_k = [&](int kt) {
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
           char* base = kring + (kt % kSlots) * K_SLOT;
-          const i32x4 r = tile_rsrc(kbase, a.k_bytes, krs, kt, hs);
+          const i32x4 r = tile_rsrc(kbase, krs, DQK, kt, hs);
 #pragma unroll
           for (int u = 0; u < 2; ++u) dma16(r, kvo[u], base + hs * (KA_BYTES / 2) + (wsc * 2 + u) * 1024);
           if (D192) dma16(r, kvo[2], base + KA_BYTES + hs * (KB_BYTES / 2) + wsc * 1024);
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
           char* base = vring + (kt % kSlots) * V_SLOT;
-          const i32x4 r = tile_rsrc(vbase, a.v_bytes, vrs, kt, hs);
+          const i32x4 r = tile_rsrc(vbase, vrs, DV, kt, hs);
 #pragma unroll
           for (int u = 0; u < 2; ++u) dma16(r, vvo[u], base + hs * (V_SLOT / 2) + (wsc * 2 + u) * 1024);
         }

@@ -30,6 +30,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, kBufferWord3);
 }
 
+// Extent of a resource based at some row of a slice: `rows` rows of
+// `stride` bytes are readable from it (rows <= 0: none), the last one
+// holding `row_bytes`. Reads of later rows fall outside and return zero,
+// which is how rows past seqlen read as zero padding. The kernels place a
+// resource at every wave's query rows and at every half key tile (a 64-bit
+// base), so rows * stride stays below 2^31 even when a tensor or a slice
+// spans more than 4 GiB.
+__device__ __forceinline__ unsigned rows_extent(int rows, int stride, int row_bytes) {
+  return rows > 0 ? (unsigned)((rows - 1) * stride + row_bytes) : 0u;
+}
+
 // 16-byte load at a byte offset; returns zeros when the offset is past the
 // resource's extent (this is how rows past seqlen read as zero padding).
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {

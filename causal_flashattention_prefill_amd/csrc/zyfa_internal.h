@@ -27,7 +27,6 @@ struct AttnArgs {
   const float* q_descale;     // fp8 only
   const float* k_descale;
   const float* v_descale;
-  unsigned q_bytes, k_bytes, v_bytes;  // extent of one (b, h) slice, bytes from its base
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int d_qk, bool with_lse, int grid, hipStream_t s);

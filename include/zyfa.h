@@ -36,7 +36,8 @@ enum zyfa_status {
   ZYFA_ERR_DESCALE = -7,   /* FP8 call without all three descale pointers */
   ZYFA_ERR_CAPTURE = -8,   /* a per-shape plan must be built while the stream is capturing */
   ZYFA_ERR_HIP = -9,       /* a HIP runtime call failed (launch, allocation, copy) */
-  ZYFA_ERR_RANGE = -10,    /* one (batch, head) slice spans more than 2^31 bytes */
+  ZYFA_ERR_RANGE = -10,    /* 64 rows of one tensor span more than 2^31 bytes (tensors and
+                              slices beyond 4 GiB are fine) */
   ZYFA_ERR_ALIGN = -11,    /* a tensor pointer is not 16-byte aligned */
   ZYFA_ERR_PMODE = -12     /* unknown FP8 probability mode */
 };

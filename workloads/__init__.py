@@ -122,3 +122,16 @@ def generate(w: Workload, seed: Optional[int] = None):
     if w.activation_like:
         activation_like(rng, w, q, k)
     return q, k, v
+
+
+def sampled_heads(seed: int, seqlen: int, heads, d_qk: int, d_v: int):
+    """Draw (q, k, v) for a few heads of a tensor too large to fill on the
+    host: float32 N(0, 1) arrays of shape (len(heads), seqlen, d) each, in
+    head order, q then k then v per head. The other heads of such a tensor
+    are left zero by the caller."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = [[], [], []]
+    for _ in heads:
+        for i, d in enumerate((d_qk, d_qk, d_v)):
+            out[i].append(rng.standard_normal((seqlen, d), dtype=np.float32))
+    return tuple(np.stack(x) for x in out)
