@@ -33,6 +33,17 @@ CASES = {
     "fp8_d128_gqa_s16384": (3, "fp8"),
     "fp8_d192_s16384": (4, "fp8"),
 }
+# Partial-range calls and the LSE merge, on the workload-3 shape (batch 1,
+# 16384 keys, 32 / 8 heads, d 128, bshd): the last 4096 queries as one chunk
+# over the whole prefix (chunked prefill, LSE returned), and the merge of two
+# partial results of all 16384 rows (HBM-bound).
+RANGE_CASES = {
+    "bf16_chunk4096_s16384": "bf16",
+    "fp8_chunk4096_s16384": "fp8",
+}
+CHUNK_Q = 4096
+MERGE_CASE = "merge_bf16_s16384"
+HBM_PEAK_GBS = 8000.0
 HEADLINE = "bf16_d192_s16384"
 DESCRIPTIONS = {
     "bf16_d192_s16384": "causal MLA-prefill form, bf16: batch 1, seqlen 16384, nheads 16 = nheads_k, d_qk 192, "
@@ -43,6 +54,17 @@ DESCRIPTIONS = {
     "fp8_d192_s16384": "causal MLA-prefill form, fp8 e4m3: batch 1, seqlen 16384, nheads 16, d_qk 192, d_v 128, "
                        "bhsd, N(0,1)",
 }
+ALL_CASES = list(CASES) + list(RANGE_CASES) + [MERGE_CASE]
+
+
+def range_flops(B, H, Sq, Sk, delta, dqk, dv):
+    """2 (d_qk + d_v) FLOPs per visible (query, key) pair; key c visible to
+    row r when c <= r + delta. For whole-sequence causal attention this is
+    S (S + 1) (d_qk + d_v) per head, the README's count up to the diagonal."""
+    import numpy as np
+    r = np.arange(Sq, dtype=np.float64)
+    pairs = np.clip(r + delta + 1, 0, Sk).sum()
+    return 2.0 * (dqk + dv) * B * H * pairs
 
 
 def parse():
@@ -52,7 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", default="", help="comma-separated subset of: " + ",".join(CASES))
+    ap.add_argument("--only", default="", help="comma-separated subset of: " + ",".join(ALL_CASES))
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference for HBM byte counters)")
     ap.add_argument("--sustain-seconds", type=float, default=3.0,
@@ -247,6 +269,48 @@ def cpu_baseline(seconds_budget: float):
                       f"bf16 d_qk=192 S=16384 workload, {dt:.1f} s; causal FLOPs of those rows / wall time"}
 
 
+def range_or_merge_case(name, zy, args):
+    """Time one partial-range case (TFLOP/s over visible pairs) or the merge
+    (GB/s of its algorithmic bytes against the HBM peak)."""
+    import torch
+    from workloads import WORKLOADS, generate
+    w = WORKLOADS[3]
+    dev = torch.device("cuda:0")
+    S, H, Hk, d = w.seqlen, w.nheads, w.nheads_k, w.d_qk
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in generate(w))
+    if name == MERGE_CASE:
+        oa = torch.empty((1, S, H, d), dtype=torch.bfloat16, device=dev)
+        la = torch.empty((1, H, S), dtype=torch.float32, device=dev)
+        ob, lb = torch.empty_like(oa), torch.empty_like(la)
+        # two partial results: keys [0, S/2) and [S/2, S)
+        h2 = S // 2
+        zy.zyfa_fwd_range(q, k[:, :h2].contiguous(), v[:, :h2].contiguous(), 0, 0, oa, la)
+        zy.zyfa_fwd_range(q, k[:, h2:].contiguous(), v[:, h2:].contiguous(), 0, h2, ob, lb)
+        out, lse = torch.empty_like(oa), torch.empty_like(la)
+        fn = lambda: zy.zyfa_lse_merge(oa, la, ob, lb, out, lse)
+        ms, _ = time_launches(fn, args.steps, args.warmup)
+        nbytes = 3 * oa.numel() * 2 + 3 * la.numel() * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"gbs": round(gbs, 1), "ms": round(ms, 4), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                "bytes": nbytes, "shape": f"batch 1, seqlen {S}, nheads {H}, d_v {d}, bshd"}
+    dtype = RANGE_CASES[name]
+    Sq = CHUNK_Q
+    qc = q[:, S - Sq:].contiguous()
+    out = torch.empty((1, Sq, H, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, H, Sq), dtype=torch.float32, device=dev)
+    if dtype == "bf16":
+        fn = lambda: zy.zyfa_fwd_range(qc, k, v, S - Sq, 0, out, lse)
+    else:
+        (q8, qs), (k8, ks), (v8, vs) = (zy.zyfa_fp8_quantize(x) for x in (qc, k, v))
+        fn = lambda: zy.zyfa_fwd_range(q8, k8, v8, S - Sq, 0, out, lse, q_descale=qs, k_descale=ks, v_descale=vs)
+    fn()
+    torch.cuda.synchronize()
+    ms, _ = time_launches(fn, args.steps, args.warmup)
+    tf = range_flops(1, H, Sq, S, S - Sq, d, d) / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 2), "ms": round(ms, 4), "pct_of_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
+            "shape": f"{Sq} queries at positions {S - Sq}.. over {S} keys, nheads {H}/{Hk}, d {d}, bshd, LSE"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -259,7 +323,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cases = args.only.split(",") if args.only else list(CASES)
+    cases = args.only.split(",") if args.only else ALL_CASES
     if args.copy_mib:
         # reference for the byte counters: a device-to-device copy of a
         # source that has been written first
@@ -273,6 +337,10 @@ def main():
     res = {}
     sustain = None
     for name in cases:
+        if name in RANGE_CASES or name == MERGE_CASE:
+            res[name] = range_or_merge_case(name, zy, args)
+            torch.cuda.empty_cache()
+            continue
         wid, dtype = CASES[name]
         w = WORKLOADS[wid]
         q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in generate(w))
@@ -298,7 +366,7 @@ def main():
         del q, k, v, out
         torch.cuda.empty_cache()
 
-    head = HEADLINE if HEADLINE in res else cases[0]
+    head = HEADLINE if HEADLINE in res else next(c for c in cases if c in CASES)
     tflops, ms = res[head]["tflops"], res[head]["ms"]
     hdt = CASES[head][1]
     line = {

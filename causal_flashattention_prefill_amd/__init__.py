@@ -57,6 +57,10 @@ def lib() -> ctypes.CDLL:
     L.zyfa_fwd.restype = i
     L.zyfa_fwd_ex.argtypes = fwd_args + [f, i, vp]
     L.zyfa_fwd_ex.restype = i
+    L.zyfa_fwd_range.argtypes = [vp, vp, vp, vp, vp, i, i, i, ll, ll, i, i, i, i, i, i, vp, vp, vp, f, i, vp]
+    L.zyfa_fwd_range.restype = i
+    L.zyfa_lse_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    L.zyfa_lse_merge.restype = i
     L.zyfa_prepare.argtypes = [i, i, i, i, i, i, i, i, i, vp]
     L.zyfa_prepare.restype = i
     L.zyfa_fp8_quantize.argtypes = [vp, i, ll, vp, vp, vp]
@@ -144,6 +148,62 @@ def zyfa_fwd(q, k, v, out=None, lse=None, *, layout: str = "bshd", return_lse: b
                            _stream(stream))
     _check(rc, "zyfa_fwd")
     return (out, lse) if lse is not None else out
+
+
+def zyfa_fwd_range(q, k, v, q_pos0: int, k_pos0: int, out=None, lse=None, *, layout: str = "bshd",
+                   return_lse: bool = True, q_descale=None, k_descale=None, v_descale=None,
+                   softmax_scale: Optional[float] = None, p_mode: str = "default", stream=None):
+    """Causal attention of queries at positions q_pos0 + r over keys at
+    positions k_pos0 + c (key visible when its position <= the query's).
+    k and v may have another seqlen than q. Rows that see no key get out = 0
+    and lse = -inf. Returns (out, lse) (lse allocated unless return_lse is
+    False and none is passed)."""
+    import torch
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    if p_mode not in P_MODES:
+        raise ValueError(f"p_mode must be one of {list(P_MODES)}")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k and v must be contiguous")
+    B, Sq, H, Hk, dqk, dv = _dims(q, k, v, layout)
+    Sk = k.shape[1] if layout == "bshd" else k.shape[2]
+    if out is None:
+        shape = (B, Sq, H, dv) if layout == "bshd" else (B, H, Sq, dv)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    rc = lib().zyfa_fwd_range(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, int(q_pos0), int(k_pos0),
+                              H, Hk, dqk, dv, LAYOUTS[layout], _dtype_code(q), _ptr(q_descale), _ptr(k_descale),
+                              _ptr(v_descale), 0.0 if softmax_scale is None else float(softmax_scale),
+                              P_MODES[p_mode], _stream(stream))
+    _check(rc, "zyfa_fwd_range")
+    return (out, lse) if lse is not None else out
+
+
+def zyfa_lse_merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, *, layout: str = "bshd", stream=None):
+    """Merge two partial results (bf16 out, fp32 lse) of the same query rows
+    over disjoint key sets. out/lse may be out_a/lse_a (in place). Returns
+    (out, lse)."""
+    import torch
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    for t in (out_a, out_b, lse_a, lse_b):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if out_a.shape != out_b.shape or lse_a.shape != lse_b.shape:
+        raise ValueError("the two partial results must have the same shapes")
+    if out_a.dtype != torch.bfloat16 or lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
+        raise TypeError("out must be bf16 and lse fp32")
+    B, H, S = lse_a.shape
+    dv = out_a.shape[-1]
+    if out is None:
+        out = torch.empty_like(out_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    _check(lib().zyfa_lse_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out), _ptr(lse), B, S, H,
+                                dv, LAYOUTS[layout], _stream(stream)), "zyfa_lse_merge")
+    return out, lse
 
 
 def zyfa_prepare(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout="bshd", dtype=DTYPE_BF16, with_lse=False,

@@ -3,6 +3,7 @@
 // step of the path runs in the gfx950 kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <map>
@@ -110,11 +111,15 @@ void strides(int layout, int seqlen, int heads, int dim, long long* sb, long lon
   }
 }
 
+// Whole-sequence attention is the range call with seqlen_q == seqlen_k and
+// q_pos0 == k_pos0.
 int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen,
-             int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale,
-             const float* k_descale, const float* v_descale, float softmax_scale, int p_mode, void* stream_) {
+             int seqlen_k, long long q_pos0, long long k_pos0, int nheads, int nheads_k, int d_qk, int d_v,
+             int layout, int dtype, const float* q_descale, const float* k_descale, const float* v_descale,
+             float softmax_scale, int p_mode, void* stream_) {
   int rc = check_shape(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype);
   if (rc) return rc;
+  if (seqlen_k <= 0) return ZYFA_ERR_SHAPE;
   if (p_mode != ZYFA_P_DEFAULT && p_mode != ZYFA_P_EXACT && p_mode != ZYFA_P_LEAN) return ZYFA_ERR_PMODE;
   if (!q || !k || !v || !out) return ZYFA_ERR_NULL;
   if (dtype == ZYFA_DTYPE_FP8_E4M3FN && (!q_descale || !k_descale || !v_descale)) return ZYFA_ERR_DESCALE;
@@ -135,13 +140,20 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   a.k.ptr = k;
   a.v.ptr = v;
   strides(layout, seqlen, nheads, d_qk, &a.q.stride_b, &a.q.stride_h, &a.q.stride_s);
-  strides(layout, seqlen, nheads_k, d_qk, &a.k.stride_b, &a.k.stride_h, &a.k.stride_s);
-  strides(layout, seqlen, nheads_k, d_v, &a.v.stride_b, &a.v.stride_h, &a.v.stride_s);
+  strides(layout, seqlen_k, nheads_k, d_qk, &a.k.stride_b, &a.k.stride_h, &a.k.stride_s);
+  strides(layout, seqlen_k, nheads_k, d_v, &a.v.stride_b, &a.v.stride_h, &a.v.stride_s);
   strides(layout, seqlen, nheads, d_v, &a.o_stride_b, &a.o_stride_h, &a.o_stride_s);
   a.out = out;
   a.lse = lse;
   a.batch = batch;
-  a.seqlen = seqlen;
+  a.seqlen_q = seqlen;
+  a.seqlen_k = seqlen_k;
+  // key c is visible to query row r when c <= r + delta. Offsets past
+  // seqlen_k (every key visible) or below -(seqlen_q + 512) (none visible)
+  // act alike, so delta is clamped there and the kernels' index sums stay
+  // far inside int.
+  const long long dl = q_pos0 - k_pos0;
+  a.delta = (int)std::max(-(long long)seqlen - 512, std::min(dl, (long long)seqlen_k));
   a.nheads = nheads;
   a.nheads_k = nheads_k;
   a.n_qtiles = plan->n_qtiles;
@@ -181,15 +193,37 @@ extern "C" {
 int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen, int nheads,
              int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale, const float* k_descale,
              const float* v_descale, void* stream) {
-  return fwd_impl(q, k, v, out, lse, batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype, q_descale, k_descale,
-                  v_descale, 0.f, ZYFA_P_DEFAULT, stream);
+  return fwd_impl(q, k, v, out, lse, batch, seqlen, seqlen, 0, 0, nheads, nheads_k, d_qk, d_v, layout, dtype,
+                  q_descale, k_descale, v_descale, 0.f, ZYFA_P_DEFAULT, stream);
 }
 
 int zyfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen,
                 int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale,
                 const float* k_descale, const float* v_descale, float softmax_scale, int p_mode, void* stream) {
-  return fwd_impl(q, k, v, out, lse, batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype, q_descale, k_descale,
-                  v_descale, softmax_scale, p_mode, stream);
+  return fwd_impl(q, k, v, out, lse, batch, seqlen, seqlen, 0, 0, nheads, nheads_k, d_qk, d_v, layout, dtype,
+                  q_descale, k_descale, v_descale, softmax_scale, p_mode, stream);
+}
+
+int zyfa_fwd_range(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen_q,
+                   int seqlen_k, long long q_pos0, long long k_pos0, int nheads, int nheads_k, int d_qk, int d_v,
+                   int layout, int dtype, const float* q_descale, const float* k_descale, const float* v_descale,
+                   float softmax_scale, int p_mode, void* stream) {
+  return fwd_impl(q, k, v, out, lse, batch, seqlen_q, seqlen_k, q_pos0, k_pos0, nheads, nheads_k, d_qk, d_v, layout,
+                  dtype, q_descale, k_descale, v_descale, softmax_scale, p_mode, stream);
+}
+
+int zyfa_lse_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,
+                   float* lse, int batch, int seqlen, int nheads, int d_v, int layout, void* stream) {
+  if (batch <= 0 || seqlen <= 0 || nheads <= 0) return ZYFA_ERR_SHAPE;
+  if (d_v != 128) return ZYFA_ERR_HEADDIM;
+  if (layout != ZYFA_LAYOUT_BSHD && layout != ZYFA_LAYOUT_BHSD) return ZYFA_ERR_LAYOUT;
+  if (!out_a || !lse_a || !out_b || !lse_b || !out || !lse) return ZYFA_ERR_NULL;
+  if (!aligned16(out_a) || !aligned16(out_b) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lse_a) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse_b) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return ZYFA_ERR_ALIGN;
+  const hipError_t e = launch_lse_merge(out_a, lse_a, out_b, lse_b, out, lse, batch, seqlen, nheads, d_v,
+                                        layout == ZYFA_LAYOUT_BSHD, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
 }
 
 int zyfa_prepare(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype,

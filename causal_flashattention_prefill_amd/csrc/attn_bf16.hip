@@ -1,8 +1,13 @@
 // Causal forward attention, BF16 inputs, for gfx950 (CDNA4).
 //
 // What is computed: "ZYFA" README, Usage and Supported configurations
-// (causal, seqlen_q == seqlen_k, GQA head sharing, natural-log LSE, BF16
-// output, zero padding to the query-tile multiple).
+// (causal, GQA head sharing, natural-log LSE, BF16 output, zero padding to
+// the query-tile multiple). Query row r sits at position r + delta relative
+// to the keys (key c is visible to row r when c <= r + delta): delta = 0
+// with seqlen_q == seqlen_k is whole-sequence causal attention; other
+// values give the partial results over a range of keys that the README's
+// Accuracy note and the RDNA3 page's split-and-merge combine through the
+// LSE. Rows that see no key get O = 0 and LSE = -inf.
 //
 // Structure (one workgroup = 8 waves = 512 threads, persistent):
 //  - A job is a pair of 256-row query tiles (i, n-1-i) of one (batch, head)
@@ -47,6 +52,7 @@ constexpr int kTileK = 64;
 constexpr int kSlots = 4;              // K and V ring depth
 constexpr float kTau = 8.0f;           // lazy-rescale threshold, log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRefFloor = -1e30f;      // initial reference maximum, base-2 units
 
 template <int DQK, bool WITH_LSE>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnArgs a) {
@@ -89,7 +95,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   // readfirstlane, and the extra live registers spilled at d_qk = 192).
   const int wq = __builtin_amdgcn_readfirstlane(wave & 3);
   const int ws = __builtin_amdgcn_readfirstlane(wave);
-  const int S = a.seqlen;
+  const int Sq = a.seqlen_q;
+  const int Sk = a.seqlen_k;
+  const int dl = a.delta;
   const float sl2 = a.scale_log2;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
     auto tile_rsrc = [&](const char* base, int stride, int row_bytes, int kt, int half) {
       const int r0 = kt * kTileK + 32 * half;
       return make_rsrc_words(base + (unsigned long long)r0 * (unsigned)stride,
-                             rows_extent(min(S - r0, 32), stride, row_bytes));
+                             rows_extent(min(Sk - r0, 32), stride, row_bytes));
     };
 
     const int tA = job.y;
@@ -150,11 +158,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       const int qt = tt == 0 ? tB : tA;
       const int q0 = qt * kTileQ;
       const int qw0 = q0 + wave * 32;
-      const int qend = min(q0 + kTileQ, S);
-      const int n_kt = (qend - 1) / kTileK + 1;
+      const int qend = min(q0 + kTileQ, Sq);
+      // key tiles that some row of the query tile sees (when any: the
+      // tile's last row sees qend + delta keys, capped at seqlen_k)
+      const bool any_key = qend + dl > 0;
+      const int n_kt = (min(Sk, qend + dl) - 1) / kTileK + 1;
       // this wave's last key tile (the one holding its diagonal), -1 if the
-      // wave has no rows
-      const int kt_w = (qw0 < S) ? min((qw0 + 31) / kTileK, n_kt - 1) : -1;
+      // wave has no rows or its rows see no key
+      const int lk_w = min(Sk - 1, qw0 + 31 + dl);
+      const int kt_w = (qw0 < Sq && lk_w >= 0) ? min(lk_w / kTileK, n_kt - 1) : -1;
 
       // Key tiles are visited in ascending order for the first (longer)
       // query tile of the pair and in descending order for the second. A
@@ -172,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       // read through a resource based at the wave's first row.
       const int qr0 = q0 + 32 * ws;
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (unsigned long long)qr0 * (unsigned)qrs,
-                                                  rows_extent(min(S - qr0, 32), qrs, 2 * DQK));
+                                                  rows_extent(min(Sq - qr0, 32), qrs, 2 * DQK));
       bf16x8 qf[2][NC];
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg)
@@ -188,7 +200,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      float mref[2] = {neg_inf(), neg_inf()};
+      // Reference maxima start at a finite floor, so rows that have seen no
+      // key yet give exp2(-inf - m) = 0 and rescale factors of 1, never NaN.
+      float mref[2] = {kRefFloor, kRefFloor};
       // lazy-rescale threshold in raw score units, (m + tau) / sl2
       float thr[2] = {neg_inf(), neg_inf()};
       float lsum[2] = {0.f, 0.f};
@@ -297,12 +311,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
         if (!has(j)) return;
         const int kt0 = tile_of(j) * kTileK;
         // ---- causal mask, on diagonal tiles only; score (kb, i) of lane
-        // group g is key 16 kb + 4 g + i of the tile
-        if (__builtin_expect(kt0 + kTileK - 1 > qw0, 0)) {
+        // group g is key 16 kb + 4 g + i of the tile. Row r sees keys up to
+        // min(r + delta, seqlen_k - 1): the cap masks the zero rows past the
+        // last key when every key is visible.
+        if (__builtin_expect(kt0 + kTileK - 1 > min(qw0 + dl, Sk - 1), 0)) {
           const float ninf = neg_inf();
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) {
-            const int q = qw0 + 16 * qg + n - kt0 - 4 * g;
+            const int q = min(qw0 + 16 * qg + n + dl, Sk - 1) - kt0 - 4 * g;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -375,37 +391,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       // no loads: it carries the longer chain of the interval (its softmax
       // and then its matrix cluster, while the lag group's softmax runs
       // beside that matrix cluster), and a wave that issues direct-to-LDS
-      // loads is held until the address unit has accepted them. The last position with work for the lag group
-      // is n_kt - 1 in descending order and its last key tile in ascending
-      // order; its PV runs two intervals later.
-      const int lag_last = rev ? n_kt - 1 : min((q0 + 127) / kTileK, n_kt - 1);
+      // loads is held until the address unit has accepted them. The last
+      // position with work for the lag group is n_kt - 1 in descending order
+      // and its last key tile in ascending order; its PV runs two intervals
+      // later. A query tile whose rows see no key skips the loop.
+      const int lag_last = rev ? n_kt - 1 : (q0 + 127 + dl >= 0 ? min((q0 + 127 + dl) / kTileK, n_kt - 1) : -1);
       const int n_int = max(n_kt + 1, lag_last + 3);
       __syncthreads();   // the previous query tile's last reads of the rings are done
-      if (!lead) {
-        issue_k(0);
-        if (n_kt > 1) issue_k(1);
-        issue_v(0);
-      }
-      wait_vm<0>();
-      __syncthreads();
-      for (int i = 0; i < n_int; ++i) {
-        if (lead) {
-          if (i >= 1) vector_cluster(i - 1);
-          matrix_cluster(i);
-        } else {
-          if (i >= 1) matrix_cluster(i - 1);
-          if (i + 2 < n_kt) issue_k(i + 2);
-          if (i + 1 < n_kt) issue_v(i + 1);
-          if (i >= 1) vector_cluster(i - 1);
-          if (i + 2 < n_kt) wait_vm<2 * (KLD + VLD)>();
-          else if (i + 1 < n_kt) wait_vm<2 * VLD>();
-          else wait_vm<0>();
+      if (any_key) {
+        if (!lead) {
+          issue_k(0);
+          if (n_kt > 1) issue_k(1);
+          issue_v(0);
         }
+        wait_vm<0>();
         __syncthreads();
+        for (int i = 0; i < n_int; ++i) {
+          if (lead) {
+            if (i >= 1) vector_cluster(i - 1);
+            matrix_cluster(i);
+          } else {
+            if (i >= 1) matrix_cluster(i - 1);
+            if (i + 2 < n_kt) issue_k(i + 2);
+            if (i + 1 < n_kt) issue_v(i + 1);
+            if (i >= 1) vector_cluster(i - 1);
+            if (i + 2 < n_kt) wait_vm<2 * (KLD + VLD)>();
+            else if (i + 1 < n_kt) wait_vm<2 * VLD>();
+            else wait_vm<0>();
+          }
+          __syncthreads();
+        }
       }
 
-      // ---- epilogue: O / l (RNE to bf16), LSE = ln2 * (m + log2 l)
-      if (kt_w >= 0) {
+      // ---- epilogue: O / l (RNE to bf16), LSE = ln2 * (m + log2 l); rows
+      // that saw no key (l = 0) get O = 0 and LSE = -inf
+      if (qw0 < Sq) {
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
           float lt;
@@ -415,9 +435,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
           } else {
             lt = lacc[qg][0];
           }
-          const float inv = 1.0f / lt;
+          const float inv = lt > 0.f ? 1.0f / lt : 0.f;
           const int q = qw0 + 16 * qg + n;
-          if (q < S) {
+          if (q < Sq) {
             __bf16* orow = (__bf16*)a.out + (b * a.o_stride_b + h * a.o_stride_h + (long long)q * a.o_stride_s);
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
@@ -426,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
               *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g) = w;
             }
             if (WITH_LSE && g == 0)
-              a.lse[((long long)b * a.nheads + h) * S + q] = (mref[qg] + fast_log2(lt)) * kLn2;
+              a.lse[((long long)b * a.nheads + h) * Sq + q] = (mref[qg] + fast_log2(lt)) * kLn2;
           }
         }
       }

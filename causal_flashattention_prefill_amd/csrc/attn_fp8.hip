@@ -4,7 +4,12 @@
 // What is computed: "ZYFA" README, Usage (descales read from device memory
 // and applied by the kernel), Supported configurations, Accuracy (the output
 // is divided by the sum of the same rounded probabilities that multiply V,
-// and the LSE comes from those rounded probabilities).
+// and the LSE comes from those rounded probabilities, so that results over
+// different key ranges merge consistently). Query row r sits at position
+// r + delta relative to the keys (key c is visible to row r when
+// c <= r + delta): delta = 0 with seqlen_q == seqlen_k is whole-sequence
+// causal attention, other values give partial results over a key range.
+// Rows that see no key get O = 0 and LSE = -inf.
 //
 // Structure (shared with the BF16 kernel: persistent 8-wave workgroups, jobs
 // = pairs of 256-row query tiles, 32 query rows per wave, transposed scores):
@@ -67,6 +72,7 @@ constexpr int kTileK = 128;
 constexpr int kSlots = 4;             // K and V ring depth
 constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRefFloor = -1e30f;      // initial reference maximum, base-2 units
 constexpr int kE8M0One = 127;           // E8M0 scale 2^0
 // Lean-P constant 56 + 8 log2(2 ln(2)^2).
 constexpr float kLeanC = 55.539734f;
@@ -137,7 +143,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   // addresses built from it stay in scalar registers.
   const int wsc = __builtin_amdgcn_readfirstlane(wave & 3);
   const int ws = __builtin_amdgcn_readfirstlane(wave);
-  const int S = a.seqlen;
+  const int Sq = a.seqlen_q;
+  const int Sk = a.seqlen_k;
+  const int dl = a.delta;
   // Scores in base-2 units: S_codes * (softmax_scale * log2 e * dq * dk).
   const float sl2 = a.scale_log2 * a.q_descale[0] * a.k_descale[0];
   const float c8s = 8.0f * sl2 * kInv65535;
@@ -170,14 +178,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       const int qt = tt == 0 ? tB : tA;
       const int q0 = qt * kTileQ;
       const int qw0 = q0 + wave * 32;
-      const int qend = min(q0 + kTileQ, S);
-      const int n_kt = (qend - 1) / kTileK + 1;
+      const int qend = min(q0 + kTileQ, Sq);
+      // key tiles that some row of the query tile sees (when any: the
+      // tile's last row sees qend + delta keys, capped at seqlen_k)
+      const bool any_key = qend + dl > 0;
+      const int n_kt = (min(Sk, qend + dl) - 1) / kTileK + 1;
       // this wave's last key tile (the one holding its diagonal), -1 if the
-      // wave has no rows
-      const int kt_w = (qw0 < S) ? min((qw0 + 31) / kTileK, n_kt - 1) : -1;
-      // key tiles from K0 on overlap this query tile: exact P and (on the
-      // diagonal) the causal mask; tiles before K0 take lean P (with LEAN)
-      const int K0 = q0 / kTileK;
+      // wave has no rows or its rows see no key
+      const int lk_w = min(Sk - 1, qw0 + 31 + dl);
+      const int kt_w = (qw0 < Sq && lk_w >= 0) ? min(lk_w / kTileK, n_kt - 1) : -1;
+      // key tiles from K0 on reach the diagonal band of this query tile:
+      // exact P and (on the diagonal) the causal mask; tiles before K0, whose
+      // keys every row of the tile sees, take lean P (with LEAN)
+      const int K0 = q0 + dl + 1 > 0 ? (q0 + dl + 1) / kTileK : 0;
 
       // Q fragments (B operand): lane (g, n) holds q[row n][16g..16g+15] and
       // q[row n][64+16g..]; for d 192 also q[row n][128+8g..+7] and
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // first row.
       const int qr0 = q0 + 32 * ws;
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (unsigned long long)qr0 * (unsigned)qrs,
-                                                  rows_extent(min(S - qr0, 32), qrs, DQK));
+                                                  rows_extent(min(Sq - qr0, 32), qrs, DQK));
       i32x8 qf[2];
       long qx[2][2];
 #pragma unroll
@@ -209,7 +222,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      float mref[2] = {neg_inf(), neg_inf()};
+      // Reference maxima start at a finite floor, so rows that have seen no
+      // key yet give exp2(-inf - m) = 0 and rescale factors of 1, never NaN.
+      float mref[2] = {kRefFloor, kRefFloor};
       // lazy-rescale threshold in raw score units, (m + tau) / sl2, and the
       // lean-P offset (C - 8 m) / 65535 of each query group
       float thr[2] = {neg_inf(), neg_inf()};
@@ -253,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       auto tile_rsrc = [&](const char* base, int stride, int row_bytes, int kt, int hs) {
         const int r0 = kt * kTileK + 64 * hs;
         return make_rsrc_words(base + (unsigned long long)r0 * (unsigned)stride,
-                               rows_extent(min(S - r0, 64), stride, row_bytes));
+                               rows_extent(min(Sk - r0, 64), stride, row_bytes));
       };
       auto issue_k = [&](int kt) {
 #pragma unroll
@@ -378,12 +393,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         if (t > kt_w) return;
         const int kt0 = t * kTileK;
         // ---- causal mask, on the diagonal tile only; score (kb, i) of lane
-        // group g is key 64 (kb / 4) + 16 g + 4 (kb % 4) + i of the tile
-        if (__builtin_expect(kt0 + kTileK - 1 > qw0, 0)) {
+        // group g is key 64 (kb / 4) + 16 g + 4 (kb % 4) + i of the tile. Row r
+        // sees keys up to min(r + delta, seqlen_k - 1): the cap masks the zero
+        // rows past the last key when every key is visible.
+        if (__builtin_expect(kt0 + kTileK - 1 > min(qw0 + dl, Sk - 1), 0)) {
           const float ninf = neg_inf();
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) {
-            const int q = qw0 + 16 * qg + n - kt0 - 16 * g;
+            const int q = min(qw0 + 16 * qg + n + dl, Sk - 1) - kt0 - 16 * g;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
@@ -491,40 +508,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // an interval the loads queue in the address unit and stall every
       // wave.) The lag group's last tile (its PV) ends in interval
       // kt_w + 2, the lead's in kt_w + 1.
-      const int lag_last = min(K0, n_kt - 1);
+      const int lag_last = q0 + 127 + dl >= 0 ? min((q0 + 127 + dl) / kTileK, n_kt - 1) : -1;
       const int n_int = max(n_kt + 1, lag_last + 3);
       __syncthreads();   // the previous query tile's last reads of the rings are done
-      if (!lead) {
-        issue_k(0);
-        if (n_kt > 1) issue_k(1);
-        issue_v(0);
-      }
-      wait_vm<0>();
-      __syncthreads();
-      for (int i = 0; i < n_int; ++i) {
-        if (lead) {
-          if (i >= 1) vector_cluster(i - 1);
-          matrix_cluster(i);
-        } else {
-          if (i >= 1) matrix_cluster(i - 1);
-          if (i + 2 < n_kt) issue_k(i + 2);
-          if (i + 1 < n_kt) issue_v(i + 1);
-          if (i >= 1) vector_cluster(i - 1);
-          if (i + 2 < n_kt) wait_vm<D192 ? 10 : 8>();
-          else if (i + 1 < n_kt) wait_vm<4>();
-          else wait_vm<0>();
+      if (any_key) {     // a query tile whose rows see no key skips the loop
+        if (!lead) {
+          issue_k(0);
+          if (n_kt > 1) issue_k(1);
+          issue_v(0);
         }
+        wait_vm<0>();
         __syncthreads();
+        for (int i = 0; i < n_int; ++i) {
+          if (lead) {
+            if (i >= 1) vector_cluster(i - 1);
+            matrix_cluster(i);
+          } else {
+            if (i >= 1) matrix_cluster(i - 1);
+            if (i + 2 < n_kt) issue_k(i + 2);
+            if (i + 1 < n_kt) issue_v(i + 1);
+            if (i >= 1) vector_cluster(i - 1);
+            if (i + 2 < n_kt) wait_vm<D192 ? 10 : 8>();
+            else if (i + 1 < n_kt) wait_vm<4>();
+            else wait_vm<0>();
+          }
+          __syncthreads();
+        }
       }
 
       // ---- epilogue: O * dv / l (RNE to bf16), LSE = ln2 * (m + log2 l)
-      if (kt_w >= 0) {
+      if (qw0 < Sq) {
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
           const float lt = lacc[qg][0];
-          const float f = dvs / lt;
+          const float f = lt > 0.f ? dvs / lt : 0.f;   // l = 0: the row saw no key
           const int q = qw0 + 16 * qg + n;
-          if (q < S) {
+          if (q < Sq) {
             __bf16* orow = (__bf16*)a.out + (b * a.o_stride_b + h * a.o_stride_h + (long long)q * a.o_stride_s);
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
@@ -533,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
               *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g) = w;
             }
             if (WITH_LSE && g == 0)
-              a.lse[((long long)b * a.nheads + h) * S + q] = (mref[qg] + fast_log2(lt)) * kLn2;
+              a.lse[((long long)b * a.nheads + h) * Sq + q] = (mref[qg] + fast_log2(lt)) * kLn2;
           }
         }
       }

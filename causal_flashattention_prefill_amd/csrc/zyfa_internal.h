@@ -18,7 +18,9 @@ struct AttnArgs {
   void* out;
   long long o_stride_b, o_stride_h, o_stride_s;
   float* lse;                 // may be null
-  int batch, seqlen, nheads, nheads_k;
+  int batch, nheads, nheads_k;
+  int seqlen_q, seqlen_k;     // query rows and keys per (batch, head)
+  int delta;                  // key c is visible to query row r when c <= r + delta
   int n_qtiles;               // query tiles per (batch, head)
   int jobs_per_wg;
   int num_wgs;                // workgroups of the launch (the job table's row length)
@@ -34,5 +36,7 @@ hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean
 hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
                                unsigned* scratch_amax, int scratch_slots, hipStream_t s);
 int quantize_scratch_slots();
+hipError_t launch_lse_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,
+                            float* lse, int batch, int seqlen, int nheads, int d_v, bool bshd, hipStream_t s);
 
 }  // namespace zyfa

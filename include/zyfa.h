@@ -117,6 +117,52 @@ int zyfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
                 float softmax_scale, int p_mode, void* stream);
 
 /*
+ * zyfa_fwd_range - causal attention of a block of queries over a range of
+ * keys, returning the partial output and its LSE so that results over
+ * different key ranges can be merged ("ZYFA" README, Accuracy: the LSE
+ * comes from the same rounded probabilities "so that results computed over
+ * different key ranges can be merged consistently"; the flash-attention
+ * RDNA3 page's split of the keys with an LSE merge). Uses: chunked prefill
+ * (a chunk of new queries over the cached prefix and itself) and a sequence
+ * split over devices.
+ *  Query row r sits at absolute position q_pos0 + r, key c at k_pos0 + c;
+ *  key c is visible to row r when k_pos0 + c <= q_pos0 + r.
+ *  q       [batch, seqlen_q, nheads, d_qk] (bshd) or [batch, nheads, seqlen_q,
+ *          d_qk] (bhsd); k and v the same with seqlen_k and nheads_k.
+ *  out     q's layout with head dim d_v, bf16. lse: fp32 [batch, nheads,
+ *          seqlen_q], natural log, or NULL.
+ *  A row that sees no key gets out = 0 and lse = -inf (the merge's
+ *  identity). q_pos0 == k_pos0 with seqlen_q == seqlen_k is zyfa_fwd_ex.
+ *  Every other argument, the errors and the plan (keyed by seqlen_q: pass
+ *  seqlen = seqlen_q to zyfa_prepare) are those of zyfa_fwd_ex;
+ *  seqlen_k <= 0 returns ZYFA_ERR_SHAPE.
+ */
+int zyfa_fwd_range(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int batch, int seqlen_q, int seqlen_k, long long q_pos0, long long k_pos0,
+                   int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype,
+                   const float* q_descale, const float* k_descale, const float* v_descale,
+                   float softmax_scale, int p_mode, void* stream);
+
+/*
+ * zyfa_lse_merge - merge two partial results of the same query rows over
+ * disjoint key sets (as zyfa_fwd_range returns them) into the result over
+ * both. Per row, with L_a, L_b the partial LSEs:
+ *   L = ln(e^L_a + e^L_b),  out = e^(L_a - L) out_a + e^(L_b - L) out_b
+ * and L = -inf, out = 0 when both are -inf. Arithmetic in fp32, out rounded
+ * to bf16 (RNE).
+ *  out_a, out_b, out  bf16, [batch, seqlen, nheads, d_v] (bshd) or
+ *                     [batch, nheads, seqlen, d_v] (bhsd), 16-byte aligned;
+ *  lse_a, lse_b, lse  fp32 [batch, nheads, seqlen].
+ *  out may be out_a or out_b and lse may be lse_a or lse_b (merging in
+ *  place); other overlaps are undefined. d_v must be 128
+ *  (ZYFA_ERR_HEADDIM otherwise). Asynchronous on `stream`; allocates
+ *  nothing.
+ */
+int zyfa_lse_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b,
+                   void* out, float* lse, int batch, int seqlen, int nheads, int d_v, int layout,
+                   void* stream);
+
+/*
  * zyfa_prepare - build (or find) the per-shape plan ahead of time so that a
  * later zyfa_fwd with the same shape allocates nothing and copies nothing
  * from the host (README, Usage: run each new shape once before capturing).

@@ -133,3 +133,22 @@ def check_fp8_rounding(out, ref_out, lse, ref_lse, what=""):
     if lse is not None:
         assert np.all(np.isfinite(lse)), what + ": non-finite lse"
         assert dl.max() <= FP8_ROUND_LSE_MAX and dl.mean() <= FP8_ROUND_LSE_MEAN, stats
+
+
+def check_partial(out, ref_out, lse, ref_lse, what="", fp8=False):
+    """Partial results over a key range: rows that see no key (oracle LSE
+    -inf) must come back as out = 0 exactly and LSE = -inf; the others are
+    held to the BF16 (or FP8) gate. out: (..., d) with lse shaped like its
+    leading axes."""
+    empty = np.isneginf(ref_lse)
+    if lse is not None:
+        assert np.array_equal(np.isneginf(lse), empty), f"{what}: -inf LSE rows differ"
+    assert np.all(out[empty] == 0.0), f"{what}: rows that see no key are not zero"
+    live = ~empty
+    if not live.any():
+        return
+    if fp8:
+        check_fp8(out[live], ref_out[live], what)
+    else:
+        check_bf16(out[live], ref_out[live], None if lse is None else lse[live], None if lse is None else ref_lse[live],
+                   what)

@@ -120,3 +120,37 @@ def test_job_table_xcd_locality():
         for x in range(8):
             heads = {int(table[r, w, 0]) for w in range(x, nw, 8)}
             assert len(heads) <= 2
+
+
+def _range(**kw):
+    a = dict(q=16, k=16, v=16, out=16, lse=None, B=1, Sq=128, Sk=300, qp=172, kp=0, H=4, Hk=2, dqk=128, dv=128,
+             layout=0, dtype=0, qd=None, kd=None, vd=None, scale=0.0, p_mode=0, stream=None)
+    a.update(kw)
+    return zy.lib().zyfa_fwd_range(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Sq"], a["Sk"], a["qp"],
+                                   a["kp"], a["H"], a["Hk"], a["dqk"], a["dv"], a["layout"], a["dtype"], a["qd"],
+                                   a["kd"], a["vd"], a["scale"], a["p_mode"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Sk=0), "ZYFA_ERR_SHAPE"), (dict(Sq=0), "ZYFA_ERR_SHAPE"), (dict(dqk=64, dv=64), "ZYFA_ERR_HEADDIM"),
+    (dict(H=6, Hk=4), "ZYFA_ERR_GQA"), (dict(layout=2), "ZYFA_ERR_LAYOUT"), (dict(v=None), "ZYFA_ERR_NULL"),
+    (dict(dtype=1), "ZYFA_ERR_DESCALE"), (dict(out=8), "ZYFA_ERR_ALIGN"), (dict(p_mode=5), "ZYFA_ERR_PMODE"),
+])
+def test_fwd_range_argument_errors(kw, status):
+    assert _range(**kw) == zy.STATUS[status]
+
+
+def _merge(**kw):
+    a = dict(oa=16, la=16, ob=16, lb=16, out=16, lse=16, B=1, S=100, H=4, dv=128, layout=0, stream=None)
+    a.update(kw)
+    return zy.lib().zyfa_lse_merge(a["oa"], a["la"], a["ob"], a["lb"], a["out"], a["lse"], a["B"], a["S"], a["H"],
+                                   a["dv"], a["layout"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), "ZYFA_ERR_SHAPE"), (dict(S=-3), "ZYFA_ERR_SHAPE"), (dict(dv=192), "ZYFA_ERR_HEADDIM"),
+    (dict(layout=4), "ZYFA_ERR_LAYOUT"), (dict(lb=None), "ZYFA_ERR_NULL"), (dict(lse=None), "ZYFA_ERR_NULL"),
+    (dict(ob=24), "ZYFA_ERR_ALIGN"), (dict(la=18), "ZYFA_ERR_ALIGN"),
+])
+def test_lse_merge_argument_errors(kw, status):
+    assert _merge(**kw) == zy.STATUS[status]
