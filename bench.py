@@ -366,7 +366,12 @@ def main():
         del q, k, v, out
         torch.cuda.empty_cache()
 
-    head = HEADLINE if HEADLINE in res else next(c for c in cases if c in CASES)
+    attn = [c for c in cases if c in CASES]
+    if not attn:
+        # only partial-range or merge cases were asked for (profiling runs)
+        print(json.dumps({"cases": res}), flush=True)
+        return
+    head = HEADLINE if HEADLINE in res else attn[0]
     tflops, ms = res[head]["tflops"], res[head]["ms"]
     hdt = CASES[head][1]
     line = {
