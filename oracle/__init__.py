@@ -17,6 +17,8 @@ Sources (cited by page title and section):
 - flash-attention RDNA3 extension page, kernel notes (partial results over
   key splits merged by an LSE reduction), with the README's Accuracy note on
   merging results over key ranges: partial.py.
+- "ZYFA" README, "Using FP8 attention in a model" (Hadamard rotation of q
+  and k before quantization): rotation.py.
 
 Parity pins for every function live in tests/test_oracle_*.py and
 tests/golden/. No function here is "parity unpinned".
@@ -27,10 +29,12 @@ from .quantize import fp8_quantize_ref
 from .attention import causal_attention_ref, causal_probs_ref, causal_attention_rows_ref
 from .fp8_p import fp8_attention_rows_ref
 from .partial import range_attention_ref, range_attention_rows_ref, lse_merge_ref, lse_merge_layout_ref
+from .rotation import hadamard, dct2_ortho, rotation_matrix, rotate_ref, quantize_rotated_ref
 
 __all__ = [
     "bf16_round", "bf16_decode", "bf16_encode_bits", "e4m3fn_decode", "e4m3fn_encode",
     "E4M3FN_MAX", "fp8_quantize_ref", "causal_attention_ref", "causal_probs_ref",
     "causal_attention_rows_ref", "fp8_attention_rows_ref", "range_attention_ref",
-    "range_attention_rows_ref", "lse_merge_ref", "lse_merge_layout_ref",
+    "range_attention_rows_ref", "lse_merge_ref", "lse_merge_layout_ref", "hadamard", "dct2_ortho",
+    "rotation_matrix", "rotate_ref", "quantize_rotated_ref",
 ]

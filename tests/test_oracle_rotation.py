@@ -1,0 +1,75 @@
+"""Pins of the rotation oracle (oracle/rotation.py): closed forms, a library
+DCT, orthogonality and the invariance the README states."""
+import numpy as np
+import pytest
+from scipy.fft import dct
+
+import oracle
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 64, 128, 256])
+def test_hadamard_closed_form(n):
+    # Sylvester's matrix has entry (-1)^popcount(i & j)
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    assert np.array_equal(oracle.hadamard(n), (-1.0) ** pc)
+
+
+def test_dct_matches_scipy():
+    # scipy's orthonormal DCT-II of the unit vectors gives the matrix column by column
+    np.testing.assert_allclose(oracle.dct2_ortho(3), dct(np.eye(3), type=2, norm="ortho", axis=0), atol=1e-15)
+    c = oracle.dct2_ortho(3)
+    np.testing.assert_allclose(c[0], [3 ** -0.5] * 3, atol=1e-15)
+    np.testing.assert_allclose(c[1], [2 ** -0.5, 0.0, -(2 ** -0.5)], atol=1e-15)
+    np.testing.assert_allclose(c[2], [6 ** -0.5, -2 * 6 ** -0.5, 6 ** -0.5], atol=1e-15)
+
+
+@pytest.mark.parametrize("d", [128, 192])
+def test_rotation_is_orthogonal_and_keeps_scores(d):
+    rng = np.random.default_rng(d)
+    s = rng.choice([-1.0, 1.0], d)
+    r = oracle.rotation_matrix(d, s)
+    np.testing.assert_allclose(r @ r.T, np.eye(d), atol=1e-14)
+    q, k = rng.standard_normal((7, d)), rng.standard_normal((9, d))
+    np.testing.assert_allclose(oracle.rotate_ref(q, s) @ oracle.rotate_ref(k, s).T, q @ k.T, atol=1e-12)
+
+
+def test_d128_spreads_a_channel_evenly():
+    rng = np.random.default_rng(1)
+    s = rng.choice([-1.0, 1.0], 128)
+    for i in (0, 5, 127):
+        y = oracle.rotate_ref(np.eye(128)[i], s)
+        pc = np.array([bin(i & j).count("1") for j in range(128)])
+        np.testing.assert_allclose(y, s[i] * (-1.0) ** pc / np.sqrt(128), atol=1e-15)
+
+
+def test_d192_block_structure():
+    rng = np.random.default_rng(2)
+    s = rng.choice([-1.0, 1.0], 192)
+    c = oracle.dct2_ortho(3)
+    h = oracle.hadamard(64)
+    for a, b in ((0, 0), (1, 17), (2, 63)):
+        y = oracle.rotate_ref(np.eye(192)[64 * a + b], s).reshape(3, 64)
+        want = s[64 * a + b] * c[:, a][:, None] * h[b][None, :] / 8.0
+        np.testing.assert_allclose(y, want, atol=1e-15)
+
+
+def test_signs_must_be_plus_minus_one():
+    with pytest.raises(ValueError):
+        oracle.rotation_matrix(128, np.zeros(128))
+    with pytest.raises(ValueError):
+        oracle.rotation_matrix(96, np.ones(96))
+
+
+@pytest.mark.parametrize("d", [128, 192])
+def test_rotated_quantize_round_trip(d):
+    rng = np.random.default_rng(3 + d)
+    s = rng.choice([-1.0, 1.0], d)
+    x = rng.standard_normal((50, d))
+    codes, ds, y = oracle.quantize_rotated_ref(x, s)
+    back = oracle.e4m3fn_decode(codes) * float(ds)
+    big = np.abs(y) >= 2.0 ** -6 * float(ds)          # normal e4m3 range
+    assert np.all(np.abs(back - y)[big] <= 2.0 ** -4 * np.abs(y)[big])
+    # rotating back recovers x up to that rounding
+    np.testing.assert_allclose(back @ oracle.rotation_matrix(d, s).T, x, atol=0.2)
