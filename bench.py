@@ -353,6 +353,16 @@ def main():
             msq, _ = time_launches(lambda: [zy.zyfa_fp8_quantize(x, x8, xs) for x, x8, xs in
                                             ((q, q8, qs), (k, k8, ks), (v, v8, vs))], args.steps, args.warmup)
             res[name + "_quantize_qkv_ms"] = round(msq, 4)
+            # q and k rotated before quantization (same signs), v plain: the
+            # README's recipe for models; attention then runs unchanged
+            signs = np.where(np.random.default_rng(0).random(w.d_qk) < 0.5, -1, 1).astype(np.int8)
+            msr, _ = time_launches(lambda: [zy.zyfa_fp8_quantize_rotated(x, signs, x8, xs) for x, x8, xs in
+                                            ((q, q8, qs), (k, k8, ks))], args.steps, args.warmup)
+            nb = (q.numel() + k.numel()) * 3      # read bf16 once, write e4m3 once
+            res[name + "_rotate_quantize_qk"] = {"ms": round(msr, 4), "gbs": round(nb / (msr * 1e-3) / 1e9, 1),
+                                                 "note": "algorithmic bytes (2 B read + 1 B written per element); "
+                                                         "the kernels read the input twice"}
+            (q8, qs), (k8, ks) = (zy.zyfa_fp8_quantize(x) for x in (q, k))
         fn()
         torch.cuda.synchronize()
         ms, _ = time_launches(fn, args.steps, args.warmup)

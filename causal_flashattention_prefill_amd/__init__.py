@@ -27,7 +27,7 @@ ZYFA_OK = 0
 STATUS = {
     "ZYFA_ERR_NULL": -1, "ZYFA_ERR_SHAPE": -2, "ZYFA_ERR_HEADDIM": -3, "ZYFA_ERR_GQA": -4,
     "ZYFA_ERR_DTYPE": -5, "ZYFA_ERR_LAYOUT": -6, "ZYFA_ERR_DESCALE": -7, "ZYFA_ERR_CAPTURE": -8,
-    "ZYFA_ERR_HIP": -9, "ZYFA_ERR_RANGE": -10, "ZYFA_ERR_ALIGN": -11, "ZYFA_ERR_PMODE": -12,
+    "ZYFA_ERR_HIP": -9, "ZYFA_ERR_RANGE": -10, "ZYFA_ERR_ALIGN": -11, "ZYFA_ERR_PMODE": -12, "ZYFA_ERR_SIGNS": -13,
 }
 # FP8 probability modes (zyfa_p_mode): default = lean P below the diagonal at
 # d_qk 128, exact P at d_qk 192.
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.zyfa_prepare.argtypes = [i, i, i, i, i, i, i, i, i, vp]
     L.zyfa_prepare.restype = i
     L.zyfa_fp8_quantize.argtypes = [vp, i, ll, vp, vp, vp]
+    L.zyfa_fp8_quantize_rotated.argtypes = [vp, i, ll, i, vp, vp, vp, vp]
+    L.zyfa_fp8_quantize_rotated.restype = i
     L.zyfa_fp8_quantize.restype = i
     L.zyfa_status_string.argtypes = [i]
     L.zyfa_status_string.restype = ctypes.c_char_p
@@ -228,6 +230,35 @@ def zyfa_fp8_quantize(x, x8=None, descale=None, stream=None):
         descale = torch.empty(1, dtype=torch.float32, device=x.device)
     _check(lib().zyfa_fp8_quantize(_ptr(x), xd, x.numel(), _ptr(x8), _ptr(descale), _stream(stream)),
            "zyfa_fp8_quantize")
+    return x8, descale
+
+
+def zyfa_fp8_quantize_rotated(x, signs=None, x8=None, descale=None, stream=None):
+    """Rotate the last axis of x (d = 128 or 192) by the orthogonal matrix of
+    zyfa.h's zyfa_fp8_quantize_rotated, then quantize per tensor. signs:
+    d values of +1 / -1 (a sequence or array on the host), or None for all
+    +1. Returns (codes as torch.float8_e4m3fn, descale as a 1-element fp32
+    CUDA tensor)."""
+    import numpy as np
+    import torch
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    xd = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}.get(x.dtype)
+    if xd is None:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    sg = None
+    if signs is not None:
+        sg = np.ascontiguousarray(np.asarray(signs.cpu() if hasattr(signs, "cpu") else signs).astype(np.int8))
+        if sg.shape != (d,):
+            raise ValueError(f"signs must hold {d} values")
+    if x8 is None:
+        x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    if descale is None:
+        descale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().zyfa_fp8_quantize_rotated(_ptr(x), xd, rows, d, None if sg is None else sg.ctypes.data,
+                                           _ptr(x8), _ptr(descale), _stream(stream)), "zyfa_fp8_quantize_rotated")
     return x8, descale
 
 

@@ -262,6 +262,38 @@ int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, flo
   return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
 }
 
+int zyfa_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const signed char* signs, void* x8,
+                              float* descale, void* stream_) {
+  if (x_dtype != ZYFA_DTYPE_BF16 && x_dtype != ZYFA_DTYPE_FP32) return ZYFA_ERR_DTYPE;
+  if (rows < 0) return ZYFA_ERR_SHAPE;
+  if (d != 128 && d != 192) return ZYFA_ERR_HEADDIM;
+  unsigned mask[6] = {0, 0, 0, 0, 0, 0};
+  if (signs) {
+    for (int i = 0; i < d; ++i) {
+      if (signs[i] != 1 && signs[i] != -1) return ZYFA_ERR_SIGNS;
+      if (signs[i] < 0) mask[i >> 5] |= 1u << (i & 31);
+    }
+  }
+  if (!descale || (rows > 0 && (!x || !x8))) return ZYFA_ERR_NULL;
+  if (rows > 0 && (!aligned16(x) || !aligned16(x8))) return ZYFA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(descale) & 3u) return ZYFA_ERR_ALIGN;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceScratch& sc = g_scratch[dev];
+  if (!sc.amax) {
+    if (stream_capturing(stream)) return ZYFA_ERR_CAPTURE;
+    if (hipMalloc(&sc.amax, sizeof(unsigned) * quantize_scratch_slots()) != hipSuccess) {
+      sc.amax = nullptr;
+      return ZYFA_ERR_HIP;
+    }
+  }
+  hipError_t e = launch_fp8_quantize_rotated(x, x_dtype == ZYFA_DTYPE_BF16 ? 0 : 2, rows, d, mask, x8, descale,
+                                             sc.amax, quantize_scratch_slots(), stream);
+  return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
+}
+
 const char* zyfa_status_string(int status) {
   switch (status) {
     case ZYFA_OK: return "ok";
@@ -277,6 +309,7 @@ const char* zyfa_status_string(int status) {
     case ZYFA_ERR_RANGE: return "the row stride is too large: 64 rows must span at most 2^31 bytes";
     case ZYFA_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case ZYFA_ERR_PMODE: return "unknown FP8 probability mode";
+    case ZYFA_ERR_SIGNS: return "rotation signs must each be +1 or -1";
     default: return "unknown status";
   }
 }

@@ -7,7 +7,7 @@
 // so that it is a normal float); code = RNE_e4m3fn(x / d).
 //
 // Three kernels on one stream, no atomics, so the result never depends on
-// timing:
+// timing (the rotated variant at the end of the file has the same shape):
 //  1. amax_partial: each block reduces a strided share of |x| to one value
 //     (non-negative floats compare like their bit patterns).
 //  2. amax_final: one block reduces the partials and writes the descale.
@@ -136,9 +136,237 @@ __global__ __launch_bounds__(kQThreads) void convert_kernel(const void* x, long 
   }
 }
 
+// ---- Rotation before quantization ("ZYFA" README, "Using FP8 attention in
+// a model"): each row x of d channels becomes y = x R with R orthogonal,
+//   d = 128: R = diag(s) H_128 / sqrt(128)  (Sylvester Hadamard, signs s)
+//   d = 192: R = diag(s) (C_3^T kron H_64) / 8  (Hadamard within each
+//            64-channel block, orthonormal DCT-II across the three blocks)
+// and the rotated tensor is quantized as above. Half a wave (32 lanes)
+// holds one row: for d = 128 lane l holds channels 4 l .. 4 l + 3, for
+// d = 192 channels 64 a + 2 l + t (a < 3, t < 2). The fast Walsh-Hadamard
+// transform does the butterflies on channel bits held in a lane in
+// registers and those held across lanes with xor shuffles inside the half
+// wave; butterfly (u, w) -> (u + w, u - w) keeps natural order, so the
+// result is x H. The two passes (maximum, then conversion) both rotate, so
+// the rotated tensor is never stored.
+
+// bit i set when s_i = -1
+struct SignMask {
+  unsigned w[6];
+};
+
+constexpr float kInvSqrt128 = 0.0883883476483184405f;
+// orthonormal DCT-II matrix, kC3[k][i] = a_k cos(pi (2 i + 1) k / 6)
+__device__ constexpr float kC3[3][3] = {{0.577350269189625765f, 0.577350269189625765f, 0.577350269189625765f},
+                                       {0.707106781186547524f, 0.0f, -0.707106781186547524f},
+                                       {0.408248290463863016f, -0.816496580927726033f, 0.408248290463863016f}};
+
+template <int D>
+struct Rot {
+  static constexpr int V = D == 128 ? 4 : 6;  // values per lane
+};
+
+// Sign bits of this lane's channels, as float sign-bit masks.
+template <int D>
+__device__ __forceinline__ void lane_signs(const SignMask& sm, int hl, unsigned (&sg)[Rot<D>::V]) {
+  if (D == 128) {
+    const unsigned w = hl < 8 ? sm.w[0] : hl < 16 ? sm.w[1] : hl < 24 ? sm.w[2] : sm.w[3];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sg[t] = ((w >> ((4 * hl + t) & 31)) & 1u) << 31;
+  } else {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const unsigned w = hl < 16 ? sm.w[2 * a] : sm.w[2 * a + 1];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sg[2 * a + t] = ((w >> ((2 * hl + t) & 31)) & 1u) << 31;
+    }
+  }
+}
+
+// butterfly across lanes: the partner at lane ^ M (within the 32-lane half
+// wave; ds_swizzle in bit mode, xor mask M) holds the channel with that bit
+// flipped
+template <int M>
+__device__ __forceinline__ float bfly_x(float v, bool upper) {
+  const float p = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x1F | (M << 10)));
+  return upper ? p - v : v + p;
+}
+
+// raw channel values of one row held by this lane (zeros past the last row)
+template <int D, int XDT>
+__device__ __forceinline__ void load_row(const void* x, long long row, bool live, int hl, float (&y)[Rot<D>::V]) {
+  const char* base = reinterpret_cast<const char*>(x);
+  if (D == 128) {
+    if (XDT == 0) {
+      u32x2 w = {0u, 0u};
+      if (live) w = *reinterpret_cast<const u32x2*>(base + row * 256 + hl * 8);
+      const unsigned w0 = w[0], w1 = w[1];
+      y[0] = bf16_lo(w0); y[1] = bf16_hi(w0); y[2] = bf16_lo(w1); y[3] = bf16_hi(w1);
+    } else {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (live) w = *reinterpret_cast<const u32x4*>(base + row * 512 + hl * 16);
+      const unsigned w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+      y[0] = as_float(w0); y[1] = as_float(w1); y[2] = as_float(w2); y[3] = as_float(w3);
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      if (XDT == 0) {
+        const unsigned w = live ? *reinterpret_cast<const unsigned*>(base + row * 384 + (64 * a + 2 * hl) * 2) : 0u;
+        y[2 * a] = bf16_lo(w); y[2 * a + 1] = bf16_hi(w);
+      } else {
+        u32x2 w = {0u, 0u};
+        if (live) w = *reinterpret_cast<const u32x2*>(base + row * 768 + (64 * a + 2 * hl) * 4);
+        const unsigned w0 = w[0], w1 = w[1];
+        y[2 * a] = as_float(w0); y[2 * a + 1] = as_float(w1);
+      }
+    }
+  }
+}
+
+template <int D, int M>
+__device__ __forceinline__ void bfly_stage(float (&y)[Rot<D>::V], int hl) {
+  const bool up = (hl & M) != 0;
+#pragma unroll
+  for (int t = 0; t < Rot<D>::V; ++t) y[t] = bfly_x<M>(y[t], up);
+}
+
+// y <- (y * s) R for one row (signs as float sign-bit masks)
+template <int D>
+__device__ __forceinline__ void transform(float (&y)[Rot<D>::V], int hl, const unsigned (&sg)[Rot<D>::V]) {
+#pragma unroll
+  for (int t = 0; t < Rot<D>::V; ++t) y[t] = as_float(__builtin_bit_cast(unsigned, y[t]) ^ sg[t]);
+  if (D == 128) {
+    // channel bits 0, 1 in the lane
+    const float a0 = y[0] + y[1], a1 = y[0] - y[1], a2 = y[2] + y[3], a3 = y[2] - y[3];
+    y[0] = a0 + a2; y[2] = a0 - a2; y[1] = a1 + a3; y[3] = a1 - a3;
+  } else {
+    // channel bit 0 of each 64-channel block in the lane
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const float u = y[2 * a], w = y[2 * a + 1];
+      y[2 * a] = u + w;
+      y[2 * a + 1] = u - w;
+    }
+  }
+  // the remaining channel bits across the lanes (lane bits 0..4)
+  bfly_stage<D, 1>(y, hl);
+  bfly_stage<D, 2>(y, hl);
+  bfly_stage<D, 4>(y, hl);
+  bfly_stage<D, 8>(y, hl);
+  bfly_stage<D, 16>(y, hl);
+  if (D == 128) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) y[t] *= kInvSqrt128;
+  } else {
+    // DCT across the blocks (and the 1/8 of the normalized Hadamard)
+    float z[6];
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        z[2 * c + t] = (kC3[c][0] * y[t] + kC3[c][1] * y[2 + t] + kC3[c][2] * y[4 + t]) * 0.125f;
+#pragma unroll
+    for (int t = 0; t < 6; ++t) y[t] = z[t];
+  }
+}
+
+// Each half wave takes kRotRows rows per step: their loads go out together,
+// so enough bytes are in flight to keep HBM busy.
+constexpr int kRotRows = 4;
+
+template <int D, int XDT>
+__global__ __launch_bounds__(kQThreads) void rot_amax_kernel(const void* x, long long rows, SignMask sm,
+                                                             unsigned* partial) {
+  __shared__ unsigned red[kQThreads / 64];
+  const int hl = threadIdx.x & 31;
+  unsigned sg[Rot<D>::V];
+  lane_signs<D>(sm, hl, sg);
+  const long long nh = ((long long)gridDim.x * kQThreads) >> 5;
+  unsigned m = 0;
+  for (long long r0 = (((long long)blockIdx.x * kQThreads + threadIdx.x) >> 5) * kRotRows; r0 < rows;
+       r0 += nh * kRotRows) {
+    float y[kRotRows][Rot<D>::V];
+#pragma unroll
+    for (int u = 0; u < kRotRows; ++u) load_row<D, XDT>(x, r0 + u, r0 + u < rows, hl, y[u]);
+#pragma unroll
+    for (int u = 0; u < kRotRows; ++u) {
+      transform<D>(y[u], hl, sg);   // rows past the end are zero and stay zero
+#pragma unroll
+      for (int t = 0; t < Rot<D>::V; ++t) m = max(m, __builtin_bit_cast(unsigned, fabsf(y[u][t])));
+    }
+  }
+  const unsigned r = block_max_u32(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = r;
+}
+
+template <int D, int XDT>
+__global__ __launch_bounds__(kQThreads) void rot_convert_kernel(const void* x, long long rows, SignMask sm,
+                                                                const float* descale, unsigned char* x8) {
+  const float inv = 1.0f / *descale;  // exact: descale is a power of two
+  const int hl = threadIdx.x & 31;
+  unsigned sg[Rot<D>::V];
+  lane_signs<D>(sm, hl, sg);
+  const long long nh = ((long long)gridDim.x * kQThreads) >> 5;
+  for (long long r0 = (((long long)blockIdx.x * kQThreads + threadIdx.x) >> 5) * kRotRows; r0 < rows;
+       r0 += nh * kRotRows) {
+    float y[kRotRows][Rot<D>::V];
+#pragma unroll
+    for (int u = 0; u < kRotRows; ++u) load_row<D, XDT>(x, r0 + u, r0 + u < rows, hl, y[u]);
+#pragma unroll
+    for (int u = 0; u < kRotRows; ++u) {
+      transform<D>(y[u], hl, sg);
+      const long long r = r0 + u;
+      if (r >= rows) continue;
+      if (D == 128) {
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[u][0] * inv, y[u][1] * inv, 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(y[u][2] * inv, y[u][3] * inv, p, true);
+        *reinterpret_cast<unsigned*>(x8 + r * 128 + 4 * hl) = (unsigned)p;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          const int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[u][2 * c] * inv, y[u][2 * c + 1] * inv, 0, false);
+          *reinterpret_cast<unsigned short*>(x8 + r * 192 + 64 * c + 2 * hl) = (unsigned short)(p & 0xFFFF);
+        }
+      }
+    }
+  }
+}
+
+template <int D, int XDT>
+hipError_t launch_rot(const void* x, long long rows, const SignMask& sm, void* x8, float* descale,
+                      unsigned* scratch_amax, int scratch_slots, hipStream_t s) {
+  constexpr int kRowsPerBlock = kQThreads / 32 * kRotRows;
+  long long want = (rows + kRowsPerBlock * 2 - 1) / (kRowsPerBlock * 2);
+  const int blocks = (int)(want < 1 ? 1 : (want > scratch_slots ? scratch_slots : want));
+  hipLaunchKernelGGL((rot_amax_kernel<D, XDT>), dim3(blocks), dim3(kQThreads), 0, s, x, rows, sm, scratch_amax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(kQThreads), 0, s, scratch_amax, blocks, descale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  long long cw = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int cblocks = (int)(cw < 1 ? 1 : (cw > 8192 ? 8192 : cw));
+  hipLaunchKernelGGL((rot_convert_kernel<D, XDT>), dim3(cblocks), dim3(kQThreads), 0, s, x, rows, sm, descale,
+                     (unsigned char*)x8);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int quantize_scratch_slots() { return kMaxPartials; }
+
+hipError_t launch_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const unsigned* sign_mask,
+                                       void* x8, float* descale, unsigned* scratch_amax, int scratch_slots,
+                                       hipStream_t s) {
+  SignMask sm;
+  for (int i = 0; i < 6; ++i) sm.w[i] = sign_mask[i];
+  if (d == 128)
+    return x_dtype == 0 ? launch_rot<128, 0>(x, rows, sm, x8, descale, scratch_amax, scratch_slots, s)
+                        : launch_rot<128, 2>(x, rows, sm, x8, descale, scratch_amax, scratch_slots, s);
+  return x_dtype == 0 ? launch_rot<192, 0>(x, rows, sm, x8, descale, scratch_amax, scratch_slots, s)
+                      : launch_rot<192, 2>(x, rows, sm, x8, descale, scratch_amax, scratch_slots, s);
+}
 
 hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
                                unsigned* scratch_amax, int scratch_slots, hipStream_t s) {

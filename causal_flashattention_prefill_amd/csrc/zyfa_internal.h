@@ -36,6 +36,10 @@ hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean
 hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
                                unsigned* scratch_amax, int scratch_slots, hipStream_t s);
 int quantize_scratch_slots();
+// sign_mask: six words, bit i set when channel i's sign is -1
+hipError_t launch_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const unsigned* sign_mask,
+                                       void* x8, float* descale, unsigned* scratch_amax, int scratch_slots,
+                                       hipStream_t s);
 hipError_t launch_lse_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,
                             float* lse, int batch, int seqlen, int nheads, int d_v, bool bshd, hipStream_t s);
 

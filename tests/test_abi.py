@@ -154,3 +154,29 @@ def _merge(**kw):
 ])
 def test_lse_merge_argument_errors(kw, status):
     assert _merge(**kw) == zy.STATUS[status]
+
+
+def _rot(**kw):
+    import numpy as np
+    a = dict(x=16, xd=0, rows=10, d=128, signs=None, x8=16, ds=16, stream=None)
+    a.update(kw)
+    sg = a["signs"]
+    ptr = None if sg is None else sg.ctypes.data
+    return zy.lib().zyfa_fp8_quantize_rotated(a["x"], a["xd"], a["rows"], a["d"], ptr, a["x8"], a["ds"], a["stream"])
+
+
+def test_quantize_rotated_argument_errors():
+    import numpy as np
+    S = zy.STATUS
+    assert _rot(xd=1) == S["ZYFA_ERR_DTYPE"]
+    assert _rot(rows=-1) == S["ZYFA_ERR_SHAPE"]
+    assert _rot(d=64) == S["ZYFA_ERR_HEADDIM"]
+    bad = np.ones(128, dtype=np.int8)
+    bad[7] = 0
+    assert _rot(signs=bad) == S["ZYFA_ERR_SIGNS"]
+    bad[7] = 2
+    assert _rot(signs=bad) == S["ZYFA_ERR_SIGNS"]
+    assert _rot(x=None) == S["ZYFA_ERR_NULL"]
+    assert _rot(ds=None) == S["ZYFA_ERR_NULL"]
+    assert _rot(x8=24) == S["ZYFA_ERR_ALIGN"]
+    assert _rot(ds=18) == S["ZYFA_ERR_ALIGN"]
