@@ -42,6 +42,17 @@ RANGE_CASES = {
     "fp8_chunk4096_s16384": "fp8",
 }
 CHUNK_Q = 4096
+# The README's own benchmark configuration at 16K tokens (Performance,
+# kernel-benchmark protocol): causal MHA, batch 1, max(32, 262144 / S) = 32
+# heads, q, k, v Gaussian with standard deviation 0.1, bshd. Reported beside
+# the README's MI355X figure for the same configuration (another software
+# stack and board: context, not the target).
+CONTEXT_CASES = {
+    "ctx_bf16_d128_std01_s16384": ("bf16", 128, 1237.0),
+    "ctx_bf16_d192_std01_s16384": ("bf16", 192, 1296.0),
+    "ctx_fp8_d128_std01_s16384": ("fp8", 128, 2597.0),
+    "ctx_fp8_d192_std01_s16384": ("fp8", 192, 2391.0),
+}
 MERGE_CASE = "merge_bf16_s16384"
 HBM_PEAK_GBS = 8000.0
 HEADLINE = "bf16_d192_s16384"
@@ -54,7 +65,7 @@ DESCRIPTIONS = {
     "fp8_d192_s16384": "causal MLA-prefill form, fp8 e4m3: batch 1, seqlen 16384, nheads 16, d_qk 192, d_v 128, "
                        "bhsd, N(0,1)",
 }
-ALL_CASES = list(CASES) + list(RANGE_CASES) + [MERGE_CASE]
+ALL_CASES = list(CASES) + list(RANGE_CASES) + [MERGE_CASE] + list(CONTEXT_CASES)
 
 
 def range_flops(B, H, Sq, Sk, delta, dqk, dv):
@@ -311,6 +322,32 @@ def range_or_merge_case(name, zy, args):
             "shape": f"{Sq} queries at positions {S - Sq}.. over {S} keys, nheads {H}/{Hk}, d {d}, bshd, LSE"}
 
 
+def context_case(name, zy, args):
+    """The README's benchmark configuration (see CONTEXT_CASES)."""
+    import numpy as np
+    import torch
+    dtype, dqk, readme = CONTEXT_CASES[name]
+    S, H = 16384, max(32, 262144 // 16384)
+    rng = np.random.Generator(np.random.PCG64(dqk))
+    dev = torch.device("cuda:0")
+    q, k = (torch.from_numpy(0.1 * rng.standard_normal((1, S, H, dqk), dtype=np.float32)).to(torch.bfloat16).to(dev)
+            for _ in range(2))
+    v = torch.from_numpy(0.1 * rng.standard_normal((1, S, H, 128), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    out = torch.empty((1, S, H, 128), dtype=torch.bfloat16, device=dev)
+    if dtype == "bf16":
+        fn = lambda: zy.zyfa_fwd(q, k, v, out)
+    else:
+        (q8, qs), (k8, ks), (v8, vs) = (zy.zyfa_fp8_quantize(x) for x in (q, k, v))
+        fn = lambda: zy.zyfa_fwd(q8, k8, v8, out, q_descale=qs, k_descale=ks, v_descale=vs)
+    fn()
+    torch.cuda.synchronize()
+    ms, _ = time_launches(fn, args.steps, args.warmup)
+    tf = float(H) * S * S * (dqk + 128) / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 2), "ms": round(ms, 4), "pct_of_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
+            "readme_mi355x_tflops": readme, "ratio_to_readme": round(tf / readme, 3),
+            "shape": f"MHA, batch 1, seqlen {S}, {H} heads, d_qk {dqk}, d_v 128, bshd, N(0, 0.1^2)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -337,6 +374,10 @@ def main():
     res = {}
     sustain = None
     for name in cases:
+        if name in CONTEXT_CASES:
+            res[name] = context_case(name, zy, args)
+            torch.cuda.empty_cache()
+            continue
         if name in RANGE_CASES or name == MERGE_CASE:
             res[name] = range_or_merge_case(name, zy, args)
             torch.cuda.empty_cache()

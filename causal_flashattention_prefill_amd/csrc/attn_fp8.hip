@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   constexpr int K_SLOT = KA_BYTES + KB_BYTES;
   // LDS fragment prefetch distance of the matrix cluster (16-key or
   // 16-column blocks); d 192 has fewer registers to spare
-  constexpr int kPf = D192 ? 1 : 2;
+  constexpr int kPfV = D192 ? 1 : 2;
+  constexpr int kPfK = D192 ? 1 : 2;
   constexpr int V_SLOT = kTileK * DV;
   static_assert(KA_BYTES == 16 * 1024 && V_SLOT == 16 * 1024 && (!D192 || KB_BYTES == 8 * 1024), "tile split");
 
@@ -340,34 +341,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         const bool pv = t >= 1 && t - 1 <= kt_w;
         if (pv) {
           const char* vs = vring + ((t - 1) % kSlots) * V_SLOT;
-          i32x8 vfb[2];
-          vfb[0] = v_frag(vs, 0);
-          if (kPf == 2) vfb[1] = v_frag(vs, 1);
+          i32x8 vfb[kPfV];
+#pragma unroll
+          for (int u = 0; u < kPfV; ++u) vfb[u] = v_frag(vs, u);
 #pragma unroll
           for (int qg = 0; qg < 2; ++qg) lacc[qg] = mfma_fp8(ones, pf[qg], lacc[qg], kE8M0One, psc[qg]);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * kPf, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * kPfV, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
-            const i32x8 cur = vfb[db % kPf];
-            if (db + kPf < 8) vfb[db % kPf] = v_frag(vs, db + kPf);
+            const i32x8 cur = vfb[db % kPfV];
+            if (db + kPfV < 8) vfb[db % kPfV] = v_frag(vs, db + kPfV);
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg) o[qg][db] = mfma_fp8(cur, pf[qg], o[qg][db], kE8M0One, psc[qg]);
-            if (db + kPf < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+            if (db + kPfV < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
           }
         }
         if (t <= kt_w) {
           const char* ka = kring + (t % kSlots) * K_SLOT;
-          // K fragments are read two 16-key blocks ahead of their MFMAs
-          KFrag kfb[2];
-          kfb[0] = k_frag(ka, 0);
-          if (kPf == 2) kfb[1] = k_frag(ka, 1);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (D192 ? 4 : 2) * kPf, 0);
+          // K fragments are read kPfK 16-key blocks ahead of their MFMAs
+          KFrag kfb[kPfK];
+#pragma unroll
+          for (int u = 0; u < kPfK; ++u) kfb[u] = k_frag(ka, u);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (D192 ? 4 : 2) * kPfK, 0);
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) {
-            const KFrag cur = kfb[kb % kPf];
-            if (kb + kPf < 8) kfb[kb % kPf] = k_frag(ka, kb + kPf);
+            const KFrag cur = kfb[kb % kPfK];
+            if (kb + kPfK < 8) kfb[kb % kPfK] = k_frag(ka, kb + kPfK);
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg)
               s[qg][kb] = mfma_fp8(cur.a, qf[qg], f32x4{0.f, 0.f, 0.f, 0.f}, kE8M0One, kE8M0One);
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
                 s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur.b1, qx[qg][1], s[qg][kb], 0, 0, 0);
               }
             }
-            if (kb + kPf < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 ? 4 : 2, 0);
+            if (kb + kPfK < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 ? 4 : 2, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, D192 ? 6 : 2, 0);
           }
         }
