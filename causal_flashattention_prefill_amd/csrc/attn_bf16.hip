@@ -15,7 +15,8 @@
 //    rows (two 16-row groups) for the whole key loop.
 //  - Keys stream in 64-key tiles through four-slot K and V rings in LDS,
 //    filled by direct global-to-LDS loads (buffer_load ... lds) two tiles
-//    (K) and one tile (V) ahead of use, all issued by the lag wave group.
+//    (K) and one tile (V) ahead of use; the lag wave group issues the K
+//    loads and the lead group the V loads.
 //  - Ping-pong (README, Kernel design: ping-pong schedule; the post
 //    "Attention at the Power Cap", two wave groups half a tile apart): the
 //    two waves that share a SIMD run half a tile apart, so while one issues
@@ -118,10 +119,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
 
     // Per-lane byte offsets of the direct-to-LDS tile loads (fixed for the
     // job; the offset of the tile, or of its upper half, goes into the
-    // buffer resource, whose extent still ends at the slice end, so rows
-    // past seqlen read as zeros). The lag group loads every tile: wave wq of
-    // it fills instructions I = wq * n + u (n = KLD or VLD) of each 32-row
-    // half. Instruction I fills bytes [1024 I, 1024 I + 1024) of the half;
+    // buffer resource, whose extent covers only the rows before seqlen, so
+    // later rows read as zeros). One wave group loads each whole tile (the
+    // lag group K, the lead group V): wave wq of the group fills
+    // instructions I = wq * n + u (n = KLD or VLD) of each 32-row half. Instruction I fills bytes [1024 I, 1024 I + 1024) of the half;
     // lane L's 16 bytes land at p = 1024 I + 16 L, which is row p / pitch,
     // chunk slot (p % pitch) / 16, so the lane fetches the global chunk that
     // belongs in that slot (the same offsets serve both halves, 32 rows
@@ -383,40 +384,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       // the matrix cluster of position i; the lag group runs the matrix
       // cluster of position i - 1 and then its vector cluster. On every SIMD
       // one wave is in a matrix cluster while the other computes a softmax.
-      // Interval i reads K(i - 1), K(i), V(i - 2) and V(i - 1). Between its
-      // two clusters each lag wave issues its share of K(i + 2) and V(i + 1)
-      // into the slots last read in interval i - 1 (four-slot rings); before
-      // the barrier it waits for the loads issued one interval earlier
-      // (K(i + 1), V(i), read from interval i + 1 on). The lead group issues
-      // no loads: it carries the longer chain of the interval (its softmax
-      // and then its matrix cluster, while the lag group's softmax runs
-      // beside that matrix cluster), and a wave that issues direct-to-LDS
-      // loads is held until the address unit has accepted them. The last
-      // position with work for the lag group is n_kt - 1 in descending order
-      // and its last key tile in ascending order; its PV runs two intervals
-      // later. A query tile whose rows see no key skips the loop.
+      // Interval i reads K(i - 1), K(i), V(i - 2) and V(i - 1). The lag
+      // group issues K(i + 2) between its two clusters and the lead group
+      // issues V(i + 1) at the start of the interval, each into the slots
+      // last read in interval i - 1 (four-slot rings); before the barrier
+      // each wave waits for the loads it issued one interval earlier (read
+      // from interval i + 1 on). A wave that issues direct-to-LDS loads is
+      // held until the address unit has accepted them, so the loads are
+      // split where each group has slack: issued by one group alone, they
+      // lengthen that group's chain past the other's. The last position
+      // with work for the lag group is n_kt - 1 in descending order and its
+      // last key tile in ascending order; its PV runs two intervals later. A
+      // query tile whose rows see no key skips the loop.
       const int lag_last = rev ? n_kt - 1 : (q0 + 127 + dl >= 0 ? min((q0 + 127 + dl) / kTileK, n_kt - 1) : -1);
       const int n_int = max(n_kt + 1, lag_last + 3);
       __syncthreads();   // the previous query tile's last reads of the rings are done
       if (any_key) {
-        if (!lead) {
+        if (lead) {
+          issue_v(0);
+        } else {
           issue_k(0);
           if (n_kt > 1) issue_k(1);
-          issue_v(0);
         }
         wait_vm<0>();
         __syncthreads();
         for (int i = 0; i < n_int; ++i) {
           if (lead) {
+            if (i + 1 < n_kt) issue_v(i + 1);
             if (i >= 1) vector_cluster(i - 1);
             matrix_cluster(i);
+            if (i + 1 < n_kt) wait_vm<2 * VLD>();
+            else wait_vm<0>();
           } else {
             if (i >= 1) matrix_cluster(i - 1);
             if (i + 2 < n_kt) issue_k(i + 2);
-            if (i + 1 < n_kt) issue_v(i + 1);
             if (i >= 1) vector_cluster(i - 1);
-            if (i + 2 < n_kt) wait_vm<2 * (KLD + VLD)>();
-            else if (i + 1 < n_kt) wait_vm<2 * VLD>();
+            if (i + 2 < n_kt) wait_vm<2 * KLD>();
             else wait_vm<0>();
           }
           __syncthreads();

@@ -15,7 +15,8 @@
 // = pairs of 256-row query tiles, 32 query rows per wave, transposed scores):
 //  - Keys stream in 128-key tiles through four-slot K and V rings in LDS,
 //    filled by direct global-to-LDS loads two tiles (K) and one tile (V)
-//    ahead of use, all issued by the lag wave group.
+//    ahead of use; the lag wave group issues the K loads and the lead
+//    group the V loads.
 //  - Ping-pong (README, Kernel design: ping-pong schedule): the two waves
 //    that share a SIMD run half a tile apart, so while one issues the
 //    matrix instructions of a tile the other runs the vector work of its
@@ -100,12 +101,16 @@ __device__ __forceinline__ float pow2_floor(float x) {
   return __builtin_bit_cast(float, e < 0x00800000u ? 0x00800000u : e);
 }
 
-// Four floats / scale -> four e4m3fn codes (RNE) in one word.
+// Four floats / scale -> four e4m3fn codes (RNE) in one word. The first
+// conversion keeps the upper half of its destination, which the second one
+// then writes, so the word may start from any value; written as assembly so
+// that no instruction zeroes it first (the builtin form always does).
 __device__ __forceinline__ unsigned cvt4_fp8(float a, float b, float c, float d, float scale) {
-  i16x2 w = {0, 0};
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, scale, false);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
-  return __builtin_bit_cast(unsigned, w);
+  unsigned w;
+  asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %5\n\tv_cvt_scalef32_pk_fp8_f32 %0, %3, %4, %5 op_sel:[0,0,0,1]"
+      : "=&v"(w)
+      : "v"(a), "v"(b), "v"(c), "v"(d), "v"(scale));
+  return w;
 }
 
 template <int DQK, bool WITH_LSE, bool LEAN>
@@ -248,9 +253,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // Per-lane byte offsets of the tile loads (fixed for the job); the
       // offset of the tile, or of its upper 64-row half, goes into the
       // buffer resource, whose extent still ends at the slice end, so rows
-      // past seqlen read as zeros. The lag group loads every tile, wave wsc
-      // of it instructions 2 wsc, 2 wsc + 1 (and wsc for d 128..191) of each
-      // half; the same offsets serve both halves (64 rows apart is a
+      // past seqlen read as zeros. One wave group loads each whole tile (the
+      // lag group K, the lead group V), wave wsc of it instructions 2 wsc,
+      // 2 wsc + 1 (and wsc for d 128..191) of each half; the same offsets serve both halves (64 rows apart is a
       // multiple of every swizzle period and kswap keeps bit 6).
       int kvo[3], vvo[2];
 #pragma unroll
@@ -498,39 +503,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // matrix cluster of tile i; the lag group runs the matrix cluster of
       // tile i - 1 and then its vector cluster. On every SIMD one wave is in
       // a matrix cluster while the other computes a softmax. Interval i
-      // reads K(i - 1), K(i), V(i - 2) and V(i - 1). Between its two
-      // clusters each lag wave issues its share of K(i + 2) and V(i + 1)
-      // into the slots last read in interval i - 1 (four-slot rings); before
-      // the barrier it waits for the loads issued one interval earlier
-      // (K(i + 1), V(i), read from interval i + 1 on). The lead group issues
-      // no loads: a wave that issues direct-to-LDS loads is held until the
-      // address unit accepts them, and the lead's softmax-then-matrix chain
-      // is the longer one. (Issued in a burst by all waves at the start of
-      // an interval the loads queue in the address unit and stall every
-      // wave.) The lag group's last tile (its PV) ends in interval
-      // kt_w + 2, the lead's in kt_w + 1.
+      // reads K(i - 1), K(i), V(i - 2) and V(i - 1). The lag group issues
+      // K(i + 2) between its two clusters and the lead group issues V(i + 1)
+      // at the start of the interval, into the slots last read in interval
+      // i - 1 (four-slot rings); before the barrier each wave waits for the
+      // loads it issued one interval earlier (read from interval i + 1 on).
+      // A wave that issues direct-to-LDS loads is held until the address
+      // unit accepts them; issued by one group alone they lengthen its chain
+      // past the other's, and issued in a burst by all waves at the start of
+      // an interval they queue in the address unit and stall every wave.
+      // The lag group's last tile (its PV) ends in interval kt_w + 2, the
+      // lead's in kt_w + 1.
       const int lag_last = q0 + 127 + dl >= 0 ? min((q0 + 127 + dl) / kTileK, n_kt - 1) : -1;
       const int n_int = max(n_kt + 1, lag_last + 3);
       __syncthreads();   // the previous query tile's last reads of the rings are done
       if (any_key) {     // a query tile whose rows see no key skips the loop
-        if (!lead) {
+        if (lead) {
+          issue_v(0);
+        } else {
           issue_k(0);
           if (n_kt > 1) issue_k(1);
-          issue_v(0);
         }
         wait_vm<0>();
         __syncthreads();
         for (int i = 0; i < n_int; ++i) {
           if (lead) {
+            if (i + 1 < n_kt) issue_v(i + 1);
             if (i >= 1) vector_cluster(i - 1);
             matrix_cluster(i);
+            if (i + 1 < n_kt) wait_vm<4>();
+            else wait_vm<0>();
           } else {
             if (i >= 1) matrix_cluster(i - 1);
             if (i + 2 < n_kt) issue_k(i + 2);
-            if (i + 1 < n_kt) issue_v(i + 1);
             if (i >= 1) vector_cluster(i - 1);
-            if (i + 2 < n_kt) wait_vm<D192 ? 10 : 8>();
-            else if (i + 1 < n_kt) wait_vm<4>();
+            if (i + 2 < n_kt) wait_vm<D192 ? 6 : 4>();
             else wait_vm<0>();
           }
           __syncthreads();
