@@ -89,7 +89,7 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference for HBM byte counters)")
     ap.add_argument("--sustain-seconds", type=float, default=3.0,
-                    help="seconds of back-to-back headline launches before the sustained-clock reading (0: skip)")
+                    help="seconds per timed run of the sustained-clock protocol on the headline case (0: skip)")
     return ap.parse_args()
 
 
@@ -199,28 +199,44 @@ def median(xs):
     return xs[len(xs) // 2] if xs else None
 
 
-def sustained(fn, flops: float, seconds: float):
-    """Back-to-back launches of fn for `seconds`, then 20 more timed with
-    events; GFX clock and socket power sampled over the last half of it."""
+def sustained(fn, flops: float, seconds: float, runs: int = 3):
+    """The README's sustained-clock protocol: 2 s idle, 1 s of back-to-back
+    warm-up launches, then `runs` runs of at least `seconds` of back-to-back
+    launches, each timed with one event pair around all of its launches; the
+    median run is reported with the median GFX clock and socket power
+    sampled during the timed runs."""
     import torch
-    t_end = time.perf_counter() + seconds
-    t_half = t_end - seconds / 2
+    time.sleep(2.0)
+    t_end = time.perf_counter() + 1.0
     n = 0
-    while time.perf_counter() < t_half:  # first half: heat up
+    while time.perf_counter() < t_end:
         fn()
         n += 1
         if n % 16 == 0:
             torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    per_run = []
     with PowerClockSampler() as smp:
-        while time.perf_counter() < t_end:
-            fn()
-            n += 1
-            if n % 16 == 0:
-                torch.cuda.synchronize()
-        ms, _ = time_launches(fn, 20, 0)
-    rec = {"seconds": seconds, "launches": n + 20, "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-           "ms": round(ms, 4), "gfxclk_mhz": median(smp.clk), "socket_power_w": median(smp.pw),
-           "samples": len(smp.clk)}
+        for _ in range(runs):
+            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t_end = time.perf_counter() + seconds
+            k = 0
+            start.record()
+            while time.perf_counter() < t_end:
+                fn()
+                k += 1
+                if k % 16 == 0:
+                    torch.cuda.synchronize()   # keeps the host within 16 launches of the GPU
+            stop.record()
+            torch.cuda.synchronize()
+            per_run.append((start.elapsed_time(stop) / k, k))
+    per_run.sort()
+    ms, k = per_run[len(per_run) // 2]
+    rec = {"protocol": f"2 s idle, 1 s warm-up, {runs} runs of >= {seconds} s back-to-back, median run",
+           "seconds": seconds, "runs": runs, "launches_median_run": k,
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
+           "tflops_runs": [round(flops / (m * 1e-3) / 1e12, 2) for m, _ in per_run],
+           "gfxclk_mhz": median(smp.clk), "socket_power_w": median(smp.pw), "samples": len(smp.clk)}
     if smp.err:
         rec["note"] = smp.err
     return rec
