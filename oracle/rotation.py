@@ -71,3 +71,24 @@ def quantize_rotated_ref(x, signs):
     y = rotate_ref(x, signs)
     codes, d = fp8_quantize_ref(y)
     return codes, d, y
+
+
+# ---- K smoothing ("ZYFA" README, "Using FP8 attention in a model"):
+# subtract the mean key of each head over the sequence before the rotation.
+# Every key of a row then loses the same vector c, so each score of the row
+# moves by the same q . c and the softmax, hence the output, is unchanged;
+# the log-sum-exp moves by scale * q . c.
+
+def key_mean_ref(k, layout: str = "bshd") -> np.ndarray:
+    """k (B, S, Hk, d) or (B, Hk, S, d) -> mean over positions, (B, Hk, d), float64."""
+    k = np.asarray(k, dtype=np.float64)
+    return k.mean(axis=1 if layout == "bshd" else 2)
+
+
+def quantize_shifted_rotated_ref(x, shift, signs, layout: str = "bshd"):
+    """(codes, descale, rotated values) of (x - shift[b, h]) R, quantized per
+    tensor; shift (B, H, d) is subtracted from every position of its head."""
+    x = np.asarray(x, dtype=np.float64)
+    sh = np.asarray(shift, dtype=np.float64)
+    sh = sh[:, None, :, :] if layout == "bshd" else sh[:, :, None, :]
+    return quantize_rotated_ref(x - sh, signs)

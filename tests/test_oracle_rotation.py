@@ -73,3 +73,49 @@ def test_rotated_quantize_round_trip(d):
     assert np.all(np.abs(back - y)[big] <= 2.0 ** -4 * np.abs(y)[big])
     # rotating back recovers x up to that rounding
     np.testing.assert_allclose(back @ oracle.rotation_matrix(d, s).T, x, atol=0.2)
+
+
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+def test_key_mean_closed_forms(layout):
+    rng = np.random.default_rng(9)
+    B, S, Hk, d = 2, 37, 3, 8
+    shp = (B, S, Hk, d) if layout == "bshd" else (B, Hk, S, d)
+    c = rng.standard_normal((B, Hk, d))
+    const = np.broadcast_to(c[:, None] if layout == "bshd" else c[:, :, None], shp)
+    np.testing.assert_allclose(oracle.key_mean_ref(const, layout), c, atol=1e-15)
+    # one position set apart: the mean moves by its deviation / S
+    k = np.array(const)
+    if layout == "bshd":
+        k[1, 5, 2] += 37.0
+    else:
+        k[1, 2, 5] += 37.0
+    want = c.copy()
+    want[1, 2] += 1.0
+    np.testing.assert_allclose(oracle.key_mean_ref(k, layout), want, atol=1e-13)
+
+
+def test_smoothing_keeps_output_and_shifts_lse():
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((1, 40, 4, 16))
+    k = rng.standard_normal((1, 40, 2, 16)) + 3.0        # keys with a large common part
+    v = rng.standard_normal((1, 40, 2, 16))
+    c = oracle.key_mean_ref(k)
+    o1, l1 = oracle.causal_attention_ref(q, k, v)
+    o2, l2 = oracle.causal_attention_ref(q, k - c[:, None], v)
+    np.testing.assert_allclose(o2, o1, atol=1e-12)
+    # LSE moves by scale * q . c of the row's KV head
+    hk = np.arange(4) * 2 // 4
+    qc = np.einsum("bshd,bhd->bhs", q, c[:, hk]) / 4.0
+    np.testing.assert_allclose(l1 - l2, qc, atol=1e-12)
+
+
+def test_shifted_rotated_quantize_is_rotate_of_difference():
+    rng = np.random.default_rng(11)
+    s = rng.choice([-1.0, 1.0], 128)
+    x = rng.standard_normal((1, 20, 2, 128)) + 5.0
+    sh = oracle.key_mean_ref(x)
+    codes, d, y = oracle.quantize_shifted_rotated_ref(x, sh, s)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-12)    # mean removed before the (linear) rotation
+    back = oracle.e4m3fn_decode(codes) * float(d)
+    big = np.abs(y) >= 2.0 ** -6 * float(d)
+    assert np.all(np.abs(back - y)[big] <= 2.0 ** -4 * np.abs(y)[big])
