@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
     L.zyfa_fp8_quantize.argtypes = [vp, i, ll, vp, vp, vp]
     L.zyfa_fp8_quantize_rotated.argtypes = [vp, i, ll, i, vp, vp, vp, vp]
     L.zyfa_fp8_quantize_rotated.restype = i
+    L.zyfa_fp8_quantize_rotated_shifted.argtypes = [vp, i, i, i, i, i, i, vp, vp, vp, vp, vp]
+    L.zyfa_fp8_quantize_rotated_shifted.restype = i
+    L.zyfa_key_mean.argtypes = [vp, i, i, i, i, i, i, vp, vp]
+    L.zyfa_key_mean.restype = i
     L.zyfa_fp8_quantize.restype = i
     L.zyfa_status_string.argtypes = [i]
     L.zyfa_status_string.restype = ctypes.c_char_p
@@ -233,12 +237,15 @@ def zyfa_fp8_quantize(x, x8=None, descale=None, stream=None):
     return x8, descale
 
 
-def zyfa_fp8_quantize_rotated(x, signs=None, x8=None, descale=None, stream=None):
+def zyfa_fp8_quantize_rotated(x, signs=None, x8=None, descale=None, *, shift=None, layout: str = "bshd",
+                              stream=None):
     """Rotate the last axis of x (d = 128 or 192) by the orthogonal matrix of
     zyfa.h's zyfa_fp8_quantize_rotated, then quantize per tensor. signs:
     d values of +1 / -1 (a sequence or array on the host), or None for all
-    +1. Returns (codes as torch.float8_e4m3fn, descale as a 1-element fp32
-    CUDA tensor)."""
+    +1. shift: optional (batch, heads, d) fp32 CUDA tensor subtracted from
+    every position of its head before the rotation (K smoothing; x is then
+    a 4-D tensor in `layout`). Returns (codes as torch.float8_e4m3fn,
+    descale as a 1-element fp32 CUDA tensor)."""
     import numpy as np
     import torch
     if not x.is_contiguous():
@@ -257,9 +264,37 @@ def zyfa_fp8_quantize_rotated(x, signs=None, x8=None, descale=None, stream=None)
         x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
     if descale is None:
         descale = torch.empty(1, dtype=torch.float32, device=x.device)
-    _check(lib().zyfa_fp8_quantize_rotated(_ptr(x), xd, rows, d, None if sg is None else sg.ctypes.data,
-                                           _ptr(x8), _ptr(descale), _stream(stream)), "zyfa_fp8_quantize_rotated")
+    sp = None if sg is None else sg.ctypes.data
+    if shift is None:
+        rc = lib().zyfa_fp8_quantize_rotated(_ptr(x), xd, rows, d, sp, _ptr(x8), _ptr(descale), _stream(stream))
+    else:
+        if x.dim() != 4 or layout not in LAYOUTS:
+            raise ValueError("a shift needs a 4-D x in bshd or bhsd")
+        B, S, H = (x.shape[0], x.shape[1], x.shape[2]) if layout == "bshd" else (x.shape[0], x.shape[2], x.shape[1])
+        if shift.dtype != torch.float32 or tuple(shift.shape) != (B, H, d) or not shift.is_contiguous():
+            raise ValueError(f"shift must be a contiguous fp32 tensor of shape {(B, H, d)}")
+        rc = lib().zyfa_fp8_quantize_rotated_shifted(_ptr(x), xd, B, S, H, d, LAYOUTS[layout], sp, _ptr(shift),
+                                                     _ptr(x8), _ptr(descale), _stream(stream))
+    _check(rc, "zyfa_fp8_quantize_rotated")
     return x8, descale
+
+
+def zyfa_key_mean(k, *, layout: str = "bshd", mean=None, stream=None):
+    """Mean key of each (batch, head) over the sequence: (batch, heads, d)
+    fp32 CUDA tensor (K smoothing, see zyfa.h)."""
+    import torch
+    if not k.is_contiguous() or k.dim() != 4:
+        raise ValueError("k must be a contiguous 4-D tensor")
+    kd = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}.get(k.dtype)
+    if kd is None:
+        raise TypeError(f"unsupported dtype {k.dtype}")
+    B, S, H = (k.shape[0], k.shape[1], k.shape[2]) if layout == "bshd" else (k.shape[0], k.shape[2], k.shape[1])
+    d = k.shape[3]
+    if mean is None:
+        mean = torch.empty((B, H, d), dtype=torch.float32, device=k.device)
+    _check(lib().zyfa_key_mean(_ptr(k), kd, B, S, H, d, LAYOUTS[layout], _ptr(mean), _stream(stream)),
+           "zyfa_key_mean")
+    return mean
 
 
 def zyfa_release() -> None:

@@ -188,6 +188,44 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
 
 using namespace zyfa;
 
+namespace {
+
+int quantize_rotated_impl(const void* x, int x_dtype, long long rows, int d, const signed char* signs,
+                          const float* shift, int seqlen, int nheads, bool bshd, void* x8, float* descale,
+                          void* stream_) {
+  if (x_dtype != ZYFA_DTYPE_BF16 && x_dtype != ZYFA_DTYPE_FP32) return ZYFA_ERR_DTYPE;
+  if (rows < 0) return ZYFA_ERR_SHAPE;
+  if (d != 128 && d != 192) return ZYFA_ERR_HEADDIM;
+  unsigned mask[6] = {0, 0, 0, 0, 0, 0};
+  if (signs) {
+    for (int i = 0; i < d; ++i) {
+      if (signs[i] != 1 && signs[i] != -1) return ZYFA_ERR_SIGNS;
+      if (signs[i] < 0) mask[i >> 5] |= 1u << (i & 31);
+    }
+  }
+  if (!descale || (rows > 0 && (!x || !x8))) return ZYFA_ERR_NULL;
+  if (rows > 0 && (!aligned16(x) || !aligned16(x8))) return ZYFA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(descale) & 3u) return ZYFA_ERR_ALIGN;
+  if (shift && !aligned16(shift)) return ZYFA_ERR_ALIGN;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceScratch& sc = g_scratch[dev];
+  if (!sc.amax) {
+    if (stream_capturing(stream)) return ZYFA_ERR_CAPTURE;
+    if (hipMalloc(&sc.amax, sizeof(unsigned) * quantize_scratch_slots()) != hipSuccess) {
+      sc.amax = nullptr;
+      return ZYFA_ERR_HIP;
+    }
+  }
+  hipError_t e = launch_fp8_quantize_rotated(x, x_dtype == ZYFA_DTYPE_BF16 ? 0 : 2, rows, d, mask, shift, seqlen,
+                                             nheads, bshd, x8, descale, sc.amax, quantize_scratch_slots(), stream);
+  return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen, int nheads,
@@ -263,34 +301,32 @@ int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, flo
 }
 
 int zyfa_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const signed char* signs, void* x8,
-                              float* descale, void* stream_) {
-  if (x_dtype != ZYFA_DTYPE_BF16 && x_dtype != ZYFA_DTYPE_FP32) return ZYFA_ERR_DTYPE;
-  if (rows < 0) return ZYFA_ERR_SHAPE;
+                              float* descale, void* stream) {
+  return quantize_rotated_impl(x, x_dtype, rows, d, signs, nullptr, 1, 1, true, x8, descale, stream);
+}
+
+int zyfa_fp8_quantize_rotated_shifted(const void* x, int x_dtype, int batch, int seqlen, int nheads, int d,
+                                      int layout, const signed char* signs, const float* shift, void* x8,
+                                      float* descale, void* stream) {
+  if (batch <= 0 || seqlen <= 0 || nheads <= 0) return ZYFA_ERR_SHAPE;
+  if (layout != ZYFA_LAYOUT_BSHD && layout != ZYFA_LAYOUT_BHSD) return ZYFA_ERR_LAYOUT;
+  if (!shift) return ZYFA_ERR_NULL;
+  const long long rows = (long long)batch * seqlen * nheads;
+  if (rows > 0x7FFFFFFFll) return ZYFA_ERR_RANGE;   // rows are indexed in 32 bits here
+  return quantize_rotated_impl(x, x_dtype, rows, d, signs, shift, seqlen, nheads, layout == ZYFA_LAYOUT_BSHD, x8,
+                               descale, stream);
+}
+
+int zyfa_key_mean(const void* k, int k_dtype, int batch, int seqlen, int nheads_k, int d, int layout, float* mean,
+                  void* stream) {
+  if (k_dtype != ZYFA_DTYPE_BF16 && k_dtype != ZYFA_DTYPE_FP32) return ZYFA_ERR_DTYPE;
+  if (batch <= 0 || seqlen <= 0 || nheads_k <= 0) return ZYFA_ERR_SHAPE;
   if (d != 128 && d != 192) return ZYFA_ERR_HEADDIM;
-  unsigned mask[6] = {0, 0, 0, 0, 0, 0};
-  if (signs) {
-    for (int i = 0; i < d; ++i) {
-      if (signs[i] != 1 && signs[i] != -1) return ZYFA_ERR_SIGNS;
-      if (signs[i] < 0) mask[i >> 5] |= 1u << (i & 31);
-    }
-  }
-  if (!descale || (rows > 0 && (!x || !x8))) return ZYFA_ERR_NULL;
-  if (rows > 0 && (!aligned16(x) || !aligned16(x8))) return ZYFA_ERR_ALIGN;
-  if (reinterpret_cast<uintptr_t>(descale) & 3u) return ZYFA_ERR_ALIGN;
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  int dev, rc;
-  if ((rc = current_device(&dev))) return rc;
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceScratch& sc = g_scratch[dev];
-  if (!sc.amax) {
-    if (stream_capturing(stream)) return ZYFA_ERR_CAPTURE;
-    if (hipMalloc(&sc.amax, sizeof(unsigned) * quantize_scratch_slots()) != hipSuccess) {
-      sc.amax = nullptr;
-      return ZYFA_ERR_HIP;
-    }
-  }
-  hipError_t e = launch_fp8_quantize_rotated(x, x_dtype == ZYFA_DTYPE_BF16 ? 0 : 2, rows, d, mask, x8, descale,
-                                             sc.amax, quantize_scratch_slots(), stream);
+  if (layout != ZYFA_LAYOUT_BSHD && layout != ZYFA_LAYOUT_BHSD) return ZYFA_ERR_LAYOUT;
+  if (!k || !mean) return ZYFA_ERR_NULL;
+  if (!aligned16(k) || (reinterpret_cast<uintptr_t>(mean) & 3u)) return ZYFA_ERR_ALIGN;
+  const hipError_t e = launch_key_mean(k, k_dtype == ZYFA_DTYPE_BF16 ? 0 : 2, batch, seqlen, nheads_k, d,
+                                       layout == ZYFA_LAYOUT_BSHD, mean, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
 }
 

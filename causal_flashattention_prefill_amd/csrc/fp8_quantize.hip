@@ -275,8 +275,51 @@ __device__ __forceinline__ void transform(float (&y)[Rot<D>::V], int hl, const u
 // so enough bytes are in flight to keep HBM busy.
 constexpr int kRotRows = 4;
 
-template <int D, int XDT>
-__global__ __launch_bounds__(kQThreads) void rot_amax_kernel(const void* x, long long rows, SignMask sm,
+// Optional vector subtracted from every row of a (batch, head) before the
+// rotation (K smoothing: the mean key of the head). Row r of the rotated
+// tensor belongs to head slot bh = b * nheads + h, whose vector is
+// shift[bh * d ..]; rows are counted in the tensor's memory order.
+struct ShiftDesc {
+  const float* shift;  // null: nothing subtracted
+  unsigned seqlen, nheads;
+  bool bshd;
+};
+
+__device__ __forceinline__ unsigned shift_slot(unsigned r, const ShiftDesc& sd) {
+  if (!sd.bshd) return r / sd.seqlen;                 // bhsd: rows of one head are contiguous
+  const unsigned bs = r / sd.nheads;                  // bshd: (batch, position) then head
+  return (bs / sd.seqlen) * sd.nheads + (r - bs * sd.nheads);
+}
+
+// this lane's channels of the row's shift vector
+template <int D>
+__device__ __forceinline__ void load_shift(const float* v, int hl, float (&sv)[Rot<D>::V]) {
+  if (D == 128) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(v + 4 * hl);
+    const unsigned w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    sv[0] = as_float(w0); sv[1] = as_float(w1); sv[2] = as_float(w2); sv[3] = as_float(w3);
+  } else {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(v + 64 * a + 2 * hl);
+      const unsigned w0 = w[0], w1 = w[1];
+      sv[2 * a] = as_float(w0); sv[2 * a + 1] = as_float(w1);
+    }
+  }
+}
+
+template <int D, bool SHIFT>
+__device__ __forceinline__ void subtract_shift(float (&y)[Rot<D>::V], long long r, bool live, int hl,
+                                               const ShiftDesc& sd) {
+  if (!SHIFT || !live) return;
+  float sv[Rot<D>::V];
+  load_shift<D>(sd.shift + (size_t)shift_slot((unsigned)r, sd) * D, hl, sv);
+#pragma unroll
+  for (int t = 0; t < Rot<D>::V; ++t) y[t] -= sv[t];
+}
+
+template <int D, int XDT, bool SHIFT>
+__global__ __launch_bounds__(kQThreads) void rot_amax_kernel(const void* x, long long rows, SignMask sm, ShiftDesc sd,
                                                              unsigned* partial) {
   __shared__ unsigned red[kQThreads / 64];
   const int hl = threadIdx.x & 31;
@@ -288,7 +331,10 @@ __global__ __launch_bounds__(kQThreads) void rot_amax_kernel(const void* x, long
        r0 += nh * kRotRows) {
     float y[kRotRows][Rot<D>::V];
 #pragma unroll
-    for (int u = 0; u < kRotRows; ++u) load_row<D, XDT>(x, r0 + u, r0 + u < rows, hl, y[u]);
+    for (int u = 0; u < kRotRows; ++u) {
+      load_row<D, XDT>(x, r0 + u, r0 + u < rows, hl, y[u]);
+      subtract_shift<D, SHIFT>(y[u], r0 + u, r0 + u < rows, hl, sd);
+    }
 #pragma unroll
     for (int u = 0; u < kRotRows; ++u) {
       transform<D>(y[u], hl, sg);   // rows past the end are zero and stay zero
@@ -300,9 +346,10 @@ __global__ __launch_bounds__(kQThreads) void rot_amax_kernel(const void* x, long
   if (threadIdx.x == 0) partial[blockIdx.x] = r;
 }
 
-template <int D, int XDT>
+template <int D, int XDT, bool SHIFT>
 __global__ __launch_bounds__(kQThreads) void rot_convert_kernel(const void* x, long long rows, SignMask sm,
-                                                                const float* descale, unsigned char* x8) {
+                                                                ShiftDesc sd, const float* descale,
+                                                                unsigned char* x8) {
   const float inv = 1.0f / *descale;  // exact: descale is a power of two
   const int hl = threadIdx.x & 31;
   unsigned sg[Rot<D>::V];
@@ -312,7 +359,10 @@ __global__ __launch_bounds__(kQThreads) void rot_convert_kernel(const void* x, l
        r0 += nh * kRotRows) {
     float y[kRotRows][Rot<D>::V];
 #pragma unroll
-    for (int u = 0; u < kRotRows; ++u) load_row<D, XDT>(x, r0 + u, r0 + u < rows, hl, y[u]);
+    for (int u = 0; u < kRotRows; ++u) {
+      load_row<D, XDT>(x, r0 + u, r0 + u < rows, hl, y[u]);
+      subtract_shift<D, SHIFT>(y[u], r0 + u, r0 + u < rows, hl, sd);
+    }
 #pragma unroll
     for (int u = 0; u < kRotRows; ++u) {
       transform<D>(y[u], hl, sg);
@@ -333,13 +383,14 @@ __global__ __launch_bounds__(kQThreads) void rot_convert_kernel(const void* x, l
   }
 }
 
-template <int D, int XDT>
-hipError_t launch_rot(const void* x, long long rows, const SignMask& sm, void* x8, float* descale,
-                      unsigned* scratch_amax, int scratch_slots, hipStream_t s) {
+template <int D, int XDT, bool SHIFT>
+hipError_t launch_rot(const void* x, long long rows, const SignMask& sm, const ShiftDesc& sd, void* x8,
+                      float* descale, unsigned* scratch_amax, int scratch_slots, hipStream_t s) {
   constexpr int kRowsPerBlock = kQThreads / 32 * kRotRows;
   long long want = (rows + kRowsPerBlock * 2 - 1) / (kRowsPerBlock * 2);
   const int blocks = (int)(want < 1 ? 1 : (want > scratch_slots ? scratch_slots : want));
-  hipLaunchKernelGGL((rot_amax_kernel<D, XDT>), dim3(blocks), dim3(kQThreads), 0, s, x, rows, sm, scratch_amax);
+  hipLaunchKernelGGL((rot_amax_kernel<D, XDT, SHIFT>), dim3(blocks), dim3(kQThreads), 0, s, x, rows, sm, sd,
+                     scratch_amax);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(kQThreads), 0, s, scratch_amax, blocks, descale);
@@ -347,9 +398,69 @@ hipError_t launch_rot(const void* x, long long rows, const SignMask& sm, void* x
   if (e != hipSuccess) return e;
   long long cw = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int cblocks = (int)(cw < 1 ? 1 : (cw > 8192 ? 8192 : cw));
-  hipLaunchKernelGGL((rot_convert_kernel<D, XDT>), dim3(cblocks), dim3(kQThreads), 0, s, x, rows, sm, descale,
-                     (unsigned char*)x8);
+  hipLaunchKernelGGL((rot_convert_kernel<D, XDT, SHIFT>), dim3(cblocks), dim3(kQThreads), 0, s, x, rows, sm, sd,
+                     descale, (unsigned char*)x8);
   return hipGetLastError();
+}
+
+template <int D, bool SHIFT>
+hipError_t launch_rot_dt(const void* x, int x_dtype, long long rows, const SignMask& sm, const ShiftDesc& sd,
+                         void* x8, float* descale, unsigned* scratch_amax, int scratch_slots, hipStream_t s) {
+  return x_dtype == 0 ? launch_rot<D, 0, SHIFT>(x, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s)
+                      : launch_rot<D, 2, SHIFT>(x, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s);
+}
+
+// ---- Mean over positions of each (batch, head), for K smoothing: one
+// workgroup of 1024 threads per (batch, head); d / 8 threads cover a row (8
+// channels each), 1024 / (d / 8) rows at a time; each thread sums its rows
+// in order, then one thread per channel adds the partial sums in order, so
+// the result does not depend on timing.
+constexpr int kMeanThreads = 1024;
+
+template <int D, int XDT>
+__global__ __launch_bounds__(kMeanThreads) void key_mean_kernel(const void* x, int seqlen, int nheads, bool bshd,
+                                                               float* mean) {
+  constexpr int TPR = D / 8;                 // threads per row
+  constexpr int RP = kMeanThreads / TPR;     // rows in parallel
+  __shared__ float part[RP][D];
+  const int bh = blockIdx.x;
+  const int b = bh / nheads, h = bh - (bh / nheads) * nheads;
+  const int t = threadIdx.x;
+  const int rp = t / TPR, c0 = (t - rp * TPR) * 8;
+  const long long row_stride = bshd ? (long long)nheads * D : D;
+  const long long base = bshd ? ((long long)b * seqlen * nheads + h) * D : (long long)bh * seqlen * D;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (rp < RP) {
+    for (int sp = rp; sp < seqlen; sp += RP) {
+      const long long e = base + sp * row_stride + c0;
+      if (XDT == 0) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned short*>(x) + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned wj = w[j];
+          acc[2 * j] += bf16_lo(wj);
+          acc[2 * j + 1] += bf16_hi(wj);
+        }
+      } else {
+        const float* f = reinterpret_cast<const float*>(x) + e;
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(f), w1 = *reinterpret_cast<const u32x4*>(f + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned a0 = w0[j], a1 = w1[j];
+          acc[j] += as_float(a0);
+          acc[4 + j] += as_float(a1);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[rp][c0 + j] = acc[j];
+  }
+  __syncthreads();
+  if (t < D) {
+    float sum = 0.f;
+    for (int i = 0; i < RP; ++i) sum += part[i][t];
+    mean[(long long)bh * D + t] = sum / (float)seqlen;
+  }
 }
 
 }  // namespace
@@ -357,15 +468,29 @@ hipError_t launch_rot(const void* x, long long rows, const SignMask& sm, void* x
 int quantize_scratch_slots() { return kMaxPartials; }
 
 hipError_t launch_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const unsigned* sign_mask,
-                                       void* x8, float* descale, unsigned* scratch_amax, int scratch_slots,
-                                       hipStream_t s) {
+                                       const float* shift, int seqlen, int nheads, bool bshd, void* x8,
+                                       float* descale, unsigned* scratch_amax, int scratch_slots, hipStream_t s) {
   SignMask sm;
   for (int i = 0; i < 6; ++i) sm.w[i] = sign_mask[i];
+  const ShiftDesc sd{shift, (unsigned)seqlen, (unsigned)nheads, bshd};
   if (d == 128)
-    return x_dtype == 0 ? launch_rot<128, 0>(x, rows, sm, x8, descale, scratch_amax, scratch_slots, s)
-                        : launch_rot<128, 2>(x, rows, sm, x8, descale, scratch_amax, scratch_slots, s);
-  return x_dtype == 0 ? launch_rot<192, 0>(x, rows, sm, x8, descale, scratch_amax, scratch_slots, s)
-                      : launch_rot<192, 2>(x, rows, sm, x8, descale, scratch_amax, scratch_slots, s);
+    return shift ? launch_rot_dt<128, true>(x, x_dtype, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s)
+                 : launch_rot_dt<128, false>(x, x_dtype, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s);
+  return shift ? launch_rot_dt<192, true>(x, x_dtype, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s)
+               : launch_rot_dt<192, false>(x, x_dtype, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s);
+}
+
+hipError_t launch_key_mean(const void* x, int x_dtype, int batch, int seqlen, int nheads, int d, bool bshd,
+                           float* mean, hipStream_t s) {
+  const dim3 g((unsigned)(batch * nheads)), b(kMeanThreads);
+  if (d == 128) {
+    if (x_dtype == 0) hipLaunchKernelGGL((key_mean_kernel<128, 0>), g, b, 0, s, x, seqlen, nheads, bshd, mean);
+    else hipLaunchKernelGGL((key_mean_kernel<128, 2>), g, b, 0, s, x, seqlen, nheads, bshd, mean);
+  } else {
+    if (x_dtype == 0) hipLaunchKernelGGL((key_mean_kernel<192, 0>), g, b, 0, s, x, seqlen, nheads, bshd, mean);
+    else hipLaunchKernelGGL((key_mean_kernel<192, 2>), g, b, 0, s, x, seqlen, nheads, bshd, mean);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,

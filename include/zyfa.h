@@ -220,6 +220,39 @@ int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, flo
 int zyfa_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const signed char* signs,
                               void* x8, float* descale, void* stream);
 
+/*
+ * zyfa_key_mean - mean key of each (batch, head) over the sequence, for K
+ * smoothing ("ZYFA" README, "Using FP8 attention in a model": subtracting
+ * the mean key of each head before the rotation lowers the quantization
+ * error further; the mean cancels in the softmax because every key of a
+ * row loses the same vector, so the output is unchanged and the LSE moves
+ * by softmax_scale * q . mean).
+ *   mean[b][h][c] = (1 / seqlen) sum_s k[b][s][h][c]   (fp32, fixed order)
+ *  k       device pointer, bf16 or fp32 (k_dtype), [batch, seqlen, nheads_k,
+ *          d] (bshd) or [batch, nheads_k, seqlen, d] (bhsd), 16-byte aligned.
+ *  mean    device pointer, batch * nheads_k * d fp32 (caller-owned).
+ *  d is 128 or 192. Deterministic; asynchronous on `stream`. Chunked prefill
+ *  and prefix caching need a mean fixed in advance (every key of a row must
+ *  lose the same vector): compute it once and pass the same one each time.
+ */
+int zyfa_key_mean(const void* k, int k_dtype, int batch, int seqlen, int nheads_k, int d, int layout,
+                  float* mean, void* stream);
+
+/*
+ * zyfa_fp8_quantize_rotated_shifted - zyfa_fp8_quantize_rotated of
+ * (x - shift[b][h]): the vector of each (batch, head) is subtracted from
+ * every position of that head before the rotation (K smoothing with the
+ * vector from zyfa_key_mean, or one fixed in advance).
+ *  x       [batch, seqlen, nheads, d] (bshd) or [batch, nheads, seqlen, d]
+ *          (bhsd), bf16 or fp32, 16-byte aligned; batch * seqlen * nheads
+ *          below 2^31 (ZYFA_ERR_RANGE otherwise).
+ *  shift   device pointer, batch * nheads * d fp32, 16-byte aligned.
+ *  Everything else as zyfa_fp8_quantize_rotated.
+ */
+int zyfa_fp8_quantize_rotated_shifted(const void* x, int x_dtype, int batch, int seqlen, int nheads, int d,
+                                      int layout, const signed char* signs, const float* shift, void* x8,
+                                      float* descale, void* stream);
+
 /* zyfa_status_string - static, human-readable text of a status code. */
 const char* zyfa_status_string(int status);
 

@@ -180,3 +180,23 @@ def test_quantize_rotated_argument_errors():
     assert _rot(ds=None) == S["ZYFA_ERR_NULL"]
     assert _rot(x8=24) == S["ZYFA_ERR_ALIGN"]
     assert _rot(ds=18) == S["ZYFA_ERR_ALIGN"]
+
+
+def test_key_mean_and_shifted_argument_errors():
+    S = zy.STATUS
+    L = zy.lib()
+    # zyfa_key_mean(k, k_dtype, batch, seqlen, nheads_k, d, layout, mean, stream)
+    assert L.zyfa_key_mean(16, 1, 1, 10, 2, 128, 0, 16, None) == S["ZYFA_ERR_DTYPE"]
+    assert L.zyfa_key_mean(16, 0, 0, 10, 2, 128, 0, 16, None) == S["ZYFA_ERR_SHAPE"]
+    assert L.zyfa_key_mean(16, 0, 1, 10, 2, 64, 0, 16, None) == S["ZYFA_ERR_HEADDIM"]
+    assert L.zyfa_key_mean(16, 0, 1, 10, 2, 128, 5, 16, None) == S["ZYFA_ERR_LAYOUT"]
+    assert L.zyfa_key_mean(None, 0, 1, 10, 2, 128, 0, 16, None) == S["ZYFA_ERR_NULL"]
+    assert L.zyfa_key_mean(24, 0, 1, 10, 2, 128, 0, 16, None) == S["ZYFA_ERR_ALIGN"]
+    # zyfa_fp8_quantize_rotated_shifted(x, xd, batch, seqlen, nheads, d, layout, signs, shift, x8, ds, stream)
+    f = L.zyfa_fp8_quantize_rotated_shifted
+    assert f(16, 0, 1, 10, 2, 128, 0, None, None, 16, 16, None) == S["ZYFA_ERR_NULL"]
+    assert f(16, 0, 1, 10, 2, 128, 7, None, 16, 16, 16, None) == S["ZYFA_ERR_LAYOUT"]
+    assert f(16, 0, 0, 10, 2, 128, 0, None, 16, 16, 16, None) == S["ZYFA_ERR_SHAPE"]
+    assert f(16, 0, 1 << 20, 1 << 12, 1, 128, 0, None, 16, 16, 16, None) == S["ZYFA_ERR_RANGE"]
+    assert f(16, 0, 1, 10, 2, 128, 0, None, 24, 16, 16, None) == S["ZYFA_ERR_ALIGN"]
+    assert f(16, 0, 1, 10, 2, 96, 0, None, 16, 16, 16, None) == S["ZYFA_ERR_HEADDIM"]

@@ -130,3 +130,75 @@ def test_rotation_lowers_error_on_activation_like_inputs():
     print(f"mean |d out| against fp64 on bf16 inputs: plain {errs[False]:.3e}, rotated {errs[True]:.3e}", flush=True)
     # measured: 8.0e-2 plain, 3.0e-2 rotated
     assert errs[True] < 0.6 * errs[False]
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "fp32"])
+@pytest.mark.parametrize("d,layout,S", [(128, "bshd", 1000), (192, "bhsd", 777), (128, "bhsd", 1), (192, "bshd", 4097)])
+def test_key_mean_matches_oracle(d, layout, S, xdt):
+    B, H = 2, 3
+    rng = np.random.Generator(np.random.PCG64(d + S))
+    shp = (B, S, H, d) if layout == "bshd" else (B, H, S, d)
+    k = rng.standard_normal(shp, dtype=np.float32) + 2.0
+    if xdt == "bf16":
+        t, ref = bf16_pair(k)
+    else:
+        t, ref = torch.from_numpy(k).cuda(), k.astype(np.float64)
+    print(f"case key mean d{d} {layout} S{S} {xdt}", flush=True)
+    mean = zy.zyfa_key_mean(t, layout=layout)
+    torch.cuda.synchronize()
+    want = oracle.key_mean_ref(ref, layout)
+    # fp32 sums of at most S terms: |error| <= S 2^-24 mean|k| (a loose bound)
+    amean = np.abs(ref).mean(axis=1 if layout == "bshd" else 2)
+    assert np.all(np.abs(mean.cpu().numpy() - want) <= S * 2.0 ** -24 * amean + 1e-30)
+    again = zy.zyfa_key_mean(t, layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(mean, again)
+
+
+@pytest.mark.parametrize("d,layout", [(128, "bshd"), (192, "bhsd")])
+def test_shifted_rotated_codes_match_oracle(d, layout):
+    B, S, H = 2, 300, 3
+    rng = np.random.Generator(np.random.PCG64(5 * d))
+    shp = (B, S, H, d) if layout == "bshd" else (B, H, S, d)
+    x = rng.standard_normal(shp, dtype=np.float32) + rng.standard_normal((1, 1, 1, d), dtype=np.float32) * 3
+    t, ref = bf16_pair(x)
+    shift = rng.standard_normal((B, H, d), dtype=np.float32)
+    s = _signs(d, 17)
+    print(f"case shifted rotated quantize d{d} {layout}", flush=True)
+    x8, ds = zy.zyfa_fp8_quantize_rotated(t, s, shift=torch.from_numpy(shift).cuda(), layout=layout)
+    torch.cuda.synchronize()
+    codes, dref, y = oracle.quantize_shifted_rotated_ref(ref, shift.astype(np.float64), s.astype(np.float64), layout)
+    assert float(ds.item()) == float(dref)
+    sh = shift.astype(np.float64)[:, None] if layout == "bshd" else shift.astype(np.float64)[:, :, None]
+    n = _check_codes(x8.view(torch.uint8).cpu().numpy(), codes, y, float(dref), np.abs(ref - sh).sum(axis=-1), d)
+    print(f"near-tie codes: {n}", flush=True)
+
+
+def test_smoothing_lowers_error_on_biased_keys():
+    """Keys with a common vector (as real keys have): subtracting the mean key
+    before the rotation shrinks what is quantized, and the attention output
+    is unchanged in exact arithmetic, so the FP8 error against fp64
+    attention on the bf16 inputs drops."""
+    w = WORKLOADS[5].resized(batch=1, seqlen=1536, name="act_smooth")
+    q, k, v = generate(w)
+    rng = np.random.Generator(np.random.PCG64(55))
+    k = k + 12.0 * rng.standard_normal((1, 1, w.nheads_k, w.d_qk), dtype=np.float32)
+    (tq, rq), (tk, rk), (tv, rv) = bf16_pair(q), bf16_pair(k), bf16_pair(v)
+    s = _signs(w.d_qk, 5)
+    ref, _ = oracle.causal_attention_ref(rq, rk, rv, layout=w.layout)
+    errs = {}
+    for smooth in (False, True):
+        q8, qs = zy.zyfa_fp8_quantize_rotated(tq, s)
+        if smooth:
+            mean = zy.zyfa_key_mean(tk, layout=w.layout)
+            k8, ks = zy.zyfa_fp8_quantize_rotated(tk, s, shift=mean, layout=w.layout)
+        else:
+            k8, ks = zy.zyfa_fp8_quantize_rotated(tk, s)
+        v8, vs = zy.zyfa_fp8_quantize(tv)
+        out = zy.zyfa_fwd(q8, k8, v8, layout=w.layout, q_descale=qs, k_descale=ks, v_descale=vs)
+        torch.cuda.synchronize()
+        errs[smooth] = float(np.mean(np.abs(out_to_f64(out) - ref)))
+    print(f"mean |d out| rotated {errs[False]:.3e}, rotated + smoothed {errs[True]:.3e}", flush=True)
+    # measured: 3.22e-2 rotated, 2.98e-2 rotated + smoothed (the rest comes
+    # from the outlier channels of q, which smoothing does not touch)
+    assert errs[True] < 0.95 * errs[False]
