@@ -89,7 +89,7 @@ int get_plan(const PlanKey& key, hipStream_t stream, const Plan** out) {
   const size_t bytes = t.entries.size() * sizeof(int32_t);
   if (hipMalloc(&p.jobs, bytes) != hipSuccess) return ZYFA_ERR_HIP;
   if (hipMemcpy(p.jobs, t.entries.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
-    hipFree(p.jobs);
+    (void)hipFree(p.jobs);
     return ZYFA_ERR_HIP;
   }
   *out = &(g_plans[key] = p);
@@ -352,19 +352,21 @@ const char* zyfa_status_string(int status) {
 
 void zyfa_release(void) {
   std::lock_guard<std::mutex> lock(g_mu);
+  // hipFree waits for work still using the memory; errors are ignored (the
+  // cache is emptied either way)
   int cur = 0;
-  hipGetDevice(&cur);
+  (void)hipGetDevice(&cur);
   for (auto& kv : g_plans) {
-    hipSetDevice(kv.first.device);
-    hipFree(kv.second.jobs);
+    (void)hipSetDevice(kv.first.device);
+    (void)hipFree(kv.second.jobs);
   }
   g_plans.clear();
   for (auto& kv : g_scratch) {
-    hipSetDevice(kv.first);
-    if (kv.second.amax) hipFree(kv.second.amax);
+    (void)hipSetDevice(kv.first);
+    if (kv.second.amax) (void)hipFree(kv.second.amax);
   }
   g_scratch.clear();
-  hipSetDevice(cur);
+  (void)hipSetDevice(cur);
 }
 
 int zyfa_plan_jobs(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int dtype, int num_cus_, int* out_tile_q,
