@@ -32,7 +32,12 @@ CASES = {
     "bf16_d128_gqa_s16384": (3, "bf16"),
     "fp8_d128_gqa_s16384": (3, "fp8"),
     "fp8_d192_s16384": (4, "fp8"),
+    "fp8_d128_share8_s16384": (3, "fp8"),
 }
+# Cases run on a resized workload: one GPU's share of workload 3 when its
+# heads are split over 8 GPUs in whole GQA groups (4 query heads over 1 KV
+# head, 16384 tokens): the kernel at the shape each GPU would run.
+RESIZED = {"fp8_d128_share8_s16384": {"nheads": 4, "nheads_k": 1, "name": "gqa_fp8_s16384_share8"}}
 # Partial-range calls and the LSE merge, on the workload-3 shape (batch 1,
 # 16384 keys, 32 / 8 heads, d 128, bshd): the last 4096 queries as one chunk
 # over the whole prefix (chunked prefill, LSE returned), and the merge of two
@@ -64,6 +69,8 @@ DESCRIPTIONS = {
                            "nheads_k 8, d 128, bshd, N(0,1)",
     "fp8_d192_s16384": "causal MLA-prefill form, fp8 e4m3: batch 1, seqlen 16384, nheads 16, d_qk 192, d_v 128, "
                        "bhsd, N(0,1)",
+    "fp8_d128_share8_s16384": "one GPU's share of the fp8 GQA case over 8 GPUs: batch 1, seqlen 16384, nheads 4, "
+                              "nheads_k 1, d 128, bshd, N(0,1)",
 }
 ALL_CASES = list(CASES) + list(RANGE_CASES) + [MERGE_CASE] + list(CONTEXT_CASES)
 
@@ -199,12 +206,14 @@ def median(xs):
     return xs[len(xs) // 2] if xs else None
 
 
-def sustained(fn, flops: float, seconds: float, runs: int = 3):
+def sustained(fn, flops: float, seconds: float, peak_tflops: float, runs: int = 3):
     """The README's sustained-clock protocol: 2 s idle, 1 s of back-to-back
     warm-up launches, then `runs` runs of at least `seconds` of back-to-back
     launches, each timed with one event pair around all of its launches; the
     median run is reported with the median GFX clock and socket power
-    sampled during the timed runs."""
+    sampled during the timed runs, and the fraction of the dense peak scaled
+    to that clock (TF/s over peak x clock / 2400 MHz), which separates the
+    schedule's efficiency from the power cap."""
     import torch
     time.sleep(2.0)
     t_end = time.perf_counter() + 1.0
@@ -237,6 +246,9 @@ def sustained(fn, flops: float, seconds: float, runs: int = 3):
            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
            "tflops_runs": [round(flops / (m * 1e-3) / 1e12, 2) for m, _ in per_run],
            "gfxclk_mhz": median(smp.clk), "socket_power_w": median(smp.pw), "samples": len(smp.clk)}
+    clk = rec["gfxclk_mhz"]
+    rec["frac_of_clock_scaled_peak"] = (round(rec["tflops"] / (peak_tflops * clk / 2400.0), 4)
+                                        if isinstance(clk, (int, float)) and clk > 0 else None)
     if smp.err:
         rec["note"] = smp.err
     return rec
@@ -291,9 +303,16 @@ def cpu_baseline(seconds_budget: float):
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         threads = os.cpu_count()
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"float64 oracle on {rows_done} query rows ({heads} head slice(s), last rows first) of the "
-                      f"bf16 d_qk=192 S=16384 workload, {dt:.1f} s; causal FLOPs of those rows / wall time"}
+                      f"bf16 d_qk=192 S=16384 workload, {dt:.1f} s on {cpu} ({os.cpu_count()} logical CPUs "
+                      f"visible, {threads} BLAS threads); causal FLOPs of those rows / wall time"}
 
 
 def range_or_merge_case(name, zy, args):
@@ -399,7 +418,7 @@ def main():
             torch.cuda.empty_cache()
             continue
         wid, dtype = CASES[name]
-        w = WORKLOADS[wid]
+        w = WORKLOADS[wid].resized(**RESIZED[name]) if name in RESIZED else WORKLOADS[wid]
         q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in generate(w))
         out = torch.empty(w.shape("q")[:-1] + (w.d_v,), dtype=torch.bfloat16, device=dev)
         if dtype == "bf16":
@@ -407,6 +426,7 @@ def main():
         else:
             (q8, qs), (k8, ks), (v8, vs) = (zy.zyfa_fp8_quantize(x) for x in (q, k, v))
             fn = lambda: zy.zyfa_fwd(q8, k8, v8, out, layout=w.layout, q_descale=qs, k_descale=ks, v_descale=vs)
+        if dtype == "fp8" and name not in RESIZED:
             msq, _ = time_launches(lambda: [zy.zyfa_fp8_quantize(x, x8, xs) for x, x8, xs in
                                             ((q, q8, qs), (k, k8, ks), (v, v8, vs))], args.steps, args.warmup)
             res[name + "_quantize_qkv_ms"] = round(msq, 4)
@@ -428,8 +448,12 @@ def main():
         res[name] = {"tflops": round(tf, 2), "ms": round(ms, 4),
                      "pct_of_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
                      "hbm_traffic_bytes": None if tr is None else int(tr)}
-        if name == (HEADLINE if HEADLINE in cases else cases[0]) and args.sustain_seconds > 0:
-            sustain = sustained(fn, w.flops(), args.sustain_seconds)
+        if args.sustain_seconds > 0 and name not in RESIZED:
+            # every 16K gate case gets the sustained-clock reading; the
+            # headline's is also reported at the top level
+            res[name]["sustained"] = sustained(fn, w.flops(), args.sustain_seconds, PEAK_TFLOPS[dtype])
+            if name == (HEADLINE if HEADLINE in cases else cases[0]):
+                sustain = res[name]["sustained"]
         del q, k, v, out
         torch.cuda.empty_cache()
 

@@ -29,8 +29,9 @@
 //    scaled MFMA) gets e_b = floor(block max - m_ref) in base-2 units, so its
 //    largest probability divided by 2^e_b lies in [1, 2) and stays normal;
 //    the PV MFMA multiplies 2^e_b back in through its B-scale operand.
-//  - Exact P: p = exp2(s - m_ref) rounded to e4m3fn as p / 2^e_b
-//    (v_cvt_scalef32_pk_fp8_f32, RNE).
+//  - Exact P: y = s - m_ref - e_b, p = exp2(y) rounded to e4m3fn (RNE,
+//    v_cvt_pk_fp8_f32); e_b is folded into the exponent's bias, so no
+//    scaling conversion is needed.
 //  - Lean P (README, Kernel design: lean P): the e4m3fn code of a positive
 //    value grows by 8 per doubling, so the code of 2^y is written directly as
 //    RNE(8 y + C), clamped to 0..255 (one FMA per score and one packing
@@ -101,15 +102,15 @@ __device__ __forceinline__ float pow2_floor(float x) {
   return __builtin_bit_cast(float, e < 0x00800000u ? 0x00800000u : e);
 }
 
-// Four floats / scale -> four e4m3fn codes (RNE) in one word. The first
-// conversion keeps the upper half of its destination, which the second one
-// then writes, so the word may start from any value; written as assembly so
-// that no instruction zeroes it first (the builtin form always does).
-__device__ __forceinline__ unsigned cvt4_fp8(float a, float b, float c, float d, float scale) {
+// Four floats -> four e4m3fn codes (RNE) in one word. The first conversion
+// keeps the upper half of its destination, which the second one then writes,
+// so the word may start from any value; written as assembly so that no
+// instruction zeroes it first (the builtin form always does).
+__device__ __forceinline__ unsigned cvt4_fp8(float a, float b, float c, float d) {
   unsigned w;
-  asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %5\n\tv_cvt_scalef32_pk_fp8_f32 %0, %3, %4, %5 op_sel:[0,0,0,1]"
+  asm("v_cvt_pk_fp8_f32 %0, %1, %2\n\tv_cvt_pk_fp8_f32 %0, %3, %4 op_sel:[0,0,1]"
       : "=&v"(w)
-      : "v"(a), "v"(b), "v"(c), "v"(d), "v"(scale));
+      : "v"(a), "v"(b), "v"(c), "v"(d));
   return w;
 }
 
@@ -483,15 +484,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
                                                       0x06040200u);
             }
           } else {
-            const float nm = -mref[qg];
-            const float sc0 = __builtin_ldexpf(1.0f, (int)e0);
-            const float sc1 = __builtin_ldexpf(1.0f, (int)e1);
+            const float nm0 = -(mref[qg] + e0);
+            const float nm1 = -(mref[qg] + e1);
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
               f32x4 p;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, nm));
-              pf[qg][kb] = (int)cvt4_fp8(p[0], p[1], p[2], p[3], kb < 4 ? sc0 : sc1);
+              for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, kb < 4 ? nm0 : nm1));
+              pf[qg][kb] = (int)cvt4_fp8(p[0], p[1], p[2], p[3]);
             }
           }
           psc[qg] = (int)es + 127;

@@ -162,7 +162,16 @@ def _sample_rows(S, rng, n=24):
 
 @pytest.mark.parametrize("wid", [3, 4, 5])
 def test_full_size_sampled_rows(wid):
-    w = WORKLOADS[wid]
+    _full_size_sampled_rows(WORKLOADS[wid], wid)
+
+
+def test_one_gpu_share_of_workload3():
+    # one GPU's share when workload 3's heads are split over 8 GPUs in whole
+    # GQA groups: 4 query heads over 1 KV head, 16384 tokens (128 jobs)
+    _full_size_sampled_rows(WORKLOADS[3].resized(nheads=4, nheads_k=1, name="gqa_fp8_s16384_share8"), 33)
+
+
+def _full_size_sampled_rows(w, wid):
     q, k, v = generate(w)
     print(f"case full fp8 {w.name}", flush=True)
     (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
