@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.zyfa_lse_merge.restype = i
     L.zyfa_prepare.argtypes = [i, i, i, i, i, i, i, i, i, vp]
     L.zyfa_prepare.restype = i
+    L.zyfa_set_tile_q.argtypes = [i, i, i, i, i, i, i]
+    L.zyfa_set_tile_q.restype = i
     L.zyfa_fp8_quantize.argtypes = [vp, i, ll, vp, vp, vp]
     L.zyfa_fp8_quantize_rotated.argtypes = [vp, i, ll, i, vp, vp, vp, vp]
     L.zyfa_fp8_quantize_rotated.restype = i
@@ -216,6 +218,12 @@ def zyfa_prepare(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout="bshd", dtyp
                  stream=None) -> None:
     _check(lib().zyfa_prepare(batch, seqlen, nheads, nheads_k, d_qk, d_v, LAYOUTS[layout], dtype, int(with_lse),
                               _stream(stream)), "zyfa_prepare")
+
+
+def zyfa_set_tile_q(batch, seqlen, nheads, nheads_k, d_qk=128, dtype=DTYPE_BF16, tile_q=0) -> None:
+    """Query-tile height (128 or 256; 0 = automatic) that calls of this shape
+    use on the current device from now on."""
+    _check(lib().zyfa_set_tile_q(batch, seqlen, nheads, nheads_k, d_qk, dtype, tile_q), "zyfa_set_tile_q")
 
 
 def zyfa_fp8_quantize(x, x8=None, descale=None, stream=None):

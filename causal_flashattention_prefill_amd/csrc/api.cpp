@@ -20,9 +20,10 @@ namespace {
 
 struct PlanKey {
   int device, batch, seqlen, nheads, nheads_k, d_qk, dtype;
+  int tile_q;  // 0 in a shape's key, the query-tile height in a plan's key
   bool operator<(const PlanKey& o) const {
-    return std::tie(device, batch, seqlen, nheads, nheads_k, d_qk, dtype) <
-           std::tie(o.device, o.batch, o.seqlen, o.nheads, o.nheads_k, o.d_qk, o.dtype);
+    return std::tie(device, batch, seqlen, nheads, nheads_k, d_qk, dtype, tile_q) <
+           std::tie(o.device, o.batch, o.seqlen, o.nheads, o.nheads_k, o.d_qk, o.dtype, o.tile_q);
   }
 };
 
@@ -40,6 +41,7 @@ struct DeviceScratch {
 
 std::mutex g_mu;
 std::map<PlanKey, Plan> g_plans;
+std::map<PlanKey, int> g_tile_choice;   // query-tile heights set by zyfa_set_tile_q
 std::map<int, DeviceScratch> g_scratch;
 std::map<int, int> g_num_cus;
 
@@ -71,16 +73,22 @@ int check_shape(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d
   return ZYFA_OK;
 }
 
-// Finds or builds the plan; caller holds g_mu.
-int get_plan(const PlanKey& key, hipStream_t stream, const Plan** out) {
+// Finds or builds the plan of a shape (shape.tile_q == 0) with the tile
+// height set for it, else the automatic one; caller holds g_mu.
+int get_plan(const PlanKey& shape, hipStream_t stream, const Plan** out) {
+  const int cus = num_cus(shape.device);
+  const auto ch = g_tile_choice.find(shape);
+  PlanKey key = shape;
+  key.tile_q = ch != g_tile_choice.end()
+                   ? ch->second
+                   : tile_q_rows(shape.batch, shape.seqlen, shape.nheads, shape.d_qk, shape.dtype, cus);
   auto it = g_plans.find(key);
   if (it != g_plans.end()) {
     *out = &it->second;
     return ZYFA_OK;
   }
   if (stream_capturing(stream)) return ZYFA_ERR_CAPTURE;
-  const int tq = tile_q_rows(key.d_qk, key.dtype);
-  JobTable t = build_job_table(key.batch, key.seqlen, key.nheads, key.nheads_k, tq, num_cus(key.device));
+  JobTable t = build_job_table(key.batch, key.seqlen, key.nheads, key.nheads_k, key.tile_q, cus);
   Plan p;
   p.num_wgs = t.num_wgs;
   p.jobs_per_wg = t.jobs_per_wg;
@@ -132,7 +140,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   if ((rc = current_device(&dev))) return rc;
   std::lock_guard<std::mutex> lock(g_mu);
   const Plan* plan = nullptr;
-  PlanKey key{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype};
+  PlanKey key{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype, 0};
   if ((rc = get_plan(key, stream, &plan))) return rc;
 
   AttnArgs a{};
@@ -176,10 +184,11 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
 
   hipError_t e;
   if (dtype == ZYFA_DTYPE_BF16)
-    e = launch_attn_bf16(a, d_qk, lse != nullptr, plan->num_wgs, stream);
+    e = launch_attn_bf16(a, d_qk, lse != nullptr, plan->tile_q, plan->num_wgs, stream);
   else
     e = launch_attn_fp8(a, d_qk, lse != nullptr,
-                        p_mode == ZYFA_P_LEAN || (p_mode == ZYFA_P_DEFAULT && d_qk == 128), plan->num_wgs, stream);
+                        p_mode == ZYFA_P_LEAN || (p_mode == ZYFA_P_DEFAULT && d_qk == 128), plan->tile_q,
+                        plan->num_wgs, stream);
   return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
 }
 
@@ -273,8 +282,21 @@ int zyfa_prepare(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int 
   if ((rc = current_device(&dev))) return rc;
   std::lock_guard<std::mutex> lock(g_mu);
   const Plan* plan = nullptr;
-  PlanKey key{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype};
+  PlanKey key{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype, 0};
   return get_plan(key, reinterpret_cast<hipStream_t>(stream), &plan);
+}
+
+int zyfa_set_tile_q(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int dtype, int tile_q) {
+  int rc = check_shape(batch, seqlen, nheads, nheads_k, d_qk, 128, ZYFA_LAYOUT_BSHD, dtype);
+  if (rc) return rc;
+  if (tile_q != 0 && tile_q != 128 && tile_q != 256) return ZYFA_ERR_SHAPE;
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  const PlanKey shape{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype, 0};
+  if (tile_q == 0) g_tile_choice.erase(shape);
+  else g_tile_choice[shape] = tile_q;
+  return ZYFA_OK;
 }
 
 int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale, void* stream_) {
@@ -375,7 +397,8 @@ int zyfa_plan_jobs(int batch, int seqlen, int nheads, int nheads_k, int d_qk, in
   if (rc) return rc;
   if (num_cus_ <= 0) return ZYFA_ERR_SHAPE;
   if (!out_tile_q || !out_num_wgs || !out_jobs_per_wg) return ZYFA_ERR_NULL;
-  JobTable t = build_job_table(batch, seqlen, nheads, nheads_k, tile_q_rows(d_qk, dtype), num_cus_);
+  JobTable t = build_job_table(batch, seqlen, nheads, nheads_k,
+                               tile_q_rows(batch, seqlen, nheads, d_qk, dtype, num_cus_), num_cus_);
   *out_tile_q = t.tile_q;
   *out_num_wgs = t.num_wgs;
   *out_jobs_per_wg = t.jobs_per_wg;

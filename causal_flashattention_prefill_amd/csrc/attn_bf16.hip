@@ -48,16 +48,17 @@ namespace zyfa {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kTileQ = 256;
 constexpr int kTileK = 64;
 constexpr int kSlots = 4;              // K and V ring depth
 constexpr float kTau = 8.0f;           // lazy-rescale threshold, log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRefFloor = -1e30f;      // initial reference maximum, base-2 units
 
-template <int DQK, bool WITH_LSE>
+template <int DQK, bool WITH_LSE, int QG>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnArgs a) {
   constexpr int DV = 128;
+  constexpr int RW = 16 * QG;                  // query rows per wave (QG 16-row groups)
+  constexpr int kTileQ = 8 * RW;               // query rows per tile
   constexpr int KCH = DQK / 8;                 // 16-byte chunks per K row
   constexpr int KPITCH = DQK * 2;              // bytes per K row in LDS
   constexpr int VPITCH = DV * 2;
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       // same keys at the same time for longer, so K and V stay in its L2
       const int qt = tt == 0 ? tB : tA;
       const int q0 = qt * kTileQ;
-      const int qw0 = q0 + wave * 32;
+      const int qw0 = q0 + wave * RW;
       const int qend = min(q0 + kTileQ, Sq);
       // key tiles that some row of the query tile sees (when any: the
       // tile's last row sees qend + delta keys, capped at seqlen_k)
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       const int n_kt = (min(Sk, qend + dl) - 1) / kTileK + 1;
       // this wave's last key tile (the one holding its diagonal), -1 if the
       // wave has no rows or its rows see no key
-      const int lk_w = min(Sk - 1, qw0 + 31 + dl);
+      const int lk_w = min(Sk - 1, qw0 + RW - 1 + dl);
       const int kt_w = (qw0 < Sq && lk_w >= 0) ? min(lk_w / kTileK, n_kt - 1) : -1;
 
       // Key tiles are visited in ascending order for the first (longer)
@@ -183,35 +184,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
 
       // Q fragments, MFMA B operand: lane (g, n) holds q[row n][32c + 8g .. +7],
       // read through a resource based at the wave's first row.
-      const int qr0 = q0 + 32 * ws;
+      const int qr0 = q0 + RW * ws;
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (unsigned long long)qr0 * (unsigned)qrs,
-                                                  rows_extent(min(Sq - qr0, 32), qrs, 2 * DQK));
-      bf16x8 qf[2][NC];
+                                                  rows_extent(min(Sq - qr0, RW), qrs, 2 * DQK));
+      bf16x8 qf[QG][NC];
 #pragma unroll
-      for (int qg = 0; qg < 2; ++qg)
+      for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
         for (int c = 0; c < NC; ++c)
           qf[qg][c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (16 * qg + n) * qrs + (32 * c + 8 * g) * 2));
 
-      f32x4 o[2][8];
-      f32x4 lacc[2];
+      f32x4 o[QG][8];
+      f32x4 lacc[QG];
 #pragma unroll
-      for (int qg = 0; qg < 2; ++qg) {
+      for (int qg = 0; qg < QG; ++qg) {
         lacc[qg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       // Reference maxima start at a finite floor, so rows that have seen no
       // key yet give exp2(-inf - m) = 0 and rescale factors of 1, never NaN.
-      float mref[2] = {kRefFloor, kRefFloor};
+      float mref[QG];
       // lazy-rescale threshold in raw score units, (m + tau) / sl2
-      float thr[2] = {neg_inf(), neg_inf()};
-      float lsum[2] = {0.f, 0.f};
+      float thr[QG];
+      float lsum[QG];
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        mref[qg] = kRefFloor;
+        thr[qg] = neg_inf();
+        lsum[qg] = 0.f;
+      }
       // scores of the tile in flight (made by a matrix cluster, turned into
       // P by the next vector cluster) and the bf16 P (made by a vector
       // cluster, multiplied into V by the next matrix cluster)
-      f32x4 s[2][4];
-      bf16x8 pb[2][2];
+      f32x4 s[QG][4];
+      bf16x8 pb[QG][2];
 
       auto issue_k = [&](int j) {
 #pragma unroll
@@ -266,22 +273,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
           for (int u = 0; u < kPfV; ++u) vfb[u] = v_frag(vs, u);
           if (!WITH_LSE) {
 #pragma unroll
-            for (int qg = 0; qg < 2; ++qg)
+            for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
               for (int kc = 0; kc < 2; ++kc)
                 lacc[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qg][kc], lacc[qg], 0, 0, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPfV, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * QG, 0);
           }
 #pragma unroll
           for (int idx = 0; idx < 16; ++idx) {
             const bf16x8 cur = vfb[idx % kPfV];
             if (idx + kPfV < 16) vfb[idx % kPfV] = v_frag(vs, idx + kPfV);
 #pragma unroll
-            for (int qg = 0; qg < 2; ++qg)
+            for (int qg = 0; qg < QG; ++qg)
               o[qg][idx & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pb[qg][idx >> 3], o[qg][idx & 7], 0, 0, 0);
             if (idx + kPfV < 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
           }
         }
         if (has(j)) {
@@ -296,10 +303,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
             if (idx + kPfK < 4 * NC) kfb[idx % kPfK] = k_frag(ks, idx + kPfK);
             const int c = idx >> 2, kb = idx & 3;
 #pragma unroll
-            for (int qg = 0; qg < 2; ++qg)
+            for (int qg = 0; qg < QG; ++qg)
               s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[qg][c], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[qg][kb], 0, 0, 0);
             if (idx + kPfK < 4 * NC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
           }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -318,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
         if (__builtin_expect(kt0 + kTileK - 1 > min(qw0 + dl, Sk - 1), 0)) {
           const float ninf = neg_inf();
 #pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
+          for (int qg = 0; qg < QG; ++qg) {
             const int q = min(qw0 + 16 * qg + n + dl, Sk - 1) - kt0 - 4 * g;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
@@ -327,21 +334,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
           }
         }
         // ---- lazy max: lane maxima of the raw scores, one ballot per tile
-        float x[2];
+        float x[QG];
+        bool need = false;
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
+        for (int qg = 0; qg < QG; ++qg) {
           float m = fmaxf(fmaxf(s[qg][0][0], s[qg][0][1]), s[qg][0][2]);
 #pragma unroll
           for (int e = 3; e < 15; e += 2)
             m = fmaxf(fmaxf(m, s[qg][e >> 2][e & 3]), s[qg][(e + 1) >> 2][(e + 1) & 3]);
           x[qg] = fmaxf(m, s[qg][3][3]);
+          need = need || (x[qg] > thr[qg]);
         }
-        if (__builtin_expect(wave_any((x[0] > thr[0]) || (x[1] > thr[1])), 0)) {
+        if (__builtin_expect(wave_any(need), 0)) {
           // Keep this branch real: with f == 1 the multiplies are harmless,
           // so the compiler would otherwise run them on every tile.
           asm volatile("" ::: "memory");
 #pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
+          for (int qg = 0; qg < QG; ++qg) {
             const float rm = max_xor32(max_xor16(x[qg])) * sl2;
             const float mn = fmaxf(mref[qg], rm);
             const float f = fast_exp2(mref[qg] - mn);
@@ -358,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
         // 16-bit values has been compiled incorrectly (every slot took
         // element 0).
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
+        for (int qg = 0; qg < QG; ++qg) {
           const float nm = -mref[qg];
           float ls = 0.f;
           u32x4 w[2];
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       // with work for the lag group is n_kt - 1 in descending order and its
       // last key tile in ascending order; its PV runs two intervals later. A
       // query tile whose rows see no key skips the loop.
-      const int lag_last = rev ? n_kt - 1 : (q0 + 127 + dl >= 0 ? min((q0 + 127 + dl) / kTileK, n_kt - 1) : -1);
+      const int lag_last = rev ? n_kt - 1 : (q0 + 4 * RW - 1 + dl >= 0 ? min((q0 + 4 * RW - 1 + dl) / kTileK, n_kt - 1) : -1);
       const int n_int = max(n_kt + 1, lag_last + 3);
       __syncthreads();   // the previous query tile's last reads of the rings are done
       if (any_key) {
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       // that saw no key (l = 0) get O = 0 and LSE = -inf
       if (qw0 < Sq) {
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
+        for (int qg = 0; qg < QG; ++qg) {
           float lt;
           if (WITH_LSE) {
             lt = lsum[qg] + swap16(lsum[qg]);
@@ -459,14 +468,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int d_qk, bool with_lse, int grid, hipStream_t s) {
+template <int DQK, int QG>
+static void launch_bf16(const AttnArgs& a, bool with_lse, dim3 gd, dim3 bd, hipStream_t s) {
+  if (with_lse) hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, true, QG>), gd, bd, 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, false, QG>), gd, bd, 0, s, a);
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int d_qk, bool with_lse, int tile_q, int grid, hipStream_t s) {
   const dim3 gd(grid), bd(kThreads);
+  if (tile_q != 128 && tile_q != 256) return hipErrorInvalidValue;
+  const bool tall = tile_q == 256;
   if (d_qk == 128) {
-    if (with_lse) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), gd, bd, 0, s, a);
+    if (tall) launch_bf16<128, 2>(a, with_lse, gd, bd, s);
+    else launch_bf16<128, 1>(a, with_lse, gd, bd, s);
   } else {
-    if (with_lse) hipLaunchKernelGGL((attn_fwd_bf16_kernel<192, true>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<192, false>), gd, bd, 0, s, a);
+    if (tall) launch_bf16<192, 2>(a, with_lse, gd, bd, s);
+    else launch_bf16<192, 1>(a, with_lse, gd, bd, s);
   }
   return hipGetLastError();
 }

@@ -69,7 +69,6 @@ namespace zyfa {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kTileQ = 256;
 constexpr int kTileK = 128;
 constexpr int kSlots = 4;             // K and V ring depth
 constexpr float kTau = 8.0f;
@@ -114,9 +113,11 @@ __device__ __forceinline__ unsigned cvt4_fp8(float a, float b, float c, float d)
   return w;
 }
 
-template <int DQK, bool WITH_LSE, bool LEAN>
+template <int DQK, bool WITH_LSE, bool LEAN, int QG>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArgs a) {
   constexpr int DV = 128;
+  constexpr int RW = 16 * QG;                       // query rows per wave (QG 16-row groups)
+  constexpr int kTileQ = 8 * RW;                    // query rows per tile
   constexpr bool D192 = DQK == 192;
   constexpr int KA_BYTES = kTileK * 128;            // K region for d 0..127
   constexpr int KB_BYTES = D192 ? kTileK * 64 : 0;  // K region for d 128..191
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // same keys at the same time for longer, so K and V stay in its L2
       const int qt = tt == 0 ? tB : tA;
       const int q0 = qt * kTileQ;
-      const int qw0 = q0 + wave * 32;
+      const int qw0 = q0 + wave * RW;
       const int qend = min(q0 + kTileQ, Sq);
       // key tiles that some row of the query tile sees (when any: the
       // tile's last row sees qend + delta keys, capped at seqlen_k)
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       const int n_kt = (min(Sk, qend + dl) - 1) / kTileK + 1;
       // this wave's last key tile (the one holding its diagonal), -1 if the
       // wave has no rows or its rows see no key
-      const int lk_w = min(Sk - 1, qw0 + 31 + dl);
+      const int lk_w = min(Sk - 1, qw0 + RW - 1 + dl);
       const int kt_w = (qw0 < Sq && lk_w >= 0) ? min(lk_w / kTileK, n_kt - 1) : -1;
       // key tiles from K0 on reach the diagonal band of this query tile:
       // exact P and (on the diagonal) the causal mask; tiles before K0, whose
@@ -204,13 +205,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // q[row n][160+8g..+7], the B operands of two 16x16x32 FP8 MFMAs over
       // d 128..191. They are read through a resource based at the wave's
       // first row.
-      const int qr0 = q0 + 32 * ws;
+      const int qr0 = q0 + RW * ws;
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (unsigned long long)qr0 * (unsigned)qrs,
-                                                  rows_extent(min(Sq - qr0, 32), qrs, DQK));
-      i32x8 qf[2];
-      long qx[2][2];
+                                                  rows_extent(min(Sq - qr0, RW), qrs, DQK));
+      i32x8 qf[QG];
+      long qx[QG][2];
 #pragma unroll
-      for (int qg = 0; qg < 2; ++qg) {
+      for (int qg = 0; qg < QG; ++qg) {
         const int off = (16 * qg + n) * qrs;
         const u32x4 lo = buf_load16(rq, off + 16 * g);
         const u32x4 hi = buf_load16(rq, off + 64 + 16 * g);
@@ -221,27 +222,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         }
       }
 
-      f32x4 o[2][8];
-      f32x4 lacc[2];
+      f32x4 o[QG][8];
+      f32x4 lacc[QG];
 #pragma unroll
-      for (int qg = 0; qg < 2; ++qg) {
+      for (int qg = 0; qg < QG; ++qg) {
         lacc[qg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       // Reference maxima start at a finite floor, so rows that have seen no
       // key yet give exp2(-inf - m) = 0 and rescale factors of 1, never NaN.
-      float mref[2] = {kRefFloor, kRefFloor};
+      float mref[QG];
       // lazy-rescale threshold in raw score units, (m + tau) / sl2, and the
       // lean-P offset (C - 8 m) / 65535 of each query group
-      float thr[2] = {neg_inf(), neg_inf()};
-      float lcs[2] = {0.f, 0.f};
+      float thr[QG];
+      float lcs[QG];
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        mref[qg] = kRefFloor;
+        thr[qg] = neg_inf();
+        lcs[qg] = 0.f;
+      }
       // scores of the tile in flight (made by a matrix cluster, turned into P
       // codes by the next vector cluster), the P codes and the E8M0 exponent
       // this lane supplies to the PV MFMA
-      f32x4 s[2][8];
-      i32x8 pf[2];
-      int psc[2];
+      f32x4 s[QG][8];
+      i32x8 pf[QG];
+      int psc[QG];
 
       // Direct global-to-LDS tile loads; K row r of a slot holds key
       // kswap(r), V row r holds key r; 16-byte chunks XOR-swizzled by row:
@@ -351,17 +358,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
 #pragma unroll
           for (int u = 0; u < kPfV; ++u) vfb[u] = v_frag(vs, u);
 #pragma unroll
-          for (int qg = 0; qg < 2; ++qg) lacc[qg] = mfma_fp8(ones, pf[qg], lacc[qg], kE8M0One, psc[qg]);
+          for (int qg = 0; qg < QG; ++qg) lacc[qg] = mfma_fp8(ones, pf[qg], lacc[qg], kE8M0One, psc[qg]);
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * kPfV, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
             const i32x8 cur = vfb[db % kPfV];
             if (db + kPfV < 8) vfb[db % kPfV] = v_frag(vs, db + kPfV);
 #pragma unroll
-            for (int qg = 0; qg < 2; ++qg) o[qg][db] = mfma_fp8(cur, pf[qg], o[qg][db], kE8M0One, psc[qg]);
+            for (int qg = 0; qg < QG; ++qg) o[qg][db] = mfma_fp8(cur, pf[qg], o[qg][db], kE8M0One, psc[qg]);
             if (db + kPfV < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
           }
         }
         if (t <= kt_w) {
@@ -371,22 +378,48 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
 #pragma unroll
           for (int u = 0; u < kPfK; ++u) kfb[u] = k_frag(ka, u);
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (D192 ? 4 : 2) * kPfK, 0);
+          // d 128..191 (d_qk = 192) accumulate onto the result of the scaled
+          // instruction. With two query groups another scaled instruction
+          // separates each such pair from the result it reads; with one, the
+          // pair of block kb - 1 is issued after the scaled instruction of
+          // block kb instead, since issued straight after the result it
+          // reads as its accumulator, the pair was given no wait states and
+          // read a stale accumulator on the GPU.
+          constexpr bool kDefer = D192 && QG == 1;
+          long pb0 = 0, pb1 = 0;   // d 128..191 K fragments of the deferred block
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) {
             const KFrag cur = kfb[kb % kPfK];
             if (kb + kPfK < 8) kfb[kb % kPfK] = k_frag(ka, kb + kPfK);
 #pragma unroll
-            for (int qg = 0; qg < 2; ++qg)
+            for (int qg = 0; qg < QG; ++qg)
               s[qg][kb] = mfma_fp8(cur.a, qf[qg], f32x4{0.f, 0.f, 0.f, 0.f}, kE8M0One, kE8M0One);
-            if (D192) {
+            if (kDefer) {
+              if (kb >= 1) {
+                // keeps the pair after this block's scaled instruction
+                __builtin_amdgcn_sched_barrier(0);
+                s[0][kb - 1] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pb0, qx[0][0], s[0][kb - 1], 0, 0, 0);
+                s[0][kb - 1] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pb1, qx[0][1], s[0][kb - 1], 0, 0, 0);
+              }
+              pb0 = cur.b0;
+              pb1 = cur.b1;
+            } else if (D192) {
 #pragma unroll
-              for (int qg = 0; qg < 2; ++qg) {
+              for (int qg = 0; qg < QG; ++qg) {
                 s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur.b0, qx[qg][0], s[qg][kb], 0, 0, 0);
                 s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur.b1, qx[qg][1], s[qg][kb], 0, 0, 0);
               }
             }
             if (kb + kPfK < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 ? 4 : 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, D192 ? 6 : 2, 0);
+            if (kDefer && kb == 0) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(kSchedMfma, (D192 ? 3 : 1) * QG, 0);
+          }
+          if (kDefer) {
+            // the pair of the last block follows the pair of block 6
+            __builtin_amdgcn_sched_barrier(0);
+            s[0][7] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pb0, qx[0][0], s[0][7], 0, 0, 0);
+            s[0][7] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pb1, qx[0][1], s[0][7], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
           }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -406,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         if (__builtin_expect(kt0 + kTileK - 1 > min(qw0 + dl, Sk - 1), 0)) {
           const float ninf = neg_inf();
 #pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
+          for (int qg = 0; qg < QG; ++qg) {
             const int q = min(qw0 + 16 * qg + n + dl, Sk - 1) - kt0 - 16 * g;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
@@ -417,9 +450,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         // ---- lane maxima of the raw scores per scale half (kb 0..3: keys
         // 16g..16g+15, kb 4..7: keys 64+16g..), then the maxima of the
         // 32-key scale blocks (held by lane groups g and g ^ 1)
-        float x0[2], x1[2], b0[2], b1[2];
+        float x0[QG], x1[QG], b0[QG], b1[QG];
+        bool need = false;
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
+        for (int qg = 0; qg < QG; ++qg) {
           float y0 = fmaxf(fmaxf(s[qg][0][0], s[qg][0][1]), s[qg][0][2]);
           float y1 = fmaxf(fmaxf(s[qg][4][0], s[qg][4][1]), s[qg][4][2]);
 #pragma unroll
@@ -433,13 +467,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
           b1[qg] = fmaxf(x1[qg], swap16(x1[qg]));
         }
         // ---- lazy test in raw score units, one ballot per tile
-        const bool need = (fmaxf(x0[0], x1[0]) > thr[0]) || (fmaxf(x0[1], x1[1]) > thr[1]);
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) need = need || (fmaxf(x0[qg], x1[qg]) > thr[qg]);
         if (__builtin_expect(wave_any(need), 0)) {
           // keep the rescale a real branch (with f == 1 it is harmless, so
           // the compiler would otherwise run it on every tile)
           asm volatile("" ::: "memory");
 #pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
+          for (int qg = 0; qg < QG; ++qg) {
             const float rm = max_xor32(fmaxf(b0[qg], b1[qg])) * sl2;
             const float mn = rm > mref[qg] + kTau ? rm : mref[qg];
             const float f = fast_exp2(mref[qg] - mn);
@@ -455,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         // and P codes
         const bool lean = LEAN && t < K0;
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
+        for (int qg = 0; qg < QG; ++qg) {
           // the block maximum is rounded to fp32 before m is subtracted,
           // exactly as m itself was (a fused multiply-subtract would give
           // e_b = -1 instead of 0 for the block that holds the maximum
@@ -514,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // an interval they queue in the address unit and stall every wave.
       // The lag group's last tile (its PV) ends in interval kt_w + 2, the
       // lead's in kt_w + 1.
-      const int lag_last = q0 + 127 + dl >= 0 ? min((q0 + 127 + dl) / kTileK, n_kt - 1) : -1;
+      const int lag_last = q0 + 4 * RW - 1 + dl >= 0 ? min((q0 + 4 * RW - 1 + dl) / kTileK, n_kt - 1) : -1;
       const int n_int = max(n_kt + 1, lag_last + 3);
       __syncthreads();   // the previous query tile's last reads of the rings are done
       if (any_key) {     // a query tile whose rows see no key skips the loop
@@ -547,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // ---- epilogue: O * dv / l (RNE to bf16), LSE = ln2 * (m + log2 l)
       if (qw0 < Sq) {
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
+        for (int qg = 0; qg < QG; ++qg) {
           const float lt = lacc[qg][0];
           const float f = lt > 0.f ? dvs / lt : 0.f;   // l = 0: the row saw no key
           const int q = qw0 + 16 * qg + n;
@@ -570,20 +605,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
 
 }  // namespace
 
-template <int DQK, bool LEAN>
+template <int DQK, bool LEAN, int QG>
 static void launch_fp8(const AttnArgs& a, bool with_lse, dim3 gd, dim3 bd, hipStream_t s) {
-  if (with_lse) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, true, LEAN>), gd, bd, 0, s, a);
-  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, false, LEAN>), gd, bd, 0, s, a);
+  if (with_lse) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, true, LEAN, QG>), gd, bd, 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, false, LEAN, QG>), gd, bd, 0, s, a);
 }
 
-hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean, int grid, hipStream_t s) {
+template <int DQK, int QG>
+static void launch_fp8_p(const AttnArgs& a, bool with_lse, bool lean, dim3 gd, dim3 bd, hipStream_t s) {
+  if (lean) launch_fp8<DQK, true, QG>(a, with_lse, gd, bd, s);
+  else launch_fp8<DQK, false, QG>(a, with_lse, gd, bd, s);
+}
+
+hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean, int tile_q, int grid,
+                           hipStream_t s) {
   const dim3 gd(grid), bd(kThreads);
+  if (tile_q != 128 && tile_q != 256) return hipErrorInvalidValue;
+  const bool tall = tile_q == 256;
   if (d_qk == 128) {
-    if (lean) launch_fp8<128, true>(a, with_lse, gd, bd, s);
-    else launch_fp8<128, false>(a, with_lse, gd, bd, s);
+    if (tall) launch_fp8_p<128, 2>(a, with_lse, lean, gd, bd, s);
+    else launch_fp8_p<128, 1>(a, with_lse, lean, gd, bd, s);
   } else {
-    if (lean) launch_fp8<192, true>(a, with_lse, gd, bd, s);
-    else launch_fp8<192, false>(a, with_lse, gd, bd, s);
+    if (tall) launch_fp8_p<192, 2>(a, with_lse, lean, gd, bd, s);
+    else launch_fp8_p<192, 1>(a, with_lse, lean, gd, bd, s);
   }
   return hipGetLastError();
 }

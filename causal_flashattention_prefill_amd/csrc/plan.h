@@ -6,8 +6,9 @@
 
 namespace zyfa {
 
-// Query-tile height (rows per workgroup job tile) of each kernel family.
-int tile_q_rows(int d_qk, int dtype);
+// Query-tile height (rows per workgroup job tile): 256, or 128 when that
+// shape has too few 256-row jobs to keep num_cus compute units busy.
+int tile_q_rows(int batch, int seqlen, int nheads, int d_qk, int dtype, int num_cus);
 
 struct JobTable {
   int tile_q = 0;        // query rows per tile

@@ -31,8 +31,10 @@ struct AttnArgs {
   const float* v_descale;
 };
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int d_qk, bool with_lse, int grid, hipStream_t s);
-hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean, int grid, hipStream_t s);
+// tile_q: query rows per tile, 256 (32 per wave) or 128 (16 per wave)
+hipError_t launch_attn_bf16(const AttnArgs& a, int d_qk, bool with_lse, int tile_q, int grid, hipStream_t s);
+hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean, int tile_q, int grid,
+                           hipStream_t s);
 hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
                                unsigned* scratch_amax, int scratch_slots, hipStream_t s);
 int quantize_scratch_slots();

@@ -173,6 +173,24 @@ int zyfa_prepare(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int 
                  int layout, int dtype, int with_lse, void* stream);
 
 /*
+ * zyfa_set_tile_q - set the query-tile height that calls of one shape use
+ * on the current device from now on. The README's work distribution pairs
+ * query tiles of one (batch, head) first with last and hands the pairs to
+ * a persistent grid; a shape with too few 256-row pairs to occupy every
+ * compute unit finishes sooner with 128-row tiles (16 query rows per wave,
+ * twice the pairs at half the work each), which the library picks by
+ * itself from a cost estimate. This call overrides that choice.
+ *  shape     as for zyfa_prepare (seqlen: query rows of the call; d_v 128)
+ *  tile_q    128 or 256, or 0 to return to the automatic choice
+ * Host-only (no HIP call, nothing allocated); the plan of the chosen height
+ * is built on the next zyfa_prepare or attention call of the shape, and
+ * plans already built stay valid. The setting outlives zyfa_release.
+ * Returns ZYFA_ERR_SHAPE for another tile_q, and the shape errors of
+ * zyfa_prepare.
+ */
+int zyfa_set_tile_q(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int dtype, int tile_q);
+
+/*
  * zyfa_fp8_quantize - per-tensor power-of-two FP8 quantization (README,
  * Usage: fp8_quantize returns the e4m3 tensor and its descale as a device
  * fp32 scalar).

@@ -33,10 +33,11 @@ For query row i (keys j <= i), with x_j = softmax_scale * log2(e) *
      value 2^floor(y) (1 + frac(y)) unbiased: its mean ratio to 2^y over a
      uniform frac(y) is 1 / (2 ln(2)^2));
    - lean P off the diagonal query tile ("lean_offdiag"): the query rows
-     are tiled in QUERY_TILE = 256 rows; keys of the key tiles that hold the
-     rows of row i's own query tile (key tile t >= 2 * floor(i / 256)) get
-     exact P, which covers every key of the rows with the fewest keys; the
-     key tiles before them get lean P. (Which tiles keep exact P is this
+     are tiled in query_tile rows (256 by default; 128 for shapes the
+     kernels run on 128-row tiles); keys of the key tiles that hold the rows
+     of row i's own query tile (key tile t >= floor(i / query_tile) *
+     query_tile / KEY_TILE) get exact P, which covers every key of the rows
+     with the fewest keys; the key tiles before them get lean P. (Which tiles keep exact P is this
      implementation's choice; the README uses lean P throughout at d = 128.)
 4. The key's weight is w_j = value(c_j) * 2^(e_b + m), with m the reference
    when its tile was visited. O_i = sum_j w_j v_j / sum_j w_j and
@@ -110,7 +111,8 @@ def row_weights(x: np.ndarray, i: int, p_mode: str, *, key_tile: int = KEY_TILE,
 
 def fp8_attention_rows_ref(q, k, v, b: int, h: int, rows, *, layout: str = "bshd",
                            softmax_scale: Optional[float] = None, p_mode: str = "exact",
-                           key_tile: int = KEY_TILE, block: int = BLOCK, tau: float = TAU):
+                           key_tile: int = KEY_TILE, block: int = BLOCK, tau: float = TAU,
+                           query_tile: int = QUERY_TILE):
     """O (len(rows), d_v) and natural-log LSE (len(rows),) of the given query
     rows of batch b and query head h, with probabilities rounded as above.
     q, k, v are the dequantized inputs (code value times descale)."""
@@ -126,7 +128,7 @@ def fp8_attention_rows_ref(q, k, v, b: int, h: int, rows, *, layout: str = "bshd
     lse = np.zeros(rows.shape[0])
     for r, i in enumerate(rows):
         x = (scale * LOG2E) * (kh[: i + 1] @ qh[i])
-        w, m = row_weights(x, int(i), p_mode, key_tile=key_tile, block=block, tau=tau)
+        w, m = row_weights(x, int(i), p_mode, key_tile=key_tile, block=block, tau=tau, query_tile=query_tile)
         l = w.sum()
         out[r] = (w @ vh[: i + 1]) / l
         lse[r] = (math.log2(l) + m) * math.log(2.0)

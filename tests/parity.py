@@ -152,3 +152,19 @@ def check_partial(out, ref_out, lse, ref_lse, what="", fp8=False):
     else:
         check_bf16(out[live], ref_out[live], None if lse is None else lse[live], None if lse is None else ref_lse[live],
                    what)
+
+
+class tile_height:
+    """Within the block, calls of one shape use query tiles of `tile_q` rows
+    (128 or 256) instead of the library's automatic choice."""
+
+    def __init__(self, zy, batch, seqlen, nheads, nheads_k, d_qk, dtype, tile_q):
+        self.zy, self.shape, self.tile_q = zy, (batch, seqlen, nheads, nheads_k, d_qk, dtype), tile_q
+
+    def __enter__(self):
+        self.zy.zyfa_set_tile_q(*self.shape, tile_q=self.tile_q)
+        return self
+
+    def __exit__(self, *exc):
+        self.zy.zyfa_set_tile_q(*self.shape, tile_q=0)
+        return False

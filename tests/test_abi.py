@@ -103,6 +103,25 @@ def test_job_table_covers_every_tile_once(B, S, H, Hk):
     assert counts.max() - counts.min() <= 1
 
 
+@pytest.mark.parametrize("B,S,H,Hk,tq", [(1, 16384, 32, 8, 256), (2, 32000, 32, 8, 256), (1, 8192, 32, 8, 256),
+                                         (1, 16384, 16, 16, 256), (1, 16384, 4, 1, 128), (1, 8192, 8, 8, 128),
+                                         (1, 4096, 4, 1, 128)])
+def test_tile_height_choice(B, S, H, Hk, tq):
+    # 128-row tiles only where 256-row pairs leave compute units idle: one
+    # GPU's share of the 16K GQA case over 8 GPUs (4 / 1 heads) has 128
+    # pairs of 256-row tiles for 256 compute units
+    assert zy.zyfa_plan_jobs(B, S, H, Hk)[0] == tq
+
+
+def test_set_tile_q_argument_errors():
+    L = zy.lib()
+    for bad in (-1, 64, 129, 512):
+        assert L.zyfa_set_tile_q(1, 1024, 4, 4, 128, 0, bad) == zy.STATUS["ZYFA_ERR_SHAPE"]
+    assert L.zyfa_set_tile_q(1, 1024, 6, 4, 128, 0, 128) == zy.STATUS["ZYFA_ERR_GQA"]
+    assert L.zyfa_set_tile_q(1, 1024, 4, 4, 96, 0, 128) == zy.STATUS["ZYFA_ERR_HEADDIM"]
+    assert L.zyfa_set_tile_q(0, 1024, 4, 4, 128, 0, 128) == zy.STATUS["ZYFA_ERR_SHAPE"]
+
+
 def test_job_pairs_have_equal_work():
     tq, nw, jp, table = zy.zyfa_plan_jobs(1, 16384, 32, 8)
     n = -(-16384 // tq)

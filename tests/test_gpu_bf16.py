@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from workloads import WORKLOADS, Workload, generate
-from parity import bf16_pair, check_bf16, out_to_f64, score_magnitude
+from parity import bf16_pair, check_bf16, out_to_f64, score_magnitude, tile_height
 
 pytestmark = pytest.mark.gpu
 
@@ -64,9 +64,12 @@ def test_workload1_full():
     (1, 257, 2, 1, 128, "bshd"),
     (1, 4097, 2, 1, 128, "bshd"),
 ])
-def test_small_shapes(B, S, H, Hk, dqk, layout, with_lse):
+@pytest.mark.parametrize("tile_q", [256, 128])
+def test_small_shapes(B, S, H, Hk, dqk, layout, with_lse, tile_q):
     w = Workload("small", B, S, H, Hk, dqk, 128, layout, ("bf16",), True, False, 1000 + S)
-    run_case(w, with_lse=with_lse)
+    print(f"tile_q {tile_q}", flush=True)
+    with tile_height(zy, B, S, H, Hk, dqk, zy.DTYPE_BF16, tile_q):
+        run_case(w, with_lse=with_lse)
 
 
 def test_no_lse_variant_workload1():
@@ -87,10 +90,12 @@ def _sample_rows(S, rng, n=24):
 
 
 @pytest.mark.parametrize("with_lse", [True, False])
-@pytest.mark.parametrize("wid", [2, 4, 5])
+@pytest.mark.parametrize("wid", [2, 4, 5, "3share"])
 def test_full_size_sampled_rows(wid, with_lse):
-    # the benchmark's shapes; the oracle computes sampled rows one by one
-    w = WORKLOADS[wid]
+    # the benchmark's shapes; the oracle computes sampled rows one by one.
+    # "3share": one GPU's share of the 16K GQA shape over 8 GPUs (4 / 1
+    # heads), which runs on 128-row query tiles
+    w = WORKLOADS[3].resized(nheads=4, nheads_k=1, name="gqa_s16384_share8") if wid == "3share" else WORKLOADS[wid]
     q, k, v = generate(w)
     (tq, rq), (tk, rk), (tv, rv) = bf16_pair(q), bf16_pair(k), bf16_pair(v)
     print(f"case full {w.name}", flush=True)
@@ -99,7 +104,7 @@ def test_full_size_sampled_rows(wid, with_lse):
     out, lse = res if with_lse else (res, None)
     o = out_to_f64(out)
     l = lse.cpu().numpy().astype(np.float64) if with_lse else None
-    rng = np.random.default_rng(wid)
+    rng = np.random.default_rng(33 if wid == "3share" else wid)
     for b in range(w.batch):
         for h in sorted(set([0, w.nheads - 1] + rng.integers(0, w.nheads, 2).tolist())):
             rows = _sample_rows(w.seqlen, rng)

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from workloads import WORKLOADS, Workload, generate
-from parity import bf16_pair, check_fp8, check_fp8_rounding, fp8_score_allowance, out_to_f64
+from parity import bf16_pair, check_fp8, check_fp8_rounding, fp8_score_allowance, out_to_f64, tile_height
 
 pytestmark = pytest.mark.gpu
 
@@ -108,9 +108,12 @@ def run_case(w: Workload, seed=None, with_lse=False, p_mode="default"):
     (1, 129, 2, 2, 192, "bshd"),
     (1, 4097, 2, 1, 128, "bshd"),
 ])
-def test_small_shapes(B, S, H, Hk, dqk, layout):
+@pytest.mark.parametrize("tile_q", [256, 128])
+def test_small_shapes(B, S, H, Hk, dqk, layout, tile_q):
     w = Workload("small_fp8", B, S, H, Hk, dqk, 128, layout, ("fp8",), False, False, 2000 + S)
-    run_case(w, with_lse=True)
+    print(f"tile_q {tile_q}", flush=True)
+    with tile_height(zy, B, S, H, Hk, dqk, zy.DTYPE_FP8, tile_q):
+        run_case(w, with_lse=True)
 
 
 @pytest.mark.parametrize("p_mode", ["exact", "lean"])
@@ -126,13 +129,15 @@ def test_modes_meet_the_gate(p_mode, dqk):
     (2, 389, 2, 1, 128, "bhsd"),
     (1, 520, 2, 2, 192, "bhsd"),
 ])
-def test_rounding_matches_fp8_oracle(p_mode, B, S, H, Hk, dqk, layout):
+@pytest.mark.parametrize("tile_q", [256, 128])
+def test_rounding_matches_fp8_oracle(p_mode, B, S, H, Hk, dqk, layout, tile_q):
     w = Workload("round_fp8", B, S, H, Hk, dqk, 128, layout, ("fp8",), False, False, 3000 + S)
     q, k, v = generate(w)
-    print(f"case fp8 rounding {p_mode} B{B} S{S} H{H}/{Hk} d{dqk} {layout}", flush=True)
+    print(f"case fp8 rounding {p_mode} B{B} S{S} H{H}/{Hk} d{dqk} {layout} tile_q {tile_q}", flush=True)
     (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
-    out, lse = zy.zyfa_fwd(q8, k8, v8, layout=layout, return_lse=True, q_descale=qs, k_descale=ks, v_descale=vs,
-                           p_mode=p_mode)
+    with tile_height(zy, B, S, H, Hk, dqk, zy.DTYPE_FP8, tile_q):
+        out, lse = zy.zyfa_fwd(q8, k8, v8, layout=layout, return_lse=True, q_descale=qs, k_descale=ks,
+                               v_descale=vs, p_mode=p_mode)
     torch.cuda.synchronize()
     o, l = out_to_f64(out), lse.cpu().numpy().astype(np.float64)
     rows = np.arange(S)
@@ -140,7 +145,7 @@ def test_rounding_matches_fp8_oracle(p_mode, B, S, H, Hk, dqk, layout):
     for b in range(B):
         for h in range(H):
             ro, rl = oracle.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=layout,
-                                                   p_mode=oracle_p_mode(p_mode, dqk))
+                                                   p_mode=oracle_p_mode(p_mode, dqk), query_tile=tile_q)
             gots.append(o[b, :, h] if layout == "bshd" else o[b, h])
             glse.append(l[b, h])
             refs.append(ro)
@@ -172,6 +177,9 @@ def test_one_gpu_share_of_workload3():
 
 
 def _full_size_sampled_rows(w, wid):
+    # query-tile height the library picks for this shape (it sets which key
+    # tiles take lean P)
+    tq = zy.zyfa_plan_jobs(w.batch, w.seqlen, w.nheads, w.nheads_k, w.d_qk, zy.DTYPE_FP8)[0]
     q, k, v = generate(w)
     print(f"case full fp8 {w.name}", flush=True)
     (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
@@ -189,7 +197,7 @@ def _full_size_sampled_rows(w, wid):
             refs.append(ro)
             if not w.activation_like:
                 rr, _ = oracle.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout,
-                                                      p_mode=oracle_p_mode("default", w.d_qk))
+                                                      p_mode=oracle_p_mode("default", w.d_qk), query_tile=tq)
                 rrefs.append(rr)
             hk = h // (w.nheads // w.nheads_k)
             extras.append(fp8_score_allowance(hv(rq)[b, h], hv(rk)[b, hk], hv(rv)[b, hk], w.softmax_scale, rows)

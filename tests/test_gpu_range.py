@@ -5,7 +5,8 @@ import pytest
 import torch
 
 import oracle
-from parity import (BF16_OUT_ABS, BF16_OUT_REL_ROUND, bf16_pair, check_bf16, check_partial, out_to_f64)
+from parity import (BF16_OUT_ABS, BF16_OUT_REL_ROUND, bf16_pair, check_bf16, check_partial, out_to_f64,
+                    tile_height)
 from workloads import WORKLOADS, Workload, generate
 
 pytestmark = pytest.mark.gpu
@@ -42,12 +43,14 @@ CASES = [
 
 @pytest.mark.parametrize("with_lse", [True, False])
 @pytest.mark.parametrize("B,Sq,Sk,qp,kp,H,Hk,dqk,layout", CASES)
-def test_range_bf16(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, with_lse):
-    print(f"case range bf16 B{B} Sq{Sq} Sk{Sk} q_pos0={qp} k_pos0={kp} H{H}/{Hk} d{dqk} {layout} lse={with_lse}",
-          flush=True)
+@pytest.mark.parametrize("tile_q", [256, 128])
+def test_range_bf16(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, with_lse, tile_q):
+    print(f"case range bf16 B{B} Sq{Sq} Sk{Sk} q_pos0={qp} k_pos0={kp} H{H}/{Hk} d{dqk} {layout} lse={with_lse} "
+          f"tile_q {tile_q}", flush=True)
     q, k, v = _draw(B, Sq, Sk, H, Hk, dqk, layout, 3000 + Sq + Sk)
     (tq, rq), (tk, rk), (tv, rv) = bf16_pair(q), bf16_pair(k), bf16_pair(v)
-    res = zy.zyfa_fwd_range(tq, tk, tv, qp, kp, layout=layout, return_lse=with_lse)
+    with tile_height(zy, B, Sq, H, Hk, dqk, zy.DTYPE_BF16, tile_q):
+        res = zy.zyfa_fwd_range(tq, tk, tv, qp, kp, layout=layout, return_lse=with_lse)
     torch.cuda.synchronize()
     out, lse = res if with_lse else (res, None)
     ro, rl = oracle.range_attention_ref(rq, rk, rv, qp, kp, layout=layout)
@@ -56,8 +59,10 @@ def test_range_bf16(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, with_lse):
 
 
 @pytest.mark.parametrize("B,Sq,Sk,qp,kp,H,Hk,dqk,layout", [CASES[0], CASES[2], CASES[3], CASES[4], CASES[7]])
-def test_range_fp8(B, Sq, Sk, qp, kp, H, Hk, dqk, layout):
-    print(f"case range fp8 B{B} Sq{Sq} Sk{Sk} q_pos0={qp} k_pos0={kp} H{H}/{Hk} d{dqk} {layout}", flush=True)
+@pytest.mark.parametrize("tile_q", [256, 128])
+def test_range_fp8(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, tile_q):
+    print(f"case range fp8 B{B} Sq{Sq} Sk{Sk} q_pos0={qp} k_pos0={kp} H{H}/{Hk} d{dqk} {layout} tile_q {tile_q}",
+          flush=True)
     q, k, v = _draw(B, Sq, Sk, H, Hk, dqk, layout, 4000 + Sq + Sk)
     deq, dev = [], []
     for x in (q, k, v):
@@ -68,7 +73,8 @@ def test_range_fp8(B, Sq, Sk, qp, kp, H, Hk, dqk, layout):
         deq.append(oracle.e4m3fn_decode(codes) * float(d))
         dev.append((x8, ds))
     (q8, qs), (k8, ks), (v8, vs) = dev
-    out, lse = zy.zyfa_fwd_range(q8, k8, v8, qp, kp, layout=layout, q_descale=qs, k_descale=ks, v_descale=vs)
+    with tile_height(zy, B, Sq, H, Hk, dqk, zy.DTYPE_FP8, tile_q):
+        out, lse = zy.zyfa_fwd_range(q8, k8, v8, qp, kp, layout=layout, q_descale=qs, k_descale=ks, v_descale=vs)
     torch.cuda.synchronize()
     ro, rl = oracle.range_attention_ref(*deq, qp, kp, layout=layout)
     # the FP8 LSE comes from the rounded probabilities: compare only where it

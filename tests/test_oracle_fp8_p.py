@@ -123,6 +123,24 @@ def test_query_tile_is_exact_in_lean_offdiag():
     assert np.array_equal(_row(x[:256], 255, "lean_offdiag"), _row(x[:256], 255, "exact"))
 
 
+def test_query_tile_of_128_rows_in_lean_offdiag():
+    # with 128-row query tiles, row 200 lies in query tile 1 (rows 128..255):
+    # key tile 1 (keys 128..) takes exact P and key tile 0 lean P; with
+    # 256-row query tiles both are exact
+    x = np.full(201, -300.0)
+    x[0] = 0.0
+    x[[1, 130, 200]] = -0.5
+    w = fp8_p.row_weights(x, 200, "lean_offdiag", query_tile=128)[0]
+    assert w[0] == 1.0 and w[1] == 0.75                 # lean, key tile 0
+    assert w[130] == 1.375 * 2.0 ** -1                  # exact, key tile 1: RNE(2^0.5)
+    assert w[200] == 1.375 * 2.0 ** -1
+    w = fp8_p.row_weights(x, 200, "lean_offdiag", query_tile=256)[0]
+    assert w[1] == 1.375 * 2.0 ** -1                    # exact: row 200 is in the first 256-row tile
+    # rows of the first 128-row query tile: every key is exact
+    assert np.array_equal(fp8_p.row_weights(x[:128], 127, "lean_offdiag", query_tile=128)[0],
+                          fp8_p.row_weights(x[:128], 127, "exact")[0])
+
+
 def test_lazy_reference():
     # tile 0 peaks at 0.5; tile 1 peaks at 1.0, within the threshold, so the
     # reference stays at 0.5 and key 128 is coded at y = 0.5 (lean: 1.5)
