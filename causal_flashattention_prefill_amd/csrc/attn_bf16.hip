@@ -10,9 +10,11 @@
 // LSE. Rows that see no key get O = 0 and LSE = -inf.
 //
 // Structure (one workgroup = 8 waves = 512 threads, persistent):
-//  - A job is a pair of 256-row query tiles (i, n-1-i) of one (batch, head)
-//    (README, Kernel design: work distribution). Each wave owns 32 query
-//    rows (two 16-row groups) for the whole key loop.
+//  - A job is a pair of query tiles (i, n-1-i) of one (batch, head)
+//    (README, Kernel design: work distribution). Each wave owns QG 16-row
+//    groups of query rows for the whole key loop: 256-row tiles with two
+//    groups, or 128-row tiles with one for shapes with few (batch, head)
+//    slices, whose 256-row pairs would leave compute units idle.
 //  - Keys stream in 64-key tiles through four-slot K and V rings in LDS,
 //    filled by direct global-to-LDS loads (buffer_load ... lds) two tiles
 //    (K) and one tile (V) ahead of use; the lag wave group issues the K

@@ -12,7 +12,8 @@
 // Rows that see no key get O = 0 and LSE = -inf.
 //
 // Structure (shared with the BF16 kernel: persistent 8-wave workgroups, jobs
-// = pairs of 256-row query tiles, 32 query rows per wave, transposed scores):
+// = pairs of query tiles, QG 16-row groups of query rows per wave (256-row
+// tiles with two, 128-row tiles with one), transposed scores):
 //  - Keys stream in 128-key tiles through four-slot K and V rings in LDS,
 //    filled by direct global-to-LDS loads two tiles (K) and one tile (V)
 //    ahead of use; the lag wave group issues the K loads and the lead
@@ -39,8 +40,8 @@
 //    conversion).
 //    C = 56 + 8 log2(2 ln^2 2) makes the piecewise-linear value unbiased.
 //    Lean P is used on key tiles that lie wholly before the workgroup's
-//    256-row query tile; the key tiles that overlap the query tile keep exact
-//    P, so the rows with the fewest keys (query tile 0) are exact throughout.
+//    query tile; the key tiles that overlap the query tile keep exact P, so
+//    the rows with the fewest keys (query tile 0) are exact throughout.
 //    The choice is uniform over the workgroup.
 //  - The row sum is one extra MFMA of the rounded, scaled P against a block
 //    of ones (README, Kernel design: row sum on the matrix unit), so the
