@@ -183,9 +183,11 @@ int zyfa_prepare(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int 
  * itself from a cost estimate. This call overrides that choice.
  *  shape     as for zyfa_prepare (seqlen: query rows of the call; d_v 128)
  *  tile_q    128 or 256, or 0 to return to the automatic choice
- * Host-only (no HIP call, nothing allocated); the plan of the chosen height
- * is built on the next zyfa_prepare or attention call of the shape, and
- * plans already built stay valid. The setting outlives zyfa_release.
+ * Reads the current device and allocates nothing; the plan of the chosen
+ * height is built on the next zyfa_prepare or attention call of the shape
+ * on that device, and plans already built stay valid (a plan is kept per
+ * height). The setting outlives zyfa_release. zyfa_plan_jobs shows the
+ * automatic choice only.
  * Returns ZYFA_ERR_SHAPE for another tile_q, and the shape errors of
  * zyfa_prepare.
  */
