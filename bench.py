@@ -272,47 +272,71 @@ def time_launches(fn, steps, warmup):
     return sum(ms) / len(ms), ms
 
 
-def cpu_baseline(seconds_budget: float):
-    """The float64 oracle on a bounded sample of the headline workload: the
-    last query rows of one (batch, head), timed on the host."""
+CPU_BLOCK_ROWS = 512
+
+
+def _cpu_worker(job):
+    """One worker of the CPU baseline: head slices of the headline workload's
+    shape (each its own seeded draw), float64 oracle rows from the last row
+    down in blocks, until the deadline; one BLAS thread. Returns rows, head
+    slices begun, FLOPs and compute time (input draws excluded)."""
+    index, deadline = job
+    from threadpoolctl import threadpool_limits
     import numpy as np
     import oracle
     from workloads import WORKLOADS
     w = WORKLOADS[4]
-    rng = np.random.Generator(np.random.PCG64(w.seed))
     S, dqk, dv = w.seqlen, w.d_qk, w.d_v
-    rows_done, flops, heads, t0 = 0, 0.0, 0, time.perf_counter()
-    block = 512
-    while time.perf_counter() - t0 < seconds_budget:
-        # one (batch, head) slice of the workload's shape per pass
-        q = oracle.bf16_round(rng.standard_normal((S, dqk), dtype=np.float32))[None, None]
-        k = oracle.bf16_round(rng.standard_normal((S, dqk), dtype=np.float32))[None, None]
-        v = oracle.bf16_round(rng.standard_normal((S, dv), dtype=np.float32))[None, None]
-        for r1 in range(S, 0, -block):
-            rows = np.arange(max(0, r1 - block), r1)
-            oracle.causal_attention_rows_ref(q, k, v, 0, 0, rows, layout="bhsd")
-            flops += float(np.sum(rows + 1)) * (dqk + dv) * 2.0
-            rows_done += len(rows)
-            if time.perf_counter() - t0 >= seconds_budget:
-                break
-        heads += 1
-    dt = time.perf_counter() - t0
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count()
+    rows_done, slices, flops, busy = 0, 0, 0.0, 0.0
+    with threadpool_limits(limits=1):
+        while time.time() < deadline:
+            rng = np.random.Generator(np.random.PCG64([w.seed, index, slices]))
+            q = oracle.bf16_round(rng.standard_normal((S, dqk), dtype=np.float32))[None, None]
+            k = oracle.bf16_round(rng.standard_normal((S, dqk), dtype=np.float32))[None, None]
+            v = oracle.bf16_round(rng.standard_normal((S, dv), dtype=np.float32))[None, None]
+            slices += 1
+            for r1 in range(S, 0, -CPU_BLOCK_ROWS):
+                if time.time() >= deadline:
+                    break
+                rows = np.arange(max(0, r1 - CPU_BLOCK_ROWS), r1)
+                t0 = time.perf_counter()
+                oracle.causal_attention_rows_ref(q, k, v, 0, 0, rows, layout="bhsd")
+                busy += time.perf_counter() - t0
+                flops += float(np.sum(rows + 1)) * (dqk + dv) * 2.0
+                rows_done += len(rows)
+    return rows_done, slices, flops, busy
+
+
+def cpu_baseline(seconds_budget: float):
+    """The float64 oracle on a bounded sample of the headline workload: one
+    head slice per worker process (one BLAS thread each, as numpy's
+    elementwise exponential runs on one thread), the last query rows first,
+    for about seconds_budget of wall time. Run before the GPU is touched;
+    workers are fresh interpreters (spawn)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    n = max(1, min(16, os.cpu_count() or 1))
+    deadline = time.time() + seconds_budget
+    t0 = time.perf_counter()
+    # a worker that dies raises here (BrokenProcessPool) instead of hanging
+    with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn")) as ex:
+        res = list(ex.map(_cpu_worker, [(i, deadline) for i in range(n)]))
+    wall = time.perf_counter() - t0
+    rows_done = sum(r[0] for r in res)
+    slices = sum(r[1] for r in res)
+    # aggregate rate: each worker's FLOPs over its own compute time
+    value = sum(r[2] / r[3] for r in res if r[3] > 0) / 1e12
     cpu = "unknown CPU"
     try:
         with open("/proc/cpuinfo") as f:
             cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"float64 oracle on {rows_done} query rows ({heads} head slice(s), last rows first) of the "
-                      f"bf16 d_qk=192 S=16384 workload, {dt:.1f} s on {cpu} ({os.cpu_count()} logical CPUs "
-                      f"visible, {threads} BLAS threads); causal FLOPs of those rows / wall time"}
+    return {"value": value, "unit": "TFLOP/s", "cores": n, "kind": "oracle",
+            "sample": f"float64 oracle on {rows_done} query rows of {slices} head slices of the bf16 d_qk=192 "
+                      f"S=16384 workload's shape ({n} worker processes with one BLAS thread each, last rows first, "
+                      f"{CPU_BLOCK_ROWS}-row blocks), {wall:.1f} s wall on {cpu} ({os.cpu_count()} logical CPUs "
+                      f"visible); sum over workers of causal FLOPs of their rows / their compute time"}
 
 
 def range_or_merge_case(name, zy, args):
@@ -388,6 +412,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+    # the CPU baseline runs first, in fresh worker processes, before this
+    # process touches the GPU
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     import numpy as np
     import torch
     import causal_flashattention_prefill_amd as zy
@@ -491,7 +518,7 @@ def main():
     if sustain is not None:
         line["sustained"] = sustain
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
