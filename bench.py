@@ -33,7 +33,11 @@ CASES = {
     "fp8_d128_gqa_s16384": (3, "fp8"),
     "fp8_d192_s16384": (4, "fp8"),
     "fp8_d128_share8_s16384": (3, "fp8"),
+    "fp8_d192_lean_s16384": (4, "fp8"),
 }
+# Cases run with a non-default FP8 probability mode: workload 4 with lean P
+# (the README keeps exact P at d_qk = 192; lean P is the library's option).
+PMODE = {"fp8_d192_lean_s16384": "lean"}
 # Cases run on a resized workload: one GPU's share of workload 3 when its
 # heads are split over 8 GPUs in whole GQA groups (4 query heads over 1 KV
 # head, 16384 tokens): the kernel at the shape each GPU would run.
@@ -71,6 +75,8 @@ DESCRIPTIONS = {
                        "bhsd, N(0,1)",
     "fp8_d128_share8_s16384": "one GPU's share of the fp8 GQA case over 8 GPUs: batch 1, seqlen 16384, nheads 4, "
                               "nheads_k 1, d 128, bshd, N(0,1)",
+    "fp8_d192_lean_s16384": "causal MLA-prefill form, fp8 e4m3 with lean P: batch 1, seqlen 16384, nheads 16, "
+                            "d_qk 192, d_v 128, bhsd, N(0,1)",
 }
 ALL_CASES = list(CASES) + list(RANGE_CASES) + [MERGE_CASE] + list(CONTEXT_CASES)
 
@@ -452,8 +458,11 @@ def main():
             fn = lambda: zy.zyfa_fwd(q, k, v, out, layout=w.layout)
         else:
             (q8, qs), (k8, ks), (v8, vs) = (zy.zyfa_fp8_quantize(x) for x in (q, k, v))
-            fn = lambda: zy.zyfa_fwd(q8, k8, v8, out, layout=w.layout, q_descale=qs, k_descale=ks, v_descale=vs)
-        if dtype == "fp8" and name not in RESIZED:
+            pm = PMODE.get(name, "default")
+            fn = lambda: zy.zyfa_fwd(q8, k8, v8, out, layout=w.layout, q_descale=qs, k_descale=ks, v_descale=vs,
+                                     p_mode=pm)
+        extra = name in RESIZED or name in PMODE   # context cases: no quantizer timing, no sustained run
+        if dtype == "fp8" and not extra:
             msq, _ = time_launches(lambda: [zy.zyfa_fp8_quantize(x, x8, xs) for x, x8, xs in
                                             ((q, q8, qs), (k, k8, ks), (v, v8, vs))], args.steps, args.warmup)
             res[name + "_quantize_qkv_ms"] = round(msq, 4)
@@ -475,7 +484,7 @@ def main():
         res[name] = {"tflops": round(tf, 2), "ms": round(ms, 4),
                      "pct_of_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
                      "hbm_traffic_bytes": None if tr is None else int(tr)}
-        if args.sustain_seconds > 0 and name not in RESIZED:
+        if args.sustain_seconds > 0 and not extra:
             # every 16K gate case gets the sustained-clock reading; the
             # headline's is also reported at the top level
             res[name]["sustained"] = sustained(fn, w.flops(), args.sustain_seconds, PEAK_TFLOPS[dtype])
