@@ -101,8 +101,10 @@ def parse():
     ap.add_argument("--only", default="", help="comma-separated subset of: " + ",".join(ALL_CASES))
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference for HBM byte counters)")
+    ap.add_argument("--protocol-a", action="store_true",
+                    help="only the README configuration cases, timed with the README's kernel-benchmark protocol")
     ap.add_argument("--sustain-seconds", type=float, default=3.0,
-                    help="seconds per timed run of the sustained-clock protocol on the headline case (0: skip)")
+                    help="seconds per timed run of the sustained-clock protocol on each 16K gate case (0: skip)")
     return ap.parse_args()
 
 
@@ -387,6 +389,61 @@ def range_or_merge_case(name, zy, args):
             "shape": f"{Sq} queries at positions {S - Sq}.. over {S} keys, nheads {H}/{Hk}, d {d}, bshd, LSE"}
 
 
+def context_setup(name, zy):
+    """Inputs and the launch of one README-configuration case: (fn, flops)."""
+    import numpy as np
+    import torch
+    dtype, dqk, readme = CONTEXT_CASES[name]
+    S, H = 16384, max(32, 262144 // 16384)
+    rng = np.random.Generator(np.random.PCG64(dqk))
+    dev = torch.device("cuda:0")
+    q, k = (torch.from_numpy(0.1 * rng.standard_normal((1, S, H, dqk), dtype=np.float32)).to(torch.bfloat16).to(dev)
+            for _ in range(2))
+    v = torch.from_numpy(0.1 * rng.standard_normal((1, S, H, 128), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    out = torch.empty((1, S, H, 128), dtype=torch.bfloat16, device=dev)
+    if dtype == "bf16":
+        fn = lambda: zy.zyfa_fwd(q, k, v, out)
+    else:
+        (q8, qs), (k8, ks), (v8, vs) = (zy.zyfa_fp8_quantize(x) for x in (q, k, v))
+        fn = lambda: zy.zyfa_fwd(q8, k8, v8, out, q_descale=qs, k_descale=ks, v_descale=vs)
+    return fn, float(H) * S * S * (dqk + 128)
+
+
+def protocol_a(zy, runs: int = 3, warmup: int = 500, timed: int = 100, idle: float = 5.0):
+    """The README's kernel-benchmark protocol on its own configuration (the
+    CONTEXT_CASES): before each case 5 s idle, then 500 warm-up launches and
+    the mean of 100 timed back-to-back launches (one event pair); three runs
+    with the case order rotated; the median run per case."""
+    import torch
+    names = list(CONTEXT_CASES)
+    setups = {n: context_setup(n, zy) for n in names}
+    per = {n: [] for n in names}
+    for r in range(runs):
+        for n in names[r % len(names):] + names[:r % len(names)]:
+            fn, flops = setups[n]
+            torch.cuda.synchronize()
+            time.sleep(idle)
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            for _ in range(timed):
+                fn()
+            stop.record()
+            torch.cuda.synchronize()
+            per[n].append(flops / (start.elapsed_time(stop) / timed * 1e-3) / 1e12)
+            print(f"protocol A run {r} {n}: {per[n][-1]:.1f} TF/s", file=sys.stderr, flush=True)
+    res = {}
+    for n in names:
+        t = sorted(per[n])[len(per[n]) // 2]
+        readme = CONTEXT_CASES[n][2]
+        res[n] = {"tflops": round(t, 2), "runs": [round(x, 1) for x in per[n]], "readme_mi355x_tflops": readme,
+                  "ratio_to_readme": round(t / readme, 3)}
+    return {"protocol": f"{idle:g} s idle, {warmup} warm-up launches, mean of {timed}, {runs} runs with the order "
+                        f"rotated, median run", "cases": res}
+
+
 def context_case(name, zy, args):
     """The README's benchmark configuration (see CONTEXT_CASES)."""
     import numpy as np
@@ -428,6 +485,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.protocol_a:
+        print(json.dumps({"protocol_a": protocol_a(zy)}), flush=True)
+        return
     cases = args.only.split(",") if args.only else ALL_CASES
     if args.copy_mib:
         # reference for the byte counters: a device-to-device copy of a
