@@ -121,10 +121,10 @@ int zyfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
 /*
  * zyfa_fwd_range - causal attention of a block of queries over a range of
  * keys, returning the partial output and its LSE so that results over
- * different key ranges can be merged ("ZYFA" README, Accuracy: the LSE
- * comes from the same rounded probabilities "so that results computed over
- * different key ranges can be merged consistently"; the flash-attention
- * RDNA3 page's split of the keys with an LSE merge). Uses: chunked prefill
+ * different key ranges can be merged ("ZYFA" README, Accuracy: the FP8 LSE
+ * is computed from the same rounded probabilities as the output, which keeps
+ * merges over key ranges consistent; the flash-attention RDNA3 page's split
+ * of the keys with an LSE merge). Uses: chunked prefill
  * (a chunk of new queries over the cached prefix and itself) and a sequence
  * split over devices.
  *  Query row r sits at absolute position q_pos0 + r, key c at k_pos0 + c;
