@@ -39,9 +39,10 @@
 //    conversion per two scores instead of an exponential and an FP8
 //    conversion).
 //    C = 56 + 8 log2(2 ln^2 2) makes the piecewise-linear value unbiased.
-//    Lean P is used on key tiles that lie wholly before the workgroup's
-//    query tile; the key tiles that overlap the query tile keep exact P, so
-//    the rows with the fewest keys (query tile 0) are exact throughout.
+//    Lean P is used on key tiles that lie wholly before the 256-row block
+//    of query rows that holds the workgroup's query tile; the key tiles that
+//    overlap the block keep exact P, so the rows with the fewest keys (rows
+//    0..255) are exact throughout, at either tile height.
 //    The choice is uniform over the workgroup.
 //  - The row sum is one extra MFMA of the rounded, scaled P against a block
 //    of ones (README, Kernel design: row sum on the matrix unit), so the
@@ -196,10 +197,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // wave has no rows or its rows see no key
       const int lk_w = min(Sk - 1, qw0 + RW - 1 + dl);
       const int kt_w = (qw0 < Sq && lk_w >= 0) ? min(lk_w / kTileK, n_kt - 1) : -1;
-      // key tiles from K0 on reach the diagonal band of this query tile:
-      // exact P and (on the diagonal) the causal mask; tiles before K0, whose
-      // keys every row of the tile sees, take lean P (with LEAN)
-      const int K0 = q0 + dl + 1 > 0 ? (q0 + dl + 1) / kTileK : 0;
+      // key tiles from K0 on reach the diagonal band of the 256-row block
+      // that holds this query tile: exact P and (on the diagonal) the causal
+      // mask; tiles before K0, whose keys every row of the block sees, take
+      // lean P (with LEAN). The block is 256 rows whatever the tile height,
+      // so rows 0..255, which have the fewest keys, are exact throughout and
+      // the rounding does not depend on the tiling.
+      const int qb = q0 & ~255;
+      const int K0 = qb + dl + 1 > 0 ? (qb + dl + 1) / kTileK : 0;
 
       // Q fragments (B operand): lane (g, n) holds q[row n][16g..16g+15] and
       // q[row n][64+16g..]; for d 192 also q[row n][128+8g..+7] and

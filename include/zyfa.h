@@ -92,9 +92,9 @@ int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  *  ZYFA_P_DEFAULT  ZYFA_P_LEAN at d_qk = 128, ZYFA_P_EXACT at d_qk = 192
  *                  (the README's choice per head dim).
  *  ZYFA_P_EXACT    exact P: e4m3fn RNE of exp2 of the base-2 score.
- *  ZYFA_P_LEAN     lean P for keys below the query's own query tile
- *                  (keys j < T floor(i / T) of row i, T the shape's tile
- *                  height: 256, or 128, see zyfa_set_tile_q): the code of 2^y
+ *  ZYFA_P_LEAN     lean P for keys below the query's own 256-row block
+ *                  (keys j < 256 floor(i / 256) of row i, at either query-
+ *                  tile height): the code of 2^y
  *                  is RNE(8 y + 56 + 8 log2(2 ln^2 2)) read as an integer
  *                  (interpolates 2^y linearly between powers of two,
  *                  unbiased on average); keys from that tile on, which

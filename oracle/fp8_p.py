@@ -33,8 +33,8 @@ For query row i (keys j <= i), with x_j = softmax_scale * log2(e) *
      value 2^floor(y) (1 + frac(y)) unbiased: its mean ratio to 2^y over a
      uniform frac(y) is 1 / (2 ln(2)^2));
    - lean P off the diagonal query tile ("lean_offdiag"): the query rows
-     are tiled in query_tile rows (256 by default; 128 for shapes the
-     kernels run on 128-row tiles); keys of the key tiles that hold the rows
+     are grouped in blocks of query_tile rows (256, which the kernels use
+     at every query-tile height); keys of the key tiles that hold the rows
      of row i's own query tile (key tile t >= floor(i / query_tile) *
      query_tile / KEY_TILE) get exact P, which covers every key of the rows
      with the fewest keys; the key tiles before them get lean P. (Which tiles keep exact P is this

@@ -116,6 +116,26 @@ def test_small_shapes(B, S, H, Hk, dqk, layout, tile_q):
         run_case(w, with_lse=True)
 
 
+@pytest.mark.parametrize("dqk", [128, 192])
+@pytest.mark.parametrize("p_mode", ["default", "lean"])
+def test_tile_heights_agree_bitwise(dqk, p_mode):
+    # which keys take lean P is fixed per 256-row block of query rows, and
+    # every row visits its key tiles in the same order, so the two query-tile
+    # heights give the same bits
+    B, S, H, Hk = 2, 1152, 8, 2
+    w = Workload("tiles_fp8", B, S, H, Hk, dqk, 128, "bhsd", ("fp8",), True, False, 6100 + dqk)
+    print(f"case fp8 tile heights B{B} S{S} H{H}/{Hk} d{dqk} {p_mode}", flush=True)
+    q, k, v = generate(w)
+    (q8, qs, _), (k8, ks, _), (v8, vs, _) = quantize_both(q), quantize_both(k), quantize_both(v)
+    res = []
+    for tq in (256, 128):
+        with tile_height(zy, B, S, H, Hk, dqk, zy.DTYPE_FP8, tq):
+            res.append(zy.zyfa_fwd(q8, k8, v8, layout="bhsd", return_lse=True, q_descale=qs, k_descale=ks,
+                                   v_descale=vs, p_mode=p_mode))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
 @pytest.mark.parametrize("p_mode", ["exact", "lean"])
 @pytest.mark.parametrize("dqk", [128, 192])
 def test_modes_meet_the_gate(p_mode, dqk):
@@ -145,7 +165,7 @@ def test_rounding_matches_fp8_oracle(p_mode, B, S, H, Hk, dqk, layout, tile_q):
     for b in range(B):
         for h in range(H):
             ro, rl = oracle.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=layout,
-                                                   p_mode=oracle_p_mode(p_mode, dqk), query_tile=tile_q)
+                                                   p_mode=oracle_p_mode(p_mode, dqk))
             gots.append(o[b, :, h] if layout == "bshd" else o[b, h])
             glse.append(l[b, h])
             refs.append(ro)
@@ -177,9 +197,6 @@ def test_one_gpu_share_of_workload3():
 
 
 def _full_size_sampled_rows(w, wid):
-    # query-tile height the library picks for this shape (it sets which key
-    # tiles take lean P)
-    tq = zy.zyfa_plan_jobs(w.batch, w.seqlen, w.nheads, w.nheads_k, w.d_qk, zy.DTYPE_FP8)[0]
     q, k, v = generate(w)
     print(f"case full fp8 {w.name}", flush=True)
     (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
@@ -197,7 +214,7 @@ def _full_size_sampled_rows(w, wid):
             refs.append(ro)
             if not w.activation_like:
                 rr, _ = oracle.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout,
-                                                      p_mode=oracle_p_mode("default", w.d_qk), query_tile=tq)
+                                                      p_mode=oracle_p_mode("default", w.d_qk))
                 rrefs.append(rr)
             hk = h // (w.nheads // w.nheads_k)
             extras.append(fp8_score_allowance(hv(rq)[b, h], hv(rk)[b, hk], hv(rv)[b, hk], w.softmax_scale, rows)
