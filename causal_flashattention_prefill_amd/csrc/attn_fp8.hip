@@ -202,9 +202,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // mask; tiles before K0, whose keys every row of the block sees, take
       // lean P (with LEAN). The block is 256 rows whatever the tile height,
       // so rows 0..255, which have the fewest keys, are exact throughout and
-      // the rounding does not depend on the tiling.
+      // the rounding does not depend on the tiling; in a call over a range
+      // of keys, a block whose first row sees fewer than 256 keys is exact
+      // throughout as well.
       const int qb = q0 & ~255;
-      const int K0 = qb + dl + 1 > 0 ? (qb + dl + 1) / kTileK : 0;
+      const int K0 = qb + dl + 1 >= 256 ? (qb + dl + 1) / kTileK : 0;
 
       // Q fragments (B operand): lane (g, n) holds q[row n][16g..16g+15] and
       // q[row n][64+16g..]; for d 192 also q[row n][128+8g..+7] and

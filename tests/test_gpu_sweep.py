@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from workloads import Workload, generate
-from parity import bf16_pair, check_bf16, check_fp8, out_to_f64, tile_height
+from parity import bf16_pair, check_bf16, check_fp8, check_partial, out_to_f64, tile_height
 
 pytestmark = pytest.mark.gpu
 
@@ -64,3 +64,60 @@ def test_random_shape(B, S, H, Hk, dqk, layout, dtype, lse, tq):
         if lse:
             dl = np.abs(got_lse.cpu().numpy() - ref_lse)
             assert np.all(np.isfinite(dl)) and dl.max() < 0.065, f"max|dLSE|={dl.max():.3e}"
+
+
+def _draw_range_case(i):
+    rng = np.random.default_rng(9500 + i)
+    B = int(rng.integers(1, 3))
+    Sq = int(rng.integers(1, 900))
+    Sk = int(rng.integers(1, 1500))
+    # query and key positions: keys before, around or after the queries
+    q_pos0 = int(rng.integers(0, 2000))
+    k_pos0 = int(rng.integers(0, 2000)) if rng.random() < 0.3 else int(rng.integers(0, max(1, q_pos0 + 1)))
+    Hk = int(rng.choice([1, 2]))
+    H = Hk * int(rng.choice([1, 2, 3]))
+    dqk = int(rng.choice([128, 192]))
+    layout = str(rng.choice(["bshd", "bhsd"]))
+    dtype = str(rng.choice(["bf16", "fp8"]))
+    tq = int(rng.choice([128, 256]))
+    return B, Sq, Sk, q_pos0, k_pos0, H, Hk, dqk, layout, dtype, tq
+
+
+RANGE_CASES = [_draw_range_case(i) for i in range(32)]
+
+
+@pytest.mark.parametrize("B,Sq,Sk,qp,kp,H,Hk,dqk,layout,dtype,tq", RANGE_CASES)
+def test_random_range(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, dtype, tq):
+    print(f"case sweep range {dtype} B{B} Sq{Sq} Sk{Sk} q_pos0={qp} k_pos0={kp} H{H}/{Hk} d{dqk} {layout} "
+          f"tile_q {tq}", flush=True)
+    rng = np.random.Generator(np.random.PCG64(7000 + Sq + Sk + qp))
+    shp = lambda s, h, d: (B, s, h, d) if layout == "bshd" else (B, h, s, d)
+    q = rng.standard_normal(shp(Sq, H, dqk), dtype=np.float32)
+    k = rng.standard_normal(shp(Sk, Hk, dqk), dtype=np.float32)
+    v = rng.standard_normal(shp(Sk, Hk, 128), dtype=np.float32)
+    pairs = [bf16_pair(x) for x in (q, k, v)]
+    zdt = zy.DTYPE_BF16 if dtype == "bf16" else zy.DTYPE_FP8
+    with tile_height(zy, B, Sq, H, Hk, dqk, zdt, tq):
+        if dtype == "bf16":
+            (tq_, rq), (tk, rk), (tv, rv) = pairs
+            out, lse = zy.zyfa_fwd_range(tq_, tk, tv, qp, kp, layout=layout)
+        else:
+            dev, deq = [], []
+            for t, r in pairs:
+                x8, ds = zy.zyfa_fp8_quantize(t)
+                codes, d = oracle.fp8_quantize_ref(r)
+                dev.append((x8, ds))
+                deq.append(oracle.e4m3fn_decode(codes) * float(d))
+            (q8, qs), (k8, ks), (v8, vs) = dev
+            rq, rk, rv = deq
+            out, lse = zy.zyfa_fwd_range(q8, k8, v8, qp, kp, layout=layout, q_descale=qs, k_descale=ks,
+                                         v_descale=vs)
+        torch.cuda.synchronize()
+    ro, rl = oracle.range_attention_ref(rq, rk, rv, qp, kp, layout=layout)
+    rows = lambda x: np.swapaxes(x, 1, 2) if layout == "bshd" else x
+    got_l = rows(lse.cpu().numpy().astype(np.float64))
+    if dtype == "bf16":
+        check_partial(out_to_f64(out), ro, got_l, rows(rl), f"sweep range bf16 Sq{Sq} Sk{Sk}")
+    else:
+        assert np.array_equal(np.isneginf(got_l), np.isneginf(rows(rl)))
+        check_partial(out_to_f64(out), ro, None, rows(rl), f"sweep range fp8 Sq{Sq} Sk{Sk}", fp8=True)
