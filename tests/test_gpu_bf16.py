@@ -72,6 +72,17 @@ def test_small_shapes(B, S, H, Hk, dqk, layout, with_lse, tile_q):
         run_case(w, with_lse=with_lse)
 
 
+@pytest.mark.parametrize("tile_q", [128, 256])
+def test_several_rounds_of_jobs(tile_q):
+    # 512 pair jobs of 128-row tiles (256 of 256-row tiles): the persistent
+    # workgroups take two jobs each at the lower height
+    B, S, H, Hk = 2, 4096, 16, 4
+    w = Workload("rounds", B, S, H, Hk, 128, 128, "bshd", ("bf16",), True, False, 4242)
+    print(f"tile_q {tile_q}", flush=True)
+    with tile_height(zy, B, S, H, Hk, 128, zy.DTYPE_BF16, tile_q):
+        run_case(w, with_lse=True, heads=[0, 5, 15])
+
+
 def test_no_lse_variant_workload1():
     # without LSE the kernel divides by the matrix-unit sum of the rounded P
     run_case(WORKLOADS[1], with_lse=False)

@@ -118,12 +118,13 @@ def test_small_shapes(B, S, H, Hk, dqk, layout, tile_q):
 
 @pytest.mark.parametrize("dqk", [128, 192])
 @pytest.mark.parametrize("p_mode", ["default", "lean"])
-def test_tile_heights_agree_bitwise(dqk, p_mode):
+@pytest.mark.parametrize("B,S,H,Hk", [(2, 1152, 8, 2), (2, 4096, 16, 4)])
+def test_tile_heights_agree_bitwise(B, S, H, Hk, dqk, p_mode):
     # which keys take lean P is fixed per 256-row block of query rows, and
     # every row visits its key tiles in the same order, so the two query-tile
-    # heights give the same bits
-    B, S, H, Hk = 2, 1152, 8, 2
-    w = Workload("tiles_fp8", B, S, H, Hk, dqk, 128, "bhsd", ("fp8",), True, False, 6100 + dqk)
+    # heights give the same bits. The second shape has 512 pair jobs of
+    # 128-row tiles: two rounds of the persistent grid.
+    w = Workload("tiles_fp8", B, S, H, Hk, dqk, 128, "bhsd", ("fp8",), True, False, 6100 + dqk + S)
     print(f"case fp8 tile heights B{B} S{S} H{H}/{Hk} d{dqk} {p_mode}", flush=True)
     q, k, v = generate(w)
     (q8, qs, _), (k8, ks, _), (v8, vs, _) = quantize_both(q), quantize_both(k), quantize_both(v)
