@@ -113,9 +113,10 @@ def _synthetic_partials(B, S, H, layout, seed, empty_frac=0.1):
 
 @pytest.mark.parametrize("layout", ["bshd", "bhsd"])
 @pytest.mark.parametrize("inplace", [False, True])
-def test_merge_kernel_matches_oracle(layout, inplace):
-    B, S, H = 2, 333, 3
-    print(f"case merge {layout} inplace={inplace}", flush=True)
+@pytest.mark.parametrize("B,S,H", [(2, 333, 3)] + [tuple(int(x) for x in np.random.default_rng(40 + i).integers(
+    [1, 1, 1], [4, 2000, 40])) for i in range(6)])
+def test_merge_kernel_matches_oracle(layout, inplace, B, S, H):
+    print(f"case merge {layout} inplace={inplace} B{B} S{S} H{H}", flush=True)
     oa, la, ob, lb = _synthetic_partials(B, S, H, layout, 21)
     (toa, roa), (tob, rob) = bf16_pair(oa), bf16_pair(ob)
     tla, tlb = torch.from_numpy(la).cuda(), torch.from_numpy(lb).cuda()
