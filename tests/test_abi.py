@@ -74,9 +74,18 @@ def test_prepare_argument_errors():
     assert L.zyfa_prepare(1, 128, 4, 4, 96, 128, 0, 0, 0, None) == zy.STATUS["ZYFA_ERR_HEADDIM"]
 
 
+def _random_shapes(n):
+    rng = np.random.default_rng(77)
+    out = []
+    for _ in range(n):
+        hk = int(rng.integers(1, 9))
+        out.append((int(rng.integers(1, 5)), int(rng.integers(1, 40000)), hk * int(rng.integers(1, 9)), hk))
+    return out
+
+
 @pytest.mark.parametrize("B,S,H,Hk", [(1, 256, 4, 4), (1, 8192, 32, 8), (1, 16384, 32, 8), (1, 16384, 16, 16),
                                       (2, 32000, 32, 8), (3, 1000, 6, 2), (1, 1, 1, 1), (1, 300, 2, 1),
-                                      (1, 16384, 4, 1)])
+                                      (1, 16384, 4, 1)] + _random_shapes(24))
 def test_job_table_covers_every_tile_once(B, S, H, Hk):
     tq, nw, jp, table = zy.zyfa_plan_jobs(B, S, H, Hk)
     n = -(-S // tq)
