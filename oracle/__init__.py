@@ -11,9 +11,8 @@ arithmetic (the bf16 and e4m3fn codecs, the power-of-two quantizer).
 Sources (cited by page title and section):
 - "ZYFA" README (GitHub page of Zyphra/zyfa): Usage (LSE, descales,
   padding), Supported configurations (formats, head dims, GQA), Accuracy
-  (fp64 attention on the same quantized inputs), Kernel design (rounding;
-  lazy rescaling, per-block scaling, lean P and the row sum for the FP8
-  probability rounding in fp8_p.py).
+  (fp64 attention on the same quantized inputs), Kernel design (every
+  conversion rounds to nearest even).
 - flash-attention RDNA3 extension page, kernel notes (partial results over
   key splits merged by an LSE reduction), with the README's Accuracy note on
   merging results over key ranges: partial.py.
@@ -27,7 +26,6 @@ from .codecs import (bf16_round, bf16_decode, bf16_encode_bits, e4m3fn_decode,
                      e4m3fn_encode, E4M3FN_MAX)
 from .quantize import fp8_quantize_ref
 from .attention import causal_attention_ref, causal_probs_ref, causal_attention_rows_ref
-from .fp8_p import fp8_attention_rows_ref
 from .partial import range_attention_ref, range_attention_rows_ref, lse_merge_ref, lse_merge_layout_ref
 from .rotation import (hadamard, dct2_ortho, rotation_matrix, rotate_ref, quantize_rotated_ref, key_mean_ref,
                        quantize_shifted_rotated_ref)
@@ -35,7 +33,7 @@ from .rotation import (hadamard, dct2_ortho, rotation_matrix, rotate_ref, quanti
 __all__ = [
     "bf16_round", "bf16_decode", "bf16_encode_bits", "e4m3fn_decode", "e4m3fn_encode",
     "E4M3FN_MAX", "fp8_quantize_ref", "causal_attention_ref", "causal_probs_ref",
-    "causal_attention_rows_ref", "fp8_attention_rows_ref", "range_attention_ref",
+    "causal_attention_rows_ref", "range_attention_ref",
     "range_attention_rows_ref", "lse_merge_ref", "lse_merge_layout_ref", "hadamard", "dct2_ortho",
     "rotation_matrix", "rotate_ref", "quantize_rotated_ref", "key_mean_ref", "quantize_shifted_rotated_ref",
 ]

@@ -1,15 +1,20 @@
-"""FP8 attention with the probabilities rounded as the FP8 kernels round them
-(oracle, float64; test infrastructure only).
+"""Model of this library's FP8 probability rounding (float64; a regression
+check of the FP8 kernels, not an oracle).
 
-The plain definition in attention.py is exact softmax attention on the
-dequantized inputs; an FP8 kernel instead multiplies V by e4m3fn-rounded
-probabilities and divides by the sum of the same rounded values. This module
-writes out which rounded values those are, following the "ZYFA" README's
-Kernel design section (lazy rescaling; per-block scaling; lean P; row sum on
-the matrix unit) and its Accuracy section (the output is a weighted average
-whose weights are the rounded probabilities, and the LSE comes from them).
-It is used to check the GPU path tightly; the accuracy gate itself compares
-against attention.py.
+The oracle (oracle/attention.py) is exact softmax attention on the
+dequantized inputs, and every FP8 accuracy claim is made against it. An FP8
+kernel instead multiplies V by e4m3fn-rounded probabilities and divides by
+the sum of the same rounded values. This module writes out which rounded
+values THIS library's kernels use, so a GPU result can be checked far more
+tightly than the accuracy gate allows. Its constants are the kernels'
+choices, not the pages': 128-key tiles, 32-key scale blocks (the scaled
+MFMA's block; the "ZYFA" README uses 64 keys), a lazy-rescale threshold of
+8 base-2 units (the README names 0.125 in FP8) and exact P on the key tiles
+of a 256-row query block (the README uses lean P throughout at d = 128).
+It follows the README's Kernel design section for the steps themselves
+(lazy rescaling; per-block scaling; lean P; row sum on the matrix unit) and
+its Accuracy section (the output is a weighted average whose weights are the
+rounded probabilities, and the LSE comes from them).
 
 For query row i (keys j <= i), with x_j = softmax_scale * log2(e) *
 <q_i, k_j> the score in base-2 units:
@@ -53,8 +58,8 @@ from typing import Optional
 
 import numpy as np
 
-from .attention import _split, kv_head
-from .codecs import e4m3fn_decode, e4m3fn_encode
+from oracle.attention import _split, kv_head
+from oracle.codecs import e4m3fn_decode, e4m3fn_encode
 
 KEY_TILE = 128
 QUERY_TILE = 256

@@ -1,7 +1,8 @@
-"""Pins of the FP8 probability-rounding oracle (oracle/fp8_p.py), CPU only.
+"""Pins of the FP8 probability-rounding model (tests/fp8_rounding_model.py),
+CPU only.
 
 Each check rests on something other than the oracle itself: hand-computed
-e4m3fn weights (tests/golden/fp8_p_worked.txt), the exact softmax definition
+e4m3fn weights (tests/golden/fp8_rounding_worked.txt), the exact softmax definition
 in the cases where rounding is exact (integer base-2 scores), closed forms of
 weighted averages, and the mean of the piecewise-linear 2^y.
 """
@@ -12,7 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import causal_attention_rows_ref, e4m3fn_decode
-from oracle import fp8_p
+import fp8_rounding_model as fp8_p
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 LN2 = math.log(2.0)
@@ -20,7 +21,7 @@ LN2 = math.log(2.0)
 
 def _worked():
     rows = []
-    with open(os.path.join(GOLD, "fp8_p_worked.txt")) as f:
+    with open(os.path.join(GOLD, "fp8_rounding_worked.txt")) as f:
         for line in f:
             if line.startswith("#") or not line.strip():
                 continue

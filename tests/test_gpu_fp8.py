@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import fp8_rounding_model
 from workloads import WORKLOADS, Workload, generate
 from parity import bf16_pair, check_fp8, check_fp8_rounding, fp8_score_allowance, out_to_f64, tile_height
 
@@ -165,7 +166,7 @@ def test_rounding_matches_fp8_oracle(p_mode, B, S, H, Hk, dqk, layout, tile_q):
     gots, glse, refs, rlse = [], [], [], []
     for b in range(B):
         for h in range(H):
-            ro, rl = oracle.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=layout,
+            ro, rl = fp8_rounding_model.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=layout,
                                                    p_mode=oracle_p_mode(p_mode, dqk))
             gots.append(o[b, :, h] if layout == "bshd" else o[b, h])
             glse.append(l[b, h])
@@ -214,7 +215,7 @@ def _full_size_sampled_rows(w, wid):
             gots.append(o[b, rows, h] if w.layout == "bshd" else o[b, h, rows])
             refs.append(ro)
             if not w.activation_like:
-                rr, _ = oracle.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout,
+                rr, _ = fp8_rounding_model.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout,
                                                       p_mode=oracle_p_mode("default", w.d_qk))
                 rrefs.append(rr)
             hk = h // (w.nheads // w.nheads_k)
