@@ -35,14 +35,9 @@ struct Plan {
   int tile_q = 0;
 };
 
-struct DeviceScratch {
-  unsigned* amax = nullptr;  // partial maxima of the FP8 quantizer
-};
-
 std::mutex g_mu;
 std::map<PlanKey, Plan> g_plans;
 std::map<PlanKey, int> g_tile_choice;   // query-tile heights set by zyfa_set_tile_q
-std::map<int, DeviceScratch> g_scratch;
 std::map<int, int> g_num_cus;
 
 int current_device(int* dev) {
@@ -216,20 +211,8 @@ int quantize_rotated_impl(const void* x, int x_dtype, long long rows, int d, con
   if (rows > 0 && (!aligned16(x) || !aligned16(x8))) return ZYFA_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(descale) & 3u) return ZYFA_ERR_ALIGN;
   if (shift && !aligned16(shift)) return ZYFA_ERR_ALIGN;
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  int dev, rc;
-  if ((rc = current_device(&dev))) return rc;
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceScratch& sc = g_scratch[dev];
-  if (!sc.amax) {
-    if (stream_capturing(stream)) return ZYFA_ERR_CAPTURE;
-    if (hipMalloc(&sc.amax, sizeof(unsigned) * quantize_scratch_slots()) != hipSuccess) {
-      sc.amax = nullptr;
-      return ZYFA_ERR_HIP;
-    }
-  }
   hipError_t e = launch_fp8_quantize_rotated(x, x_dtype == ZYFA_DTYPE_BF16 ? 0 : 2, rows, d, mask, shift, seqlen,
-                                             nheads, bshd, x8, descale, sc.amax, quantize_scratch_slots(), stream);
+                                             nheads, bshd, x8, descale, reinterpret_cast<hipStream_t>(stream_));
   return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
 }
 
@@ -305,20 +288,8 @@ int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, flo
   if (!descale || (numel > 0 && (!x || !x8))) return ZYFA_ERR_NULL;
   if (numel > 0 && (!aligned16(x) || !aligned16(x8))) return ZYFA_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(descale) & 3u) return ZYFA_ERR_ALIGN;
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  int dev, rc;
-  if ((rc = current_device(&dev))) return rc;
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceScratch& sc = g_scratch[dev];
-  if (!sc.amax) {
-    if (stream_capturing(stream)) return ZYFA_ERR_CAPTURE;
-    if (hipMalloc(&sc.amax, sizeof(unsigned) * quantize_scratch_slots()) != hipSuccess) {
-      sc.amax = nullptr;
-      return ZYFA_ERR_HIP;
-    }
-  }
-  hipError_t e = launch_fp8_quantize(x, x_dtype == ZYFA_DTYPE_BF16 ? 0 : 2, numel, x8, descale, sc.amax,
-                                     quantize_scratch_slots(), stream);
+  hipError_t e = launch_fp8_quantize(x, x_dtype == ZYFA_DTYPE_BF16 ? 0 : 2, numel, x8, descale,
+                                     reinterpret_cast<hipStream_t>(stream_));
   return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
 }
 
@@ -383,11 +354,6 @@ void zyfa_release(void) {
     (void)hipFree(kv.second.jobs);
   }
   g_plans.clear();
-  for (auto& kv : g_scratch) {
-    (void)hipSetDevice(kv.first);
-    if (kv.second.amax) (void)hipFree(kv.second.amax);
-  }
-  g_scratch.clear();
   (void)hipSetDevice(cur);
 }
 

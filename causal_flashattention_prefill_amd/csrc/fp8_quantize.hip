@@ -13,6 +13,11 @@
 //  2. amax_final: one block reduces the partials and writes the descale.
 //  3. convert: x * (1/d) is exact (d is a power of two), then
 //     v_cvt_pk_fp8_f32 rounds to nearest even.
+// The partial maxima are kept in the first bytes of the call's own output
+// x8 (at most one 4-byte partial per 4 output bytes), which step 3 then
+// overwrites: a call touches no memory but its own arguments, so calls on
+// different streams, or in parallel branches of a graph, cannot interfere.
+// A grid of one block (small tensors) writes the descale in step 1.
 #include "device_common.h"
 #include "zyfa_internal.h"
 
@@ -39,9 +44,32 @@ __device__ __forceinline__ unsigned block_max_u32(unsigned v, unsigned* red) {
   return r;  // valid in thread 0
 }
 
+// descale = smallest power of two d >= 2^-126 with amax <= 448 * d.
+// With amax = m * 2^E (1 <= m < 2): 448 = 1.75 * 2^8, so
+// amax <= 448 * 2^e  <=>  e >= E - 8 when m <= 1.75, else e >= E - 7.
+__device__ __forceinline__ float pow2_descale_from_bits(unsigned amax_bits) {
+  if (amax_bits == 0) return 1.0f;
+  int E;
+  unsigned mant;
+  const unsigned ef = amax_bits >> 23;
+  if (ef == 0) {  // subnormal amax: normalise
+    const int lz = __clz(amax_bits) - 8;     // leading zeros within the 23-bit field + 1
+    E = -126 - lz;
+    mant = (amax_bits << lz) & 0x7FFFFFu;
+  } else {
+    E = (int)ef - 127;
+    mant = amax_bits & 0x7FFFFFu;
+  }
+  int e = E - 8 + (mant > 0x600000u ? 1 : 0);  // 0x600000: mantissa field of 1.75
+  if (e < -126) e = -126;
+  return __builtin_bit_cast(float, (unsigned)(e + 127) << 23);
+}
+
 // x_dtype 0: bf16 (8 values per 16 bytes), 2: fp32 (4 values per 16 bytes).
-template <int XDT>
-__global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const void* x, long long numel, unsigned* partial) {
+// FINAL: a grid of one block, which writes the descale itself.
+template <int XDT, bool FINAL>
+__global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const void* x, long long numel, unsigned* partial,
+                                                                 float* descale) {
   __shared__ unsigned red[kQThreads / 64];
   constexpr int PER = XDT == 0 ? 8 : 4;
   const long long nvec = numel / PER;
@@ -68,28 +96,10 @@ __global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const void* x, 
     }
   }
   const unsigned r = block_max_u32(m, red);
-  if (threadIdx.x == 0) partial[blockIdx.x] = r;
-}
-
-// descale = smallest power of two d >= 2^-126 with amax <= 448 * d.
-// With amax = m * 2^E (1 <= m < 2): 448 = 1.75 * 2^8, so
-// amax <= 448 * 2^e  <=>  e >= E - 8 when m <= 1.75, else e >= E - 7.
-__device__ __forceinline__ float pow2_descale_from_bits(unsigned amax_bits) {
-  if (amax_bits == 0) return 1.0f;
-  int E;
-  unsigned mant;
-  const unsigned ef = amax_bits >> 23;
-  if (ef == 0) {  // subnormal amax: normalise
-    const int lz = __clz(amax_bits) - 8;     // leading zeros within the 23-bit field + 1
-    E = -126 - lz;
-    mant = (amax_bits << lz) & 0x7FFFFFu;
-  } else {
-    E = (int)ef - 127;
-    mant = amax_bits & 0x7FFFFFu;
+  if (threadIdx.x == 0) {
+    if (FINAL) *descale = pow2_descale_from_bits(r);
+    else partial[blockIdx.x] = r;
   }
-  int e = E - 8 + (mant > 0x600000u ? 1 : 0);  // 0x600000: mantissa field of 1.75
-  if (e < -126) e = -126;
-  return __builtin_bit_cast(float, (unsigned)(e + 127) << 23);
 }
 
 __global__ __launch_bounds__(kQThreads) void amax_final_kernel(const unsigned* partial, int np, float* descale) {
@@ -318,9 +328,9 @@ __device__ __forceinline__ void subtract_shift(float (&y)[Rot<D>::V], long long 
   for (int t = 0; t < Rot<D>::V; ++t) y[t] -= sv[t];
 }
 
-template <int D, int XDT, bool SHIFT>
+template <int D, int XDT, bool SHIFT, bool FINAL>
 __global__ __launch_bounds__(kQThreads) void rot_amax_kernel(const void* x, long long rows, SignMask sm, ShiftDesc sd,
-                                                             unsigned* partial) {
+                                                             unsigned* partial, float* descale) {
   __shared__ unsigned red[kQThreads / 64];
   const int hl = threadIdx.x & 31;
   unsigned sg[Rot<D>::V];
@@ -343,7 +353,10 @@ __global__ __launch_bounds__(kQThreads) void rot_amax_kernel(const void* x, long
     }
   }
   const unsigned r = block_max_u32(m, red);
-  if (threadIdx.x == 0) partial[blockIdx.x] = r;
+  if (threadIdx.x == 0) {
+    if (FINAL) *descale = pow2_descale_from_bits(r);
+    else partial[blockIdx.x] = r;
+  }
 }
 
 template <int D, int XDT, bool SHIFT>
@@ -383,18 +396,32 @@ __global__ __launch_bounds__(kQThreads) void rot_convert_kernel(const void* x, l
   }
 }
 
+// Number of amax partials: one per block, capped so that they fit in the
+// first bytes of the output (4 bytes each) and at kMaxPartials.
+long long partial_blocks(long long want, long long out_bytes) {
+  long long b = want < 1 ? 1 : want;
+  if (b > out_bytes / 4) b = out_bytes / 4;
+  if (b > kMaxPartials) b = kMaxPartials;
+  return b < 1 ? 1 : b;
+}
+
 template <int D, int XDT, bool SHIFT>
 hipError_t launch_rot(const void* x, long long rows, const SignMask& sm, const ShiftDesc& sd, void* x8,
-                      float* descale, unsigned* scratch_amax, int scratch_slots, hipStream_t s) {
+                      float* descale, hipStream_t s) {
   constexpr int kRowsPerBlock = kQThreads / 32 * kRotRows;
-  long long want = (rows + kRowsPerBlock * 2 - 1) / (kRowsPerBlock * 2);
-  const int blocks = (int)(want < 1 ? 1 : (want > scratch_slots ? scratch_slots : want));
-  hipLaunchKernelGGL((rot_amax_kernel<D, XDT, SHIFT>), dim3(blocks), dim3(kQThreads), 0, s, x, rows, sm, sd,
-                     scratch_amax);
+  const int blocks = (int)partial_blocks((rows + kRowsPerBlock * 2 - 1) / (kRowsPerBlock * 2), rows * D);
+  unsigned* partial = reinterpret_cast<unsigned*>(x8);
+  if (blocks == 1) {
+    hipLaunchKernelGGL((rot_amax_kernel<D, XDT, SHIFT, true>), dim3(1), dim3(kQThreads), 0, s, x, rows, sm, sd,
+                       partial, descale);
+  } else {
+    hipLaunchKernelGGL((rot_amax_kernel<D, XDT, SHIFT, false>), dim3(blocks), dim3(kQThreads), 0, s, x, rows, sm,
+                       sd, partial, descale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(kQThreads), 0, s, partial, blocks, descale);
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(kQThreads), 0, s, scratch_amax, blocks, descale);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   long long cw = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int cblocks = (int)(cw < 1 ? 1 : (cw > 8192 ? 8192 : cw));
@@ -405,9 +432,9 @@ hipError_t launch_rot(const void* x, long long rows, const SignMask& sm, const S
 
 template <int D, bool SHIFT>
 hipError_t launch_rot_dt(const void* x, int x_dtype, long long rows, const SignMask& sm, const ShiftDesc& sd,
-                         void* x8, float* descale, unsigned* scratch_amax, int scratch_slots, hipStream_t s) {
-  return x_dtype == 0 ? launch_rot<D, 0, SHIFT>(x, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s)
-                      : launch_rot<D, 2, SHIFT>(x, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s);
+                         void* x8, float* descale, hipStream_t s) {
+  return x_dtype == 0 ? launch_rot<D, 0, SHIFT>(x, rows, sm, sd, x8, descale, s)
+                      : launch_rot<D, 2, SHIFT>(x, rows, sm, sd, x8, descale, s);
 }
 
 // ---- Mean over positions of each (batch, head), for K smoothing: one
@@ -465,19 +492,17 @@ __global__ __launch_bounds__(kMeanThreads) void key_mean_kernel(const void* x, i
 
 }  // namespace
 
-int quantize_scratch_slots() { return kMaxPartials; }
-
 hipError_t launch_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const unsigned* sign_mask,
                                        const float* shift, int seqlen, int nheads, bool bshd, void* x8,
-                                       float* descale, unsigned* scratch_amax, int scratch_slots, hipStream_t s) {
+                                       float* descale, hipStream_t s) {
   SignMask sm;
   for (int i = 0; i < 6; ++i) sm.w[i] = sign_mask[i];
   const ShiftDesc sd{shift, (unsigned)seqlen, (unsigned)nheads, bshd};
   if (d == 128)
-    return shift ? launch_rot_dt<128, true>(x, x_dtype, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s)
-                 : launch_rot_dt<128, false>(x, x_dtype, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s);
-  return shift ? launch_rot_dt<192, true>(x, x_dtype, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s)
-               : launch_rot_dt<192, false>(x, x_dtype, rows, sm, sd, x8, descale, scratch_amax, scratch_slots, s);
+    return shift ? launch_rot_dt<128, true>(x, x_dtype, rows, sm, sd, x8, descale, s)
+                 : launch_rot_dt<128, false>(x, x_dtype, rows, sm, sd, x8, descale, s);
+  return shift ? launch_rot_dt<192, true>(x, x_dtype, rows, sm, sd, x8, descale, s)
+               : launch_rot_dt<192, false>(x, x_dtype, rows, sm, sd, x8, descale, s);
 }
 
 hipError_t launch_key_mean(const void* x, int x_dtype, int batch, int seqlen, int nheads, int d, bool bshd,
@@ -494,19 +519,28 @@ hipError_t launch_key_mean(const void* x, int x_dtype, int batch, int seqlen, in
 }
 
 hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
-                               unsigned* scratch_amax, int scratch_slots, hipStream_t s) {
+                               hipStream_t s) {
   const int per = x_dtype == 0 ? 8 : 4;
   const long long nvec = numel / per;
-  long long want = (nvec + kQThreads * 4 - 1) / (kQThreads * 4);
-  int blocks = (int)(want < 1 ? 1 : (want > scratch_slots ? scratch_slots : want));
-  if (x_dtype == 0)
-    hipLaunchKernelGGL(amax_partial_kernel<0>, dim3(blocks), dim3(kQThreads), 0, s, x, numel, scratch_amax);
-  else
-    hipLaunchKernelGGL(amax_partial_kernel<2>, dim3(blocks), dim3(kQThreads), 0, s, x, numel, scratch_amax);
+  const int blocks = (int)partial_blocks((nvec + kQThreads * 4 - 1) / (kQThreads * 4), numel);
+  unsigned* partial = reinterpret_cast<unsigned*>(x8);
+  if (blocks == 1) {
+    if (x_dtype == 0)
+      hipLaunchKernelGGL((amax_partial_kernel<0, true>), dim3(1), dim3(kQThreads), 0, s, x, numel, partial, descale);
+    else
+      hipLaunchKernelGGL((amax_partial_kernel<2, true>), dim3(1), dim3(kQThreads), 0, s, x, numel, partial, descale);
+  } else {
+    if (x_dtype == 0)
+      hipLaunchKernelGGL((amax_partial_kernel<0, false>), dim3(blocks), dim3(kQThreads), 0, s, x, numel, partial,
+                         descale);
+    else
+      hipLaunchKernelGGL((amax_partial_kernel<2, false>), dim3(blocks), dim3(kQThreads), 0, s, x, numel, partial,
+                         descale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(kQThreads), 0, s, partial, blocks, descale);
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(kQThreads), 0, s, scratch_amax, blocks, descale);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   long long cw = (nvec + kQThreads - 1) / kQThreads;
   int cblocks = (int)(cw < 1 ? 1 : (cw > 8192 ? 8192 : cw));

@@ -35,16 +35,16 @@ struct AttnArgs {
 hipError_t launch_attn_bf16(const AttnArgs& a, int d_qk, bool with_lse, int tile_q, int grid, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean, int tile_q, int grid,
                            hipStream_t s);
+// x8 doubles as the scratch of the amax partials (overwritten by the codes)
 hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
-                               unsigned* scratch_amax, int scratch_slots, hipStream_t s);
-int quantize_scratch_slots();
+                               hipStream_t s);
 // sign_mask: six words, bit i set when channel i's sign is -1
 // shift: null, or a device vector per (batch, head) slot subtracted from
 // each row before the rotation (rows in the tensor's memory order, seqlen
 // positions and nheads heads per batch, bshd or bhsd)
 hipError_t launch_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const unsigned* sign_mask,
                                        const float* shift, int seqlen, int nheads, bool bshd, void* x8,
-                                       float* descale, unsigned* scratch_amax, int scratch_slots, hipStream_t s);
+                                       float* descale, hipStream_t s);
 hipError_t launch_key_mean(const void* x, int x_dtype, int batch, int seqlen, int nheads, int d, bool bshd,
                            float* mean, hipStream_t s);
 hipError_t launch_lse_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,

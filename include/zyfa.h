@@ -207,7 +207,10 @@ int zyfa_set_tile_q(int batch, int seqlen, int nheads, int nheads_k, int d_qk, i
  *  descale device pointer to one fp32 (caller-owned); written on device, the
  *          host never reads it.
  *  numel == 0 writes descale = 1. Deterministic: the result does not depend
- *  on timing.
+ *  on timing. x8 also holds the partial maxima between the passes (they are
+ *  overwritten by the codes), so a call reads and writes nothing but its own
+ *  arguments and calls on different streams do not interfere; x8 must not
+ *  overlap x. Allocates nothing.
  */
 int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
                       void* stream);
@@ -235,8 +238,9 @@ int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, flo
  *          otherwise), or NULL for all +1. Read during the call only.
  *  x8      device pointer, rows * d bytes; descale: device pointer to one
  *          fp32. Both caller-owned, written on the device.
- *  Asynchronous on `stream`; deterministic. The first quantize call on a
- *  device allocates a small scratch buffer (ZYFA_ERR_CAPTURE under capture).
+ *  Asynchronous on `stream`; deterministic; allocates nothing. As in
+ *  zyfa_fp8_quantize, x8 also holds the partial maxima between the passes
+ *  and must not overlap x.
  */
 int zyfa_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const signed char* signs,
                               void* x8, float* descale, void* stream);
@@ -278,7 +282,7 @@ int zyfa_fp8_quantize_rotated_shifted(const void* x, int x_dtype, int batch, int
 const char* zyfa_status_string(int status);
 
 /* zyfa_release - free every cached plan on every device (device memory of
- * job tables and scratch). Must not race with calls in flight. */
+ * the job tables). Must not race with calls in flight. */
 void zyfa_release(void);
 
 /*
