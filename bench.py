@@ -1,12 +1,15 @@
 """Throughput of causal prefill attention on one MI355X, one JSON line.
 
-A step is one pass of the hot path over the 16K-token workloads: BF16
-attention on the MLA-prefill shape (batch 1, seqlen 16384, 16 heads,
-d_qk 192 / d_v 128, bhsd) is the headline value; when the FP8 path is built,
-the step also quantizes q, k and v of the GQA FP8 workload (batch 1, seqlen
-16384, 32 / 8 heads, d 128) and runs FP8 attention on it. Inputs are
-resident in HBM before timing starts. Each kernel's average duration is
-measured with HIP events on the stream it is launched on.
+The headline (`value`, `ms_per_step`, `roofline`) is one step of the hot
+path on the MLA-prefill workload: one BF16 attention launch on batch 1,
+seqlen 16384, 16 heads, d_qk 192 / d_v 128, bhsd, timed as the average of
+`--steps` back-to-back launches. Every other case (BF16 and FP8 GQA at 16K
+tokens with the FP8 quantizer timed separately, FP8 at d_qk 192, the
+precise FP8 mode, workload 5, one GPU's share, partial-range calls, the LSE
+merge, the README's own configuration) is timed the same way and reported
+under `config.cases`; none of them is part of `ms_per_step`. Inputs are
+resident in HBM before timing starts. Each launch is bracketed by HIP
+events on the stream it runs on.
 
 Throughput is causal TFLOP/s = B * H * S^2 * (d_qk + d_v) / time, the
 count of the "ZYFA" README's kernel-benchmark protocol.
@@ -34,10 +37,19 @@ CASES = {
     "fp8_d192_s16384": (4, "fp8"),
     "fp8_d128_share8_s16384": (3, "fp8"),
     "fp8_d192_lean_s16384": (4, "fp8"),
+    "fp8_d128_gqa_precise_s16384": (3, "fp8"),
+    "bf16_act_s32000_b2": (5, "bf16"),
+    "fp8_act_s32000_b2": (5, "fp8"),
+    "fp8_act_precise_s32000_b2": (5, "fp8"),
 }
 # Cases run with a non-default FP8 probability mode: workload 4 with lean P
-# (the README keeps exact P at d_qk = 192; lean P is the library's option).
-PMODE = {"fp8_d192_lean_s16384": "lean"}
+# (the README keeps exact P at d_qk = 192; lean P is the library's option),
+# and the precise mode (bf16-MFMA scores, P split into two e4m3 parts; the
+# mode that meets the FP8 gate on workload 5's activation-like inputs).
+PMODE = {"fp8_d192_lean_s16384": "lean", "fp8_d128_gqa_precise_s16384": "precise",
+         "fp8_act_precise_s32000_b2": "precise"}
+# Cases reported without the quantizer timing and the sustained-clock runs.
+EXTRA = {"bf16_act_s32000_b2", "fp8_act_s32000_b2"}
 # Cases run on a resized workload: one GPU's share of workload 3 when its
 # heads are split over 8 GPUs in whole GQA groups (4 query heads over 1 KV
 # head, 16384 tokens): the kernel at the shape each GPU would run.
@@ -77,6 +89,14 @@ DESCRIPTIONS = {
                               "nheads_k 1, d 128, bshd, N(0,1)",
     "fp8_d192_lean_s16384": "causal MLA-prefill form, fp8 e4m3 with lean P: batch 1, seqlen 16384, nheads 16, "
                             "d_qk 192, d_v 128, bhsd, N(0,1)",
+    "fp8_d128_gqa_precise_s16384": "causal GQA, fp8 e4m3, precise mode (bf16-MFMA scores, hi + lo P): batch 1, "
+                                   "seqlen 16384, nheads 32, nheads_k 8, d 128, bshd, N(0,1)",
+    "bf16_act_s32000_b2": "causal GQA, bf16, activation-like q/k: batch 2, seqlen 32000, nheads 32, nheads_k 8, "
+                          "d 128, bshd",
+    "fp8_act_s32000_b2": "causal GQA, fp8 e4m3 (default mode, known accuracy limit on these inputs), "
+                         "activation-like q/k: batch 2, seqlen 32000, nheads 32, nheads_k 8, d 128, bshd",
+    "fp8_act_precise_s32000_b2": "causal GQA, fp8 e4m3 precise mode, activation-like q/k: batch 2, seqlen 32000, "
+                                 "nheads 32, nheads_k 8, d 128, bshd",
 }
 ALL_CASES = list(CASES) + list(RANGE_CASES) + [MERGE_CASE] + list(CONTEXT_CASES)
 
@@ -521,7 +541,8 @@ def main():
             pm = PMODE.get(name, "default")
             fn = lambda: zy.zyfa_fwd(q8, k8, v8, out, layout=w.layout, q_descale=qs, k_descale=ks, v_descale=vs,
                                      p_mode=pm)
-        extra = name in RESIZED or name in PMODE   # context cases: no quantizer timing, no sustained run
+        # context cases: no quantizer timing, no sustained run
+        extra = name in RESIZED or name in PMODE or name in EXTRA
         if dtype == "fp8" and not extra:
             msq, _ = time_launches(lambda: [zy.zyfa_fp8_quantize(x, x8, xs) for x, x8, xs in
                                             ((q, q8, qs), (k, k8, ks), (v, v8, vs))], args.steps, args.warmup)

@@ -30,8 +30,9 @@ STATUS = {
     "ZYFA_ERR_HIP": -9, "ZYFA_ERR_RANGE": -10, "ZYFA_ERR_ALIGN": -11, "ZYFA_ERR_PMODE": -12, "ZYFA_ERR_SIGNS": -13,
 }
 # FP8 probability modes (zyfa_p_mode): default = lean P below the diagonal at
-# d_qk 128, exact P at d_qk 192.
-P_MODES = {"default": 0, "exact": 1, "lean": 2}
+# d_qk 128, exact P at d_qk 192; precise = bf16-MFMA scores and P split into
+# hi + lo e4m3 parts.
+P_MODES = {"default": 0, "exact": 1, "lean": 2, "precise": 3}
 
 _lib = None
 _lib_err: Optional[str] = None
@@ -128,7 +129,7 @@ def zyfa_fwd(q, k, v, out=None, lse=None, *, layout: str = "bshd", return_lse: b
              p_mode: str = "default", stream=None):
     """Causal forward attention. q, k, v: contiguous CUDA tensors (bf16, or
     float8_e4m3fn / uint8 codes with fp32 device descales). p_mode selects
-    the FP8 probability rounding ("default", "exact", "lean"; see
+    the FP8 probability rounding ("default", "exact", "lean", "precise"; see
     zyfa_p_mode in zyfa.h). Returns out, or (out, lse) when return_lse (or
     an lse tensor is passed)."""
     import torch

@@ -68,15 +68,17 @@ int check_shape(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d
   return ZYFA_OK;
 }
 
-// Finds or builds the plan of a shape (shape.tile_q == 0) with the tile
-// height set for it, else the automatic one; caller holds g_mu.
-int get_plan(const PlanKey& shape, hipStream_t stream, const Plan** out) {
+// Finds or builds the plan of a shape (shape.tile_q == 0): with tile_q
+// rows when given, else with the height set for the shape, else the
+// automatic one; caller holds g_mu.
+int get_plan(const PlanKey& shape, hipStream_t stream, const Plan** out, int tile_q = 0) {
   const int cus = num_cus(shape.device);
   const auto ch = g_tile_choice.find(shape);
   PlanKey key = shape;
-  key.tile_q = ch != g_tile_choice.end()
-                   ? ch->second
-                   : tile_q_rows(shape.batch, shape.seqlen, shape.nheads, shape.d_qk, shape.dtype, cus);
+  key.tile_q = tile_q                    ? tile_q
+               : ch != g_tile_choice.end() ? ch->second
+                                           : tile_q_rows(shape.batch, shape.seqlen, shape.nheads, shape.d_qk,
+                                                         shape.dtype, cus);
   auto it = g_plans.find(key);
   if (it != g_plans.end()) {
     *out = &it->second;
@@ -123,7 +125,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   int rc = check_shape(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype);
   if (rc) return rc;
   if (seqlen_k <= 0) return ZYFA_ERR_SHAPE;
-  if (p_mode != ZYFA_P_DEFAULT && p_mode != ZYFA_P_EXACT && p_mode != ZYFA_P_LEAN) return ZYFA_ERR_PMODE;
+  if (p_mode != ZYFA_P_DEFAULT && p_mode != ZYFA_P_EXACT && p_mode != ZYFA_P_LEAN && p_mode != ZYFA_P_PRECISE)
+    return ZYFA_ERR_PMODE;
   if (!q || !k || !v || !out) return ZYFA_ERR_NULL;
   if (dtype == ZYFA_DTYPE_FP8_E4M3FN && (!q_descale || !k_descale || !v_descale)) return ZYFA_ERR_DESCALE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
@@ -136,7 +139,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   std::lock_guard<std::mutex> lock(g_mu);
   const Plan* plan = nullptr;
   PlanKey key{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype, 0};
-  if ((rc = get_plan(key, stream, &plan))) return rc;
+  // the precise FP8 mode runs on 128-row query tiles only
+  const bool precise = dtype == ZYFA_DTYPE_FP8_E4M3FN && p_mode == ZYFA_P_PRECISE;
+  if ((rc = get_plan(key, stream, &plan, precise ? 128 : 0))) return rc;
 
   AttnArgs a{};
   a.q.ptr = q;
@@ -182,8 +187,10 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
     e = launch_attn_bf16(a, d_qk, lse != nullptr, plan->tile_q, plan->num_wgs, stream);
   else
     e = launch_attn_fp8(a, d_qk, lse != nullptr,
-                        p_mode == ZYFA_P_LEAN || (p_mode == ZYFA_P_DEFAULT && d_qk == 128), plan->tile_q,
-                        plan->num_wgs, stream);
+                        p_mode == ZYFA_P_PRECISE                                       ? FP8Mode::kPrecise
+                        : p_mode == ZYFA_P_LEAN || (p_mode == ZYFA_P_DEFAULT && d_qk == 128) ? FP8Mode::kLean
+                                                                                           : FP8Mode::kExact,
+                        plan->tile_q, plan->num_wgs, stream);
   return e == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
 }
 
@@ -266,7 +273,10 @@ int zyfa_prepare(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int 
   std::lock_guard<std::mutex> lock(g_mu);
   const Plan* plan = nullptr;
   PlanKey key{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype, 0};
-  return get_plan(key, reinterpret_cast<hipStream_t>(stream), &plan);
+  if ((rc = get_plan(key, reinterpret_cast<hipStream_t>(stream), &plan))) return rc;
+  // FP8: also the 128-row plan of the precise mode
+  if (dtype == ZYFA_DTYPE_FP8_E4M3FN) rc = get_plan(key, reinterpret_cast<hipStream_t>(stream), &plan, 128);
+  return rc;
 }
 
 int zyfa_set_tile_q(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int dtype, int tile_q) {

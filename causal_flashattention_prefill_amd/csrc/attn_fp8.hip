@@ -58,6 +58,17 @@
 //    each E8M0 scale block is 32 consecutive keys.
 //  - d_qk = 192 adds d 128..191 to every score block through two
 //    v_mfma_f32_16x16x32_fp8_fp8 (8-byte operands, no zero padding).
+//  - Precise mode (for inputs whose channels differ widely in magnitude,
+//    such as activations with outlier channels): gfx950's FP8 matrix
+//    instructions sum their products with an error of up to 2^-11.5 of
+//    sum |q_c k_c| on such rows, enough to move the softmax weights of keys
+//    whose scores are close. Here the e4m3 codes of q and k are converted to
+//    bf16 (exactly: every e4m3 value is a bf16 value) and S^T = K Q^T runs on
+//    v_mfma_f32_16x16x32_bf16, whose sums hold to ~2^-22; and each
+//    probability of a block is split into two e4m3 values, hi = RNE(p) and
+//    lo = RNE(p - hi), multiplied into V (and into the row sum) by two PV
+//    matrix instructions with the block's scale, which carries p to about
+//    7 significant bits instead of 4. Exact P only.
 //
 // Fragment layout of the 16x16x128 FP8 MFMA (lane = 16*g + r, g = lane/16):
 // A (16 x 128): lane holds row r, bytes 0..15 = k 16g..16g+15 and bytes
@@ -91,6 +102,28 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
+// Probability modes of the kernel template (zyfa_p_mode resolved per call).
+constexpr int kPmExact = 0;
+constexpr int kPmLean = 1;
+constexpr int kPmPrecise = 2;
+
+// Eight e4m3fn codes (two words, byte j = element j) -> eight bf16 values,
+// exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1, two codes per
+// instruction). Words are passed by value.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned w0, unsigned w1) {
+  const unsigned r0 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  const unsigned r1 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  const unsigned r2 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  const unsigned r3 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return __builtin_bit_cast(bf16x8, u32x4{r0, r1, r2, r3});
+}
+
+// e4m3fn codes 0, 1 (HI false) or 2, 3 (HI true) of word w as floats.
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8_pair_to_f32(unsigned w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
 // a * b rounded to fp32 on its own: never fused with a following add.
 __device__ __forceinline__ float mul_nofma(float a, float b) {
 #pragma clang fp contract(off)
@@ -115,9 +148,12 @@ __device__ __forceinline__ unsigned cvt4_fp8(float a, float b, float c, float d)
   return w;
 }
 
-template <int DQK, bool WITH_LSE, bool LEAN, int QG>
+template <int DQK, bool WITH_LSE, int PM, int QG>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArgs a) {
   constexpr int DV = 128;
+  constexpr bool LEAN = PM == kPmLean;
+  constexpr bool PRECISE = PM == kPmPrecise;
+  constexpr int NCB = DQK / 32;                     // bf16 MFMA k-steps over d_qk (precise mode)
   constexpr int RW = 16 * QG;                       // query rows per wave (QG 16-row groups)
   constexpr int kTileQ = 8 * RW;                    // query rows per tile
   constexpr bool D192 = DQK == 192;
@@ -206,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // of keys, a block whose first row sees fewer than 256 keys is exact
       // throughout as well.
       const int qb = q0 & ~255;
-      const int K0 = qb + dl + 1 >= 256 ? (qb + dl + 1) / kTileK : 0;
+      const int K0 = min(qb + dl + 1, Sk) >= 256 ? (qb + dl + 1) / kTileK : 0;
 
       // Q fragments (B operand): lane (g, n) holds q[row n][16g..16g+15] and
       // q[row n][64+16g..]; for d 192 also q[row n][128+8g..+7] and
@@ -227,6 +263,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         if (D192) {
           qx[qg][0] = __builtin_bit_cast(long, buf_load8(rq, off + 128 + 8 * g));
           qx[qg][1] = __builtin_bit_cast(long, buf_load8(rq, off + 160 + 8 * g));
+        }
+      }
+      // Precise mode: the B operands of the bf16 score MFMAs, k-step c of
+      // lane group g holding the same d values as the K operand: c = 0..3
+      // are bytes 8 (c % 2) .. of the 16-byte chunks g (c < 2) and 4 + g
+      // (c >= 2), c = 4, 5 the d 128..191 words.
+      bf16x8 qbf[PRECISE ? QG : 1][PRECISE ? NCB : 1];
+      if (PRECISE) {
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const unsigned w0 = (unsigned)qf[qg][2 * c], w1 = (unsigned)qf[qg][2 * c + 1];
+            qbf[qg][c] = fp8x8_to_bf16(w0, w1);
+          }
+          if (D192) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const unsigned long long x = (unsigned long long)qx[qg][c];
+              qbf[qg][4 + c] = fp8x8_to_bf16((unsigned)x, (unsigned)(x >> 32));
+            }
+          }
         }
       }
 
@@ -256,6 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // this lane supplies to the PV MFMA
       f32x4 s[QG][8];
       i32x8 pf[QG];
+      i32x8 pl[PRECISE ? QG : 1];   // precise mode: the lo parts of P
       int psc[QG];
 
       // Direct global-to-LDS tile loads; K row r of a slot holds key
@@ -360,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       auto matrix_cluster = [&](int t) {
         __builtin_amdgcn_s_setprio(1);
         const bool pv = t >= 1 && t - 1 <= kt_w;
-        if (pv) {
+        if (pv && !PRECISE) {
           const char* vs = vring + ((t - 1) % kSlots) * V_SLOT;
           i32x8 vfb[kPfV];
 #pragma unroll
@@ -379,7 +438,82 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
           }
         }
-        if (t <= kt_w) {
+        if (pv && PRECISE) {
+          // hi parts of column block db at step db, lo parts at step db + 1,
+          // so two products into one accumulator are never adjacent
+          const char* vs = vring + ((t - 1) % kSlots) * V_SLOT;
+          i32x8 vfb[kPfV];
+#pragma unroll
+          for (int u = 0; u < kPfV; ++u) vfb[u] = v_frag(vs, u);
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) lacc[qg] = mfma_fp8(ones, pf[qg], lacc[qg], kE8M0One, psc[qg]);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * kPfV, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
+          i32x8 prev = vfb[0];
+#pragma unroll
+          for (int st = 0; st <= 8; ++st) {
+            i32x8 cur = prev;
+            if (st < 8) {
+              cur = vfb[st % kPfV];
+              if (st + kPfV < 8) vfb[st % kPfV] = v_frag(vs, st + kPfV);
+#pragma unroll
+              for (int qg = 0; qg < QG; ++qg) o[qg][st] = mfma_fp8(cur, pf[qg], o[qg][st], kE8M0One, psc[qg]);
+            }
+            if (st >= 1) {
+#pragma unroll
+              for (int qg = 0; qg < QG; ++qg)
+                o[qg][st - 1] = mfma_fp8(prev, pl[qg], o[qg][st - 1], kE8M0One, psc[qg]);
+            }
+            prev = cur;
+            if (st + kPfV < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+            if (st == 0 || st == 8) __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
+            else __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * QG, 0);
+          }
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) lacc[qg] = mfma_fp8(ones, pl[qg], lacc[qg], kE8M0One, psc[qg]);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
+        }
+        if (t <= kt_w && PRECISE) {
+          // scores on the bf16 instruction: each K fragment's codes become
+          // NCB bf16 operands, k-steps in the order of the Q operands. Two
+          // key blocks are interleaved, so the k-steps accumulating into one
+          // score block are never adjacent; the next pair's fragments are
+          // read while this pair's instructions run.
+          const char* ka = kring + (t % kSlots) * K_SLOT;
+          KFrag kfb[2][2];
+          kfb[0][0] = k_frag(ka, 0);
+          kfb[0][1] = k_frag(ka, 1);
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            const KFrag c0 = kfb[pr & 1][0], c1 = kfb[pr & 1][1];
+            if (pr < 3) {
+              kfb[(pr + 1) & 1][0] = k_frag(ka, 2 * pr + 2);
+              kfb[(pr + 1) & 1][1] = k_frag(ka, 2 * pr + 3);
+            }
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                const KFrag& cur = j ? c1 : c0;
+                bf16x8 kc;
+                if (c < 4) {
+                  const unsigned w0 = (unsigned)cur.a[2 * c], w1 = (unsigned)cur.a[2 * c + 1];
+                  kc = fp8x8_to_bf16(w0, w1);
+                } else {
+                  const unsigned long long x = (unsigned long long)(c == 4 ? cur.b0 : cur.b1);
+                  kc = fp8x8_to_bf16((unsigned)x, (unsigned)(x >> 32));
+                }
+                const int kb = 2 * pr + j;
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg)
+                  s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, qbf[qg][c],
+                                                                      c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[qg][kb],
+                                                                      0, 0, 0);
+              }
+            }
+          }
+        }
+        if (t <= kt_w && !PRECISE) {
           const char* ka = kring + (t % kSlots) * K_SLOT;
           // K fragments are read kPfK 16-key blocks ahead of their MFMAs
           KFrag kfb[kPfK];
@@ -387,12 +521,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
           for (int u = 0; u < kPfK; ++u) kfb[u] = k_frag(ka, u);
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (D192 ? 4 : 2) * kPfK, 0);
           // d 128..191 (d_qk = 192) accumulate onto the result of the scaled
-          // instruction. With two query groups another scaled instruction
-          // separates each such pair from the result it reads; with one, the
-          // pair of block kb - 1 is issued after the scaled instruction of
-          // block kb instead, since issued straight after the result it
-          // reads as its accumulator, the pair was given no wait states and
-          // read a stale accumulator on the GPU.
+          // instruction. Issued straight after that result, such a pair was
+          // given no wait states and read a stale accumulator on the GPU, so
+          // another instruction always sits between them: with two query
+          // groups the other group's scaled instruction, with one the scaled
+          // instruction of block kb + 1 (the pair of block kb - 1 is issued
+          // after the scaled instruction of block kb). Scheduling barriers
+          // hold the order; a CPU test checks it in the built code.
           constexpr bool kDefer = D192 && QG == 1;
           long pb0 = 0, pb1 = 0;   // d 128..191 K fragments of the deferred block
 #pragma unroll
@@ -412,6 +547,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
               pb0 = cur.b0;
               pb1 = cur.b1;
             } else if (D192) {
+              // both groups' scaled instructions first, held there by a
+              // scheduling barrier: the other group's scaled instruction then
+              // separates each pair from the result it accumulates onto
+              __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
               for (int qg = 0; qg < QG; ++qg) {
                 s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur.b0, qx[qg][0], s[qg][kb], 0, 0, 0);
@@ -534,7 +673,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
               f32x4 p;
 #pragma unroll
               for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], sl2, kb < 4 ? nm0 : nm1));
-              pf[qg][kb] = (int)cvt4_fp8(p[0], p[1], p[2], p[3]);
+              const unsigned hi = cvt4_fp8(p[0], p[1], p[2], p[3]);
+              pf[qg][kb] = (int)hi;
+              if (PRECISE) {
+                // lo = RNE(p - hi); p - hi is exact in fp32
+                const f32x2 h01 = fp8_pair_to_f32<false>(hi), h23 = fp8_pair_to_f32<true>(hi);
+                const float h0 = h01[0], h1 = h01[1], h2 = h23[0], h3 = h23[1];
+                pl[qg][kb] = (int)cvt4_fp8(p[0] - h0, p[1] - h1, p[2] - h2, p[3] - h3);
+              }
             }
           }
           psc[qg] = (int)es + 127;
@@ -613,31 +759,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
 
 }  // namespace
 
-template <int DQK, bool LEAN, int QG>
+template <int DQK, int PM, int QG>
 static void launch_fp8(const AttnArgs& a, bool with_lse, dim3 gd, dim3 bd, hipStream_t s) {
-  if (with_lse) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, true, LEAN, QG>), gd, bd, 0, s, a);
-  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, false, LEAN, QG>), gd, bd, 0, s, a);
+  if (with_lse) hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, true, PM, QG>), gd, bd, 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, false, PM, QG>), gd, bd, 0, s, a);
 }
 
+// The precise mode runs on 128-row tiles only (one 16-row group per wave):
+// with two groups its bf16 Q operands and lo parts do not fit the register
+// file beside the scores and accumulators.
 template <int DQK, int QG>
-static void launch_fp8_p(const AttnArgs& a, bool with_lse, bool lean, dim3 gd, dim3 bd, hipStream_t s) {
-  if (lean) launch_fp8<DQK, true, QG>(a, with_lse, gd, bd, s);
-  else launch_fp8<DQK, false, QG>(a, with_lse, gd, bd, s);
+static hipError_t launch_fp8_p(const AttnArgs& a, bool with_lse, int pm, dim3 gd, dim3 bd, hipStream_t s) {
+  if (pm == kPmLean) launch_fp8<DQK, kPmLean, QG>(a, with_lse, gd, bd, s);
+  else if (pm == kPmExact) launch_fp8<DQK, kPmExact, QG>(a, with_lse, gd, bd, s);
+  else if constexpr (QG == 1) launch_fp8<DQK, kPmPrecise, QG>(a, with_lse, gd, bd, s);
+  else return hipErrorInvalidValue;
+  return hipSuccess;
 }
 
-hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean, int tile_q, int grid,
+hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, FP8Mode mode, int tile_q, int grid,
                            hipStream_t s) {
   const dim3 gd(grid), bd(kThreads);
   if (tile_q != 128 && tile_q != 256) return hipErrorInvalidValue;
+  const int pm = mode == FP8Mode::kLean ? kPmLean : mode == FP8Mode::kPrecise ? kPmPrecise : kPmExact;
   const bool tall = tile_q == 256;
-  if (d_qk == 128) {
-    if (tall) launch_fp8_p<128, 2>(a, with_lse, lean, gd, bd, s);
-    else launch_fp8_p<128, 1>(a, with_lse, lean, gd, bd, s);
-  } else {
-    if (tall) launch_fp8_p<192, 2>(a, with_lse, lean, gd, bd, s);
-    else launch_fp8_p<192, 1>(a, with_lse, lean, gd, bd, s);
-  }
-  return hipGetLastError();
+  hipError_t e;
+  if (d_qk == 128) e = tall ? launch_fp8_p<128, 2>(a, with_lse, pm, gd, bd, s) : launch_fp8_p<128, 1>(a, with_lse, pm, gd, bd, s);
+  else e = tall ? launch_fp8_p<192, 2>(a, with_lse, pm, gd, bd, s) : launch_fp8_p<192, 1>(a, with_lse, pm, gd, bd, s);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace zyfa

@@ -33,7 +33,10 @@ struct AttnArgs {
 
 // tile_q: query rows per tile, 256 (32 per wave) or 128 (16 per wave)
 hipError_t launch_attn_bf16(const AttnArgs& a, int d_qk, bool with_lse, int tile_q, int grid, hipStream_t s);
-hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, bool lean, int tile_q, int grid,
+// How the FP8 kernel rounds probabilities (and, precise, computes scores);
+// zyfa_p_mode resolved for the call's head dim.
+enum class FP8Mode { kExact, kLean, kPrecise };
+hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, FP8Mode mode, int tile_q, int grid,
                            hipStream_t s);
 // x8 doubles as the scratch of the amax partials (overwritten by the codes)
 hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,

@@ -100,12 +100,25 @@ int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  *                  unbiased on average); keys from that tile on, which
  *                  include every key of the rows with fewest keys, keep
  *                  exact P.
+ *  ZYFA_P_PRECISE  for inputs whose channels differ widely in magnitude
+ *                  (activations with outlier channels): the scores are
+ *                  computed on the bf16 matrix instruction from the e4m3
+ *                  codes (exact products, fp32-accurate sums; the FP8
+ *                  matrix instructions sum to about 2^-11.5 of
+ *                  sum_c |q_c k_c| there), and each probability is split
+ *                  into two e4m3 values hi = RNE(p), lo = RNE(p - hi), both
+ *                  multiplied into V and summed into the denominator (about
+ *                  7 significant bits of p instead of 4). Exact P
+ *                  otherwise. Always runs on 128-row query tiles (its
+ *                  operands do not fit the register file at 256 rows);
+ *                  slower than the other modes.
  * BF16 calls ignore the mode.
  */
 enum zyfa_p_mode {
   ZYFA_P_DEFAULT = 0,
   ZYFA_P_EXACT = 1,
-  ZYFA_P_LEAN = 2
+  ZYFA_P_LEAN = 2,
+  ZYFA_P_PRECISE = 3
 };
 
 /* zyfa_fwd with an explicit softmax scale (flash-attn's softmax_scale
@@ -168,6 +181,8 @@ int zyfa_lse_merge(const void* out_a, const float* lse_a, const void* out_b, con
  * zyfa_prepare - build (or find) the per-shape plan ahead of time so that a
  * later zyfa_fwd with the same shape allocates nothing and copies nothing
  * from the host (README, Usage: run each new shape once before capturing).
+ * For FP8 it also builds the 128-row plan of ZYFA_P_PRECISE. with_lse is
+ * accepted for symmetry and ignored (plans do not depend on it).
  * Returns ZYFA_ERR_CAPTURE if the plan is missing and `stream` is capturing.
  */
 int zyfa_prepare(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v,

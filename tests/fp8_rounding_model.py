@@ -37,6 +37,9 @@ For query row i (keys j <= i), with x_j = softmax_scale * log2(e) *
      8 log2(2 ln(2)^2) = 55.54 instead of 56 makes the piecewise-linear
      value 2^floor(y) (1 + frac(y)) unbiased: its mean ratio to 2^y over a
      uniform frac(y) is 1 / (2 ln(2)^2));
+   - precise ("precise"): two codes per key, hi = RNE_e4m3fn(2^y) and
+     lo = RNE_e4m3fn(2^y - value(hi)), whose values add (the library's
+     precise mode multiplies both into V with the block's scale);
    - lean P off the diagonal query tile ("lean_offdiag"): the query rows
      are grouped in blocks of query_tile rows (256, which the kernels use
      at every query-tile height); keys of the key tiles that hold the rows
@@ -44,7 +47,8 @@ For query row i (keys j <= i), with x_j = softmax_scale * log2(e) *
      query_tile / KEY_TILE) get exact P, which covers every key of the rows
      with the fewest keys; the key tiles before them get lean P. (Which tiles keep exact P is this
      implementation's choice; the README uses lean P throughout at d = 128.)
-4. The key's weight is w_j = value(c_j) * 2^(e_b + m), with m the reference
+4. The key's weight is w_j = value(c_j) * 2^(e_b + m) (precise: the sum of
+   the two values), with m the reference
    when its tile was visited. O_i = sum_j w_j v_j / sum_j w_j and
    LSE_i = ln(sum_j w_j).
 
@@ -67,7 +71,7 @@ BLOCK = 32
 TAU = 8.0
 LOG2E = 1.4426950408889634073599246810019
 LEAN_C = 56.0 + 8.0 * math.log2(2.0 * math.log(2.0) ** 2)
-P_MODES = ("exact", "lean", "lean_offdiag")
+P_MODES = ("exact", "lean", "lean_offdiag", "precise")
 
 
 def lean_code(y) -> np.ndarray:
@@ -79,6 +83,13 @@ def lean_code(y) -> np.ndarray:
 def exact_code(y) -> np.ndarray:
     """RNE e4m3fn code of 2^y."""
     return e4m3fn_encode(np.exp2(np.asarray(y, dtype=np.float64))).astype(np.int64)
+
+
+def precise_value(y) -> np.ndarray:
+    """value(hi) + value(lo) of the precise mode for p = 2^y."""
+    p = np.exp2(np.asarray(y, dtype=np.float64))
+    hi = e4m3fn_decode(e4m3fn_encode(p))
+    return hi + e4m3fn_decode(e4m3fn_encode(p - hi))
 
 
 def row_weights(x: np.ndarray, i: int, p_mode: str, *, key_tile: int = KEY_TILE, block: int = BLOCK,
@@ -95,6 +106,7 @@ def row_weights(x: np.ndarray, i: int, p_mode: str, *, key_tile: int = KEY_TILE,
     m = -np.inf
     exps = np.zeros(n)     # e_b + m_t per key
     codes = np.zeros(n, dtype=np.int64)
+    vals = np.zeros(n)     # precise mode: value(hi) + value(lo)
     diag_tile = i // key_tile
     exact_from = (i // query_tile) * query_tile // key_tile
     for t in range(diag_tile + 1):
@@ -107,10 +119,15 @@ def row_weights(x: np.ndarray, i: int, p_mode: str, *, key_tile: int = KEY_TILE,
             e_b = max(math.floor(x[b0:b1].max() - m), -126)
             y = x[b0:b1] - m - e_b
             lean = p_mode == "lean" or (p_mode == "lean_offdiag" and t < exact_from)
-            codes[b0:b1] = lean_code(y) if lean else exact_code(y)
+            if p_mode == "precise":
+                vals[b0:b1] = precise_value(y)
+            else:
+                codes[b0:b1] = lean_code(y) if lean else exact_code(y)
             exps[b0:b1] = e_b + m
     m_final = m
-    w = e4m3fn_decode(codes.astype(np.uint8)) * np.exp2(exps - m_final)
+    if p_mode != "precise":
+        vals = e4m3fn_decode(codes.astype(np.uint8))
+    w = vals * np.exp2(exps - m_final)
     return w, m_final
 
 

@@ -20,6 +20,11 @@ BF16_LSE_ABS = 1e-3
 # with the same bf16 output-rounding allowance on the max.
 FP8_OUT_MAX = 6e-2
 FP8_OUT_MEAN = 5e-3
+# FP8 LSE (from the rounded probabilities): each weight is off by at most
+# 2^-4 relative (one e4m3 rounding), so the row sum's log by < 0.065 nats;
+# the precise mode keeps 2^-8 (hi + lo), i.e. < 0.004 nats, gated at 0.008.
+FP8_LSE_MAX = 0.065
+FP8_PRECISE_LSE_MAX = 0.008
 
 
 def bf16_pair(x: np.ndarray, device="cuda"):
@@ -65,17 +70,37 @@ def check_bf16(out, ref_out, lse=None, ref_lse=None, what="", lse_mag=None):
     return d.max()
 
 
-def check_fp8(out, ref_out, what="", extra=None):
-    """extra: optional per-row (leading axes of out) allowance added to the max bound."""
+def check_fp8(out, ref_out, what=""):
+    """The FP8 gate: max |d out| <= 6e-2 (plus the bf16 output's half ulp,
+    2^-8 |ref|) and mean <= 5e-3."""
     d = np.abs(out - ref_out)
     bound = FP8_OUT_MAX + BF16_OUT_REL_ROUND * np.abs(ref_out)
-    if extra is not None:
-        bound = bound + extra[..., None]
     assert np.all(np.isfinite(out)), what + ": non-finite output"
     worst = np.unravel_index(np.argmax(d - bound), d.shape)
+    print(f"{what}: max|dout|={d.max():.3e} mean={d.mean():.2e}", flush=True)
     assert np.all(d <= bound), f"{what}: max|dout|={d.max():.3e} at {worst} (ref {ref_out[worst]:.4f} got {out[worst]:.4f})"
     assert d.mean() <= FP8_OUT_MEAN, f"{what}: mean|dout|={d.mean():.3e}"
     return d.max(), d.mean()
+
+
+def fp8_known_limit(out, ref_out, allowance, what=""):
+    """The fast FP8 modes on activation-like inputs, which do not meet the
+    max gate (the FP8 matrix instructions' score sums; see FP8_MFMA_REL):
+    prints the literal max and the number of elements over the gate, holds
+    the mean gate, and, as a separate diagnostic, checks that every element
+    stays within the gate plus the error that score precision explains
+    (allowance: per row, leading axes of out). The precise mode meets the
+    gate itself (check_fp8)."""
+    d = np.abs(out - ref_out)
+    bound = FP8_OUT_MAX + BF16_OUT_REL_ROUND * np.abs(ref_out)
+    over = int(np.count_nonzero(d > bound))
+    print(f"{what}: KNOWN LIMIT literal max|dout|={d.max():.3e}, {over} of {d.size} elements over the 6e-2 gate, "
+          f"mean={d.mean():.2e}", flush=True)
+    assert np.all(np.isfinite(out)), what + ": non-finite output"
+    assert d.mean() <= FP8_OUT_MEAN, f"{what}: mean|dout|={d.mean():.3e}"
+    diag = bound + allowance[..., None]
+    assert np.all(d <= diag), f"{what}: error beyond what FP8 score precision explains: max {d.max():.3e}"
+    return d.max(), d.mean(), over
 
 
 # gfx950's FP8 matrix instructions (v_mfma_scale_f32_16x16x128_f8f6f4 and the
@@ -90,7 +115,8 @@ FP8_MFMA_REL = 2.0 ** -11
 
 
 def fp8_score_allowance(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, rows) -> np.ndarray:
-    """Per-row bound on |d out| caused by the FP8 MFMA's score error alone.
+    """Per-row bound on |d out| caused by the FP8 MFMA's score error alone
+    (a diagnostic of the known limit, never part of the gate).
 
     Each score carries an error of at most e_j = FP8_MFMA_REL * scale * log2(e)
     * sum_c |q_ic k_jc| (log2 units), so each softmax weight moves by at most a
@@ -105,8 +131,8 @@ def fp8_score_allowance(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: f
     return (np.exp2(2 * e) - 1.0) * vmax
 
 
-# Tight check against the oracle that rounds the probabilities as the
-# selected FP8 mode does. What still differs is the score: the kernel's FP8
+# Tight check against the model of this library's probability rounding
+# (tests/fp8_rounding_model.py; a regression check, not the accuracy gate). What still differs is the score: the kernel's FP8
 # MFMA sums in fp32 with its own rounding (bounded by 2^-15.7 sum|ab| on
 # N(0, 1) data), so a code whose 8 y + C (lean) or 2^y (exact) lies that
 # close to a rounding boundary can land one code step (at most 2^(1/8), 9%)
@@ -149,6 +175,11 @@ def check_partial(out, ref_out, lse, ref_lse, what="", fp8=False):
         return
     if fp8:
         check_fp8(out[live], ref_out[live], what)
+        if lse is not None:
+            # the FP8 LSE comes from the rounded probabilities: one e4m3
+            # rounding moves a row sum by at most 2^-4 relative, < 0.065 nats
+            dl = np.abs(lse[live] - ref_lse[live])
+            assert np.all(np.isfinite(dl)) and dl.max() < FP8_LSE_MAX, f"{what}: max|dLSE|={dl.max():.3e}"
     else:
         check_bf16(out[live], ref_out[live], None if lse is None else lse[live], None if lse is None else ref_lse[live],
                    what)

@@ -52,7 +52,7 @@ def test_fwd_argument_errors(kw, status):
     assert _fwd(**kw) == zy.STATUS[status]
 
 
-@pytest.mark.parametrize("p_mode", [-1, 3, 100])
+@pytest.mark.parametrize("p_mode", [-1, 4, 100])
 def test_fwd_ex_rejects_unknown_p_mode(p_mode):
     L = zy.lib()
     rc = L.zyfa_fwd_ex(16, 16, 16, 16, None, 1, 128, 4, 2, 128, 128, 0, 1, 16, 16, 16, 0.0, p_mode, None)

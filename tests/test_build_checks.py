@@ -1,0 +1,107 @@
+"""Checks of the gfx950 code built from the attention sources (CPU only:
+hipcc compiles for gfx950 without a GPU).
+
+gfx950 does not always insert wait states between a matrix instruction and
+a matrix instruction of another kind that reads its result as the
+accumulator: the FP8 kernel at d_qk = 192 adds d 128..191 to each score
+block with v_mfma_f32_16x16x32_fp8_fp8 onto the result of
+v_mfma_scale_f32_16x16x128_f8f6f4, and issued straight after it the second
+instruction once read a stale accumulator. The kernel orders its
+instructions so that another matrix instruction always sits between the two
+(scheduling barriers); this test reads the built code and fails if any
+scaled FP8 result is read by the next matrix instruction of another kind.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "causal_flashattention_prefill_amd", "csrc", "attn_fp8.hip")
+
+
+def _hipcc():
+    p = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    return p if os.path.exists(p) else shutil.which("hipcc")
+
+
+@pytest.fixture(scope="module")
+def fp8_asm(tmp_path_factory):
+    hipcc = _hipcc()
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    from causal_flashattention_prefill_amd.build import EXTRA_FLAGS, HIPCC_FLAGS
+    out = str(tmp_path_factory.mktemp("asm") / "attn_fp8.s")
+    flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [hipcc, *flags, *EXTRA_FLAGS["attn_fp8.hip"], "-I", os.path.join(ROOT, "include"),
+           "--cuda-device-only", "-S", SRC, "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    with open(out) as f:
+        return f.read()
+
+
+_MFMA = re.compile(r"^\s*(v_mfma\w*)\s+([va]\[?[\d:]+\]?),\s*([va]\[?[\d:]+\]?),\s*([va]\[?[\d:]+\]?),\s*"
+                   r"([va]\[?[\d:]+\]?|0)")
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return m.group(1), int(m.group(2)), int(m.group(3))
+    m = re.match(r"([va])(\d+)$", tok)
+    if m:
+        return m.group(1), int(m.group(2)), int(m.group(2))
+    return None
+
+
+def _overlap(a, b):
+    return a is not None and b is not None and a[0] == b[0] and a[1] <= b[2] and b[1] <= a[2]
+
+
+def kernels(asm):
+    """{kernel name: [matrix instructions as (opcode, dst, a, b, c)]} in
+    program order."""
+    out, cur = {}, None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\w+attn_fwd_fp8_kernel\w+):", line)
+        if m:
+            cur = out.setdefault(m.group(1), [])
+            continue
+        if cur is None:
+            continue
+        if line.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        m = _MFMA.match(line)
+        if m:
+            cur.append((m.group(1),) + tuple(_regs(t) for t in m.groups()[1:]))
+    return out
+
+
+def test_every_fp8_kernel_variant_was_found(fp8_asm):
+    ks = kernels(fp8_asm)
+    # d_qk 128/192 x LSE x (exact, lean) x 2 tile heights + precise at 128 rows
+    assert len(ks) == 2 * 2 * 2 * 2 + 2 * 2, sorted(ks)
+    assert all(len(v) > 0 for v in ks.values())
+
+
+def test_scaled_result_is_not_read_by_the_next_matrix_instruction(fp8_asm):
+    bad = []
+    for name, ins in kernels(fp8_asm).items():
+        for i in range(len(ins) - 1):
+            op, dst = ins[i][0], ins[i][1]
+            nxt = ins[i + 1]
+            if "mfma_scale" not in op or nxt[0] == op:
+                continue
+            if any(_overlap(dst, r) for r in nxt[2:]):
+                bad.append((name, i, op, nxt[0]))
+    assert not bad, f"{len(bad)} scaled results read straight away: {bad[:5]}"
+
+
+def test_d192_kernels_mix_the_two_kinds(fp8_asm):
+    # the check above only means something where the two kinds meet
+    ks = kernels(fp8_asm)
+    mixed = [n for n, ins in ks.items() if "Li192E" in n and any("fp8_fp8" in x[0] for x in ins)]
+    assert len(mixed) >= 8, mixed

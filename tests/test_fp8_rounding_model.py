@@ -32,9 +32,25 @@ def _worked():
 
 @pytest.mark.parametrize("mode,y,code,w", _worked())
 def test_worked_codes(mode, y, code, w):
-    c = (fp8_p.exact_code if mode == "exact" else fp8_p.lean_code)(np.array([y]))[0]
+    c = (fp8_p.lean_code if mode == "lean" else fp8_p.exact_code)(np.array([y]))[0]
     assert c == code
-    assert e4m3fn_decode(np.array([c], np.uint8))[0] == w
+    if mode == "precise":
+        assert fp8_p.precise_value(np.array([y]))[0] == w
+    else:
+        assert e4m3fn_decode(np.array([c], np.uint8))[0] == w
+
+
+def test_precise_value_error_bound():
+    # hi carries 4 significant bits (error <= 2^-4 relative); lo rounds the
+    # remainder to 4 more, so |hi + lo - p| <= 2^-4 * 2^-4 * p for p in the
+    # normal range of e4m3 (p >= 2^-2 keeps the remainder normal too)
+    rng = np.random.default_rng(8)
+    y = rng.uniform(-2.0, 0.999, 100000)
+    p = np.exp2(y)
+    r = np.abs(fp8_p.precise_value(y) - p) / p
+    assert r.max() <= 2.0 ** -8
+    hi = e4m3fn_decode(fp8_p.exact_code(y).astype(np.uint8))
+    assert (np.abs(hi - p) / p).max() > 2.0 ** -6   # hi alone is much coarser
 
 
 def test_lean_constant_rounds_integers_to_the_exact_code():

@@ -1,8 +1,14 @@
 """GPU parity of the FP8 path: the quantizer bit for bit against the oracle's,
-and FP8 attention (through the C ABI) against two float64 oracles on the
-oracle's own dequantized inputs: exact softmax attention (the accuracy
-gate), and attention with the probabilities rounded the way the selected
-FP8 mode rounds them (a tight check that the kernel computes that mode)."""
+and FP8 attention (through the C ABI) on the oracle's own dequantized
+inputs, against exact softmax attention in float64 (the oracle; the accuracy
+gate), and, as a tighter regression check, against the model of this
+library's probability rounding (tests/fp8_rounding_model.py).
+
+On activation-like inputs (workload 5's generator) the fast modes do not
+meet the max gate: gfx950's FP8 matrix instructions sum q.k with an error
+that moves the weights of near-tied keys. Those cases report the literal
+max and count over the gate and hold the mean gate (parity.fp8_known_limit);
+the precise mode meets the full gate on them."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +16,8 @@ import torch
 import oracle
 import fp8_rounding_model
 from workloads import WORKLOADS, Workload, generate
-from parity import bf16_pair, check_fp8, check_fp8_rounding, fp8_score_allowance, out_to_f64, tile_height
+from parity import (FP8_LSE_MAX, FP8_PRECISE_LSE_MAX, bf16_pair, check_fp8, check_fp8_rounding, fp8_known_limit,
+                    fp8_score_allowance, out_to_f64, tile_height)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,8 +79,10 @@ def _allowance(rq, rk, rv, w):
     return np.swapaxes(al, 1, 2) if w.layout == "bshd" else al
 
 
-def oracle_p_mode(p_mode: str, d_qk: int) -> str:
-    """The oracle's rounding mode for a library p_mode (zyfa_p_mode)."""
+def model_p_mode(p_mode: str, d_qk: int) -> str:
+    """The rounding model's mode for a library p_mode (zyfa_p_mode)."""
+    if p_mode == "precise":
+        return "precise"
     if p_mode == "exact" or (p_mode == "default" and d_qk == 192):
         return "exact"
     return "lean_offdiag"
@@ -89,13 +98,16 @@ def run_case(w: Workload, seed=None, with_lse=False, p_mode="default"):
     torch.cuda.synchronize()
     out, lse = res if with_lse else (res, None)
     ref_out, ref_lse = oracle.causal_attention_ref(rq, rk, rv, layout=w.layout)
-    extra = _allowance(rq, rk, rv, w) if w.activation_like else None
-    md, mn = check_fp8(out_to_f64(out), ref_out, w.name, extra=extra)
+    what = f"{w.name} {p_mode}"
+    if w.activation_like and p_mode != "precise":
+        md, mn, _ = fp8_known_limit(out_to_f64(out), ref_out, _allowance(rq, rk, rv, w), what)
+    else:
+        md, mn = check_fp8(out_to_f64(out), ref_out, what)
     if with_lse:
         dl = np.abs(lse.cpu().numpy() - ref_lse)
-        # the FP8 LSE comes from the rounded probabilities; one e4m3 rounding
-        # moves a row sum by at most 2^-4 relative, i.e. < 0.065 nats
-        assert np.all(np.isfinite(dl)) and dl.max() < 0.065, f"max|dLSE|={dl.max():.3e}"
+        # the FP8 LSE comes from the rounded probabilities (parity.FP8_LSE_MAX)
+        lim = FP8_PRECISE_LSE_MAX if p_mode == "precise" else FP8_LSE_MAX
+        assert np.all(np.isfinite(dl)) and dl.max() < lim, f"max|dLSE|={dl.max():.3e}"
     return md, mn
 
 
@@ -138,14 +150,29 @@ def test_tile_heights_agree_bitwise(B, S, H, Hk, dqk, p_mode):
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
 
 
-@pytest.mark.parametrize("p_mode", ["exact", "lean"])
+@pytest.mark.parametrize("B,S,H,Hk,dqk,layout", [
+    (1, 256, 4, 4, 128, "bshd"),
+    (2, 700, 4, 2, 128, "bshd"),
+    (1, 1000, 4, 1, 128, "bhsd"),
+    (1, 600, 2, 2, 192, "bhsd"),
+    (2, 520, 3, 3, 192, "bshd"),
+    (1, 1, 2, 1, 128, "bshd"),
+    (1, 129, 2, 2, 192, "bshd"),
+    (1, 4097, 2, 1, 128, "bshd"),
+])
+def test_precise_small_shapes(B, S, H, Hk, dqk, layout):
+    w = Workload("small_fp8", B, S, H, Hk, dqk, 128, layout, ("fp8",), False, False, 2000 + S)
+    run_case(w, with_lse=True, p_mode="precise")
+
+
+@pytest.mark.parametrize("p_mode", ["exact", "lean", "precise"])
 @pytest.mark.parametrize("dqk", [128, 192])
 def test_modes_meet_the_gate(p_mode, dqk):
     w = Workload("mode_fp8", 1, 1100, 4, 2, dqk, 128, "bshd", ("fp8",), False, False, 77 + dqk)
     run_case(w, with_lse=True, p_mode=p_mode)
 
 
-@pytest.mark.parametrize("p_mode", ["default", "exact", "lean"])
+@pytest.mark.parametrize("p_mode", ["default", "exact", "lean", "precise"])
 @pytest.mark.parametrize("B,S,H,Hk,dqk,layout", [
     (1, 700, 4, 2, 128, "bshd"),
     (2, 389, 2, 1, 128, "bhsd"),
@@ -167,7 +194,7 @@ def test_rounding_matches_fp8_oracle(p_mode, B, S, H, Hk, dqk, layout, tile_q):
     for b in range(B):
         for h in range(H):
             ro, rl = fp8_rounding_model.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=layout,
-                                                   p_mode=oracle_p_mode(p_mode, dqk))
+                                                   p_mode=model_p_mode(p_mode, dqk))
             gots.append(o[b, :, h] if layout == "bshd" else o[b, h])
             glse.append(l[b, h])
             refs.append(ro)
@@ -176,8 +203,31 @@ def test_rounding_matches_fp8_oracle(p_mode, B, S, H, Hk, dqk, layout, tile_q):
                        f"{p_mode} d{dqk} S{S}")
 
 
-def test_activation_like_small():
+def test_activation_like_small_known_limit():
     run_case(WORKLOADS[5].resized(batch=1, seqlen=1536, name="act_small_fp8"))
+
+
+def test_activation_like_small_precise():
+    """The precise mode on activation-like inputs: every row of a 1536-token
+    slice of workload 5's generator at the full FP8 gate and the precise LSE
+    bound, and sampled rows against the rounding model."""
+    w = WORKLOADS[5].resized(batch=1, seqlen=1536, name="act_small_fp8")
+    run_case(w, with_lse=True, p_mode="precise")
+    q, k, v = generate(w)
+    (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
+    out, lse = zy.zyfa_fwd(q8, k8, v8, return_lse=True, q_descale=qs, k_descale=ks, v_descale=vs, p_mode="precise")
+    torch.cuda.synchronize()
+    o, l = out_to_f64(out), lse.cpu().numpy().astype(np.float64)
+    rows = np.unique(np.concatenate([np.arange(0, 300), np.random.default_rng(15).integers(300, w.seqlen, 200)]))
+    gots, glse, refs, rlse = [], [], [], []
+    for h in (0, 5, 17, 31):
+        ro, rl = fp8_rounding_model.fp8_attention_rows_ref(rq, rk, rv, 0, h, rows, p_mode="precise")
+        gots.append(o[0, rows, h])
+        glse.append(l[0, h, rows])
+        refs.append(ro)
+        rlse.append(rl)
+    check_fp8_rounding(np.concatenate(gots), np.concatenate(refs), np.concatenate(glse), np.concatenate(rlse),
+                       "act_small precise rounding")
 
 
 def _sample_rows(S, rng, n=24):
@@ -192,38 +242,47 @@ def test_full_size_sampled_rows(wid):
     _full_size_sampled_rows(WORKLOADS[wid], wid)
 
 
+@pytest.mark.parametrize("wid", [3, 4, 5])
+def test_full_size_sampled_rows_precise(wid):
+    _full_size_sampled_rows(WORKLOADS[wid], wid, p_mode="precise")
+
+
 def test_one_gpu_share_of_workload3():
     # one GPU's share when workload 3's heads are split over 8 GPUs in whole
     # GQA groups: 4 query heads over 1 KV head, 16384 tokens (128 jobs)
     _full_size_sampled_rows(WORKLOADS[3].resized(nheads=4, nheads_k=1, name="gqa_fp8_s16384_share8"), 33)
 
 
-def _full_size_sampled_rows(w, wid):
+def _full_size_sampled_rows(w, wid, p_mode="default"):
     q, k, v = generate(w)
-    print(f"case full fp8 {w.name}", flush=True)
+    print(f"case full fp8 {w.name} {p_mode}", flush=True)
     (q8, qs, rq), (k8, ks, rk), (v8, vs, rv) = quantize_both(q), quantize_both(k), quantize_both(v)
-    out = zy.zyfa_fwd(q8, k8, v8, layout=w.layout, q_descale=qs, k_descale=ks, v_descale=vs)
+    out = zy.zyfa_fwd(q8, k8, v8, layout=w.layout, q_descale=qs, k_descale=ks, v_descale=vs, p_mode=p_mode)
     torch.cuda.synchronize()
     o = out_to_f64(out)
     rng = np.random.default_rng(wid)
     gots, refs, extras, rrefs = [], [], [], []
     hv = lambda x: np.swapaxes(x, 1, 2) if w.layout == "bshd" else x
+    known_limit = w.activation_like and p_mode != "precise"
     for b in range(w.batch):
         for h in sorted(set([0, w.nheads - 1] + rng.integers(0, w.nheads, 2).tolist())):
             rows = _sample_rows(w.seqlen, rng)
             ro, _ = oracle.causal_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout)
             gots.append(o[b, rows, h] if w.layout == "bshd" else o[b, h, rows])
             refs.append(ro)
-            if not w.activation_like:
+            if not known_limit:
                 rr, _ = fp8_rounding_model.fp8_attention_rows_ref(rq, rk, rv, b, h, rows, layout=w.layout,
-                                                      p_mode=oracle_p_mode("default", w.d_qk))
+                                                                  p_mode=model_p_mode(p_mode, w.d_qk))
                 rrefs.append(rr)
-            hk = h // (w.nheads // w.nheads_k)
-            extras.append(fp8_score_allowance(hv(rq)[b, h], hv(rk)[b, hk], hv(rv)[b, hk], w.softmax_scale, rows)
-                          if w.activation_like else np.zeros(len(rows)))
-    check_fp8(np.concatenate(gots), np.concatenate(refs), w.name, extra=np.concatenate(extras))
-    if rrefs:
-        check_fp8_rounding(np.concatenate(gots), np.concatenate(rrefs), None, None, w.name + " rounding")
+            else:
+                hk = h // (w.nheads // w.nheads_k)
+                extras.append(fp8_score_allowance(hv(rq)[b, h], hv(rk)[b, hk], hv(rv)[b, hk], w.softmax_scale, rows))
+    what = f"{w.name} {p_mode}"
+    if known_limit:
+        fp8_known_limit(np.concatenate(gots), np.concatenate(refs), np.concatenate(extras), what)
+    else:
+        check_fp8(np.concatenate(gots), np.concatenate(refs), what)
+        check_fp8_rounding(np.concatenate(gots), np.concatenate(rrefs), None, None, what + " rounding")
 
 
 def test_bitwise_deterministic():

@@ -1,8 +1,11 @@
-"""The C ABI under HIP graph capture: after the plan (and the quantizer's
-scratch) exist, zyfa_fwd, zyfa_fp8_quantize, zyfa_fwd_range and
-zyfa_lse_merge allocate nothing and copy nothing from the host, so they can
-be captured; every replay must reproduce the eager results bit for bit, with
-eager work and synchronizations between replays."""
+"""The C ABI under HIP graph capture: once the plan of a shape exists,
+zyfa_fwd, zyfa_fwd_range, zyfa_lse_merge (and zyfa_fp8_quantize always)
+allocate nothing and copy nothing from the host, so they can be captured;
+every replay must reproduce the eager results bit for bit, with eager work
+and synchronizations between replays. A call that would have to build a
+plan under capture returns ZYFA_ERR_CAPTURE without enqueueing anything
+("ZYFA" README, Usage: run each new shape once before capturing), and the
+stream stays usable."""
 import numpy as np
 import pytest
 import torch
@@ -20,7 +23,7 @@ def test_graph_replays_match_eager():
     q, k, v = generate(w)
     tq, tk, tv = (bf16_pair(x)[0] for x in (q, k, v))
     print("case graph capture B1 S700 H4/2 d128", flush=True)
-    # eager results (also builds the plans and the quantizer scratch)
+    # eager results (also builds the plans)
     out_e, lse_e = zy.zyfa_fwd(tq, tk, tv, return_lse=True)
     (q8e, qse), (k8e, kse), (v8e, vse) = (zy.zyfa_fp8_quantize(x) for x in (tq, tk, tv))
     out8_e = zy.zyfa_fwd(q8e, k8e, v8e, q_descale=qse, k_descale=kse, v_descale=vse)
@@ -71,3 +74,41 @@ def test_graph_replays_match_eager():
         assert torch.equal(q8.view(torch.uint8), q8e.view(torch.uint8)) and torch.equal(qs, qse), f"replay {i}: quantize"
         assert torch.equal(out8_g, out8_e), f"replay {i}: fp8 differs"
         assert torch.equal(om_g, om_e) and torch.equal(lm_g, lm_e), f"replay {i}: range/merge differs"
+
+
+def test_unprepared_shape_under_capture_returns_capture_error():
+    w = Workload("capture", 1, 333, 4, 2, 128, 128, "bshd", ("bf16", "fp8"), True, False, 92)
+    q, k, v = generate(w)
+    tq, tk, tv = (bf16_pair(x)[0] for x in (q, k, v))
+    (q8, qs), (k8, ks), (v8, vs) = (zy.zyfa_fp8_quantize(x) for x in (tq, tk, tv))
+    out = torch.empty((1, 333, 4, 128), dtype=torch.bfloat16, device="cuda")
+    zy.zyfa_release()      # no plan exists for any shape now
+    torch.cuda.synchronize()
+    print("case capture error path B1 S333 H4/2 d128", flush=True)
+    errors = []
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for call in (lambda: zy.zyfa_prepare(1, 333, 4, 2, 128, 128, stream=s),
+                     lambda: zy.zyfa_fwd(tq, tk, tv, out, stream=s),
+                     lambda: zy.zyfa_fwd(q8, k8, v8, out, q_descale=qs, k_descale=ks, v_descale=vs,
+                                         p_mode="precise", stream=s),
+                     lambda: zy.zyfa_fwd_range(tq, tk, tv, 0, 0, out, stream=s)):
+            try:
+                call()
+            except zy.ZyfaError as e:
+                errors.append(e.status)
+        zy.zyfa_fp8_quantize(tq, q8, qs, stream=s)   # needs no plan: captured
+    assert errors == [zy.STATUS["ZYFA_ERR_CAPTURE"]] * 4, errors
+    # the stream (and the library) stay usable: prepare, then the same calls
+    zy.zyfa_prepare(1, 333, 4, 2, 128, 128, dtype=zy.DTYPE_FP8, stream=s)
+    zy.zyfa_prepare(1, 333, 4, 2, 128, 128, stream=s)
+    with torch.cuda.stream(s):
+        o1 = zy.zyfa_fwd(tq, tk, tv, stream=s)
+        o2 = zy.zyfa_fwd(q8, k8, v8, q_descale=qs, k_descale=ks, v_descale=vs, p_mode="precise", stream=s)
+    s.synchronize()
+    ref = zy.zyfa_fwd(tq, tk, tv)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, ref) and torch.isfinite(o2.float()).all()
+    g.replay()       # the captured quantize alone
+    torch.cuda.synchronize()

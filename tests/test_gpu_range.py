@@ -5,8 +5,8 @@ import pytest
 import torch
 
 import oracle
-from parity import (BF16_OUT_ABS, BF16_OUT_REL_ROUND, bf16_pair, check_bf16, check_partial, out_to_f64,
-                    tile_height)
+from parity import (BF16_OUT_ABS, BF16_OUT_REL_ROUND, FP8_LSE_MAX, FP8_OUT_MAX, FP8_OUT_MEAN,
+                    FP8_PRECISE_LSE_MAX, bf16_pair, check_bf16, check_partial, out_to_f64, tile_height)
 from workloads import WORKLOADS, Workload, generate
 
 pytestmark = pytest.mark.gpu
@@ -38,6 +38,8 @@ CASES = [
     (1, 700, 700, 37, 0, 3, 1, 128, "bshd"),       # offset not a tile multiple
     (1, 129, 1, 5, 5, 2, 1, 128, "bshd"),          # one key
     (1, 1000, 4097, 3097, 0, 2, 1, 192, "bshd"),   # several tiles each way, ragged
+    (1, 300, 200, 2000, 0, 2, 1, 128, "bshd"),     # fewer than 256 keys, all before the queries
+    (1, 520, 230, 5000, 0, 2, 2, 192, "bhsd"),     # the same at d_qk 192
 ]
 
 
@@ -58,12 +60,9 @@ def test_range_bf16(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, with_lse, tile_q):
     check_partial(out_to_f64(out), ro, l, _lse_rows(rl, layout), f"range bf16 Sq{Sq} Sk{Sk} {qp}/{kp}")
 
 
-@pytest.mark.parametrize("B,Sq,Sk,qp,kp,H,Hk,dqk,layout", [CASES[0], CASES[2], CASES[3], CASES[4], CASES[7]])
-@pytest.mark.parametrize("tile_q", [256, 128])
-def test_range_fp8(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, tile_q):
-    print(f"case range fp8 B{B} Sq{Sq} Sk{Sk} q_pos0={qp} k_pos0={kp} H{H}/{Hk} d{dqk} {layout} tile_q {tile_q}",
-          flush=True)
-    q, k, v = _draw(B, Sq, Sk, H, Hk, dqk, layout, 4000 + Sq + Sk)
+def _fp8_inputs(q, k, v):
+    """GPU quantize of each tensor, checked bit for bit against the oracle's;
+    returns ([(codes, descale)] on the GPU, [oracle dequantized values])."""
     deq, dev = [], []
     for x in (q, k, v):
         t, r = bf16_pair(x)
@@ -72,17 +71,68 @@ def test_range_fp8(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, tile_q):
         assert np.array_equal(x8.view(torch.uint8).cpu().numpy(), codes) and float(ds.item()) == float(d)
         deq.append(oracle.e4m3fn_decode(codes) * float(d))
         dev.append((x8, ds))
-    (q8, qs), (k8, ks), (v8, vs) = dev
+    return dev, deq
+
+
+@pytest.mark.parametrize("B,Sq,Sk,qp,kp,H,Hk,dqk,layout", [CASES[i] for i in (0, 1, 2, 3, 4, 7, 8, 9)])
+@pytest.mark.parametrize("tile_q,p_mode", [(256, "default"), (128, "default"), (128, "precise")])
+def test_range_fp8(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, tile_q, p_mode):
+    print(f"case range fp8 B{B} Sq{Sq} Sk{Sk} q_pos0={qp} k_pos0={kp} H{H}/{Hk} d{dqk} {layout} tile_q {tile_q} "
+          f"{p_mode}", flush=True)
+    q, k, v = _draw(B, Sq, Sk, H, Hk, dqk, layout, 4000 + Sq + Sk)
+    ((q8, qs), (k8, ks), (v8, vs)), deq = _fp8_inputs(q, k, v)
     with tile_height(zy, B, Sq, H, Hk, dqk, zy.DTYPE_FP8, tile_q):
-        out, lse = zy.zyfa_fwd_range(q8, k8, v8, qp, kp, layout=layout, q_descale=qs, k_descale=ks, v_descale=vs)
+        out, lse = zy.zyfa_fwd_range(q8, k8, v8, qp, kp, layout=layout, q_descale=qs, k_descale=ks, v_descale=vs,
+                                     p_mode=p_mode)
     torch.cuda.synchronize()
     ro, rl = oracle.range_attention_ref(*deq, qp, kp, layout=layout)
-    # the FP8 LSE comes from the rounded probabilities: compare only where it
-    # must be -inf; its value is held by the whole-sequence FP8 tests
-    empty = np.isneginf(_lse_rows(rl, layout))
     got_l = _lse_rows(lse.cpu().numpy().astype(np.float64), layout)
-    assert np.array_equal(np.isneginf(got_l), empty)
-    check_partial(out_to_f64(out), ro, None, _lse_rows(rl, layout), f"range fp8 Sq{Sq} Sk{Sk}", fp8=True)
+    # out and the LSE (from the rounded probabilities) at the FP8 bounds
+    check_partial(out_to_f64(out), ro, got_l, _lse_rows(rl, layout), f"range fp8 Sq{Sq} Sk{Sk}", fp8=True)
+    if p_mode == "precise":
+        live = ~np.isneginf(_lse_rows(rl, layout))
+        dl = np.abs(got_l - _lse_rows(rl, layout))[live]
+        assert dl.size == 0 or dl.max() < FP8_PRECISE_LSE_MAX, f"max|dLSE|={dl.max():.3e}"
+
+
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+@pytest.mark.parametrize("split", [100, 256, 611])
+@pytest.mark.parametrize("p_mode", ["default", "precise"])
+def test_fp8_split_and_merge_is_whole_attention(layout, split, p_mode):
+    """FP8 keys [0, split) and [split, S) as two range calls (one descale per
+    tensor, the codes split), merged on the GPU, against fp64 attention on
+    the dequantized inputs over all keys: the merge is consistent because
+    each partial's LSE comes from the same rounded probabilities as its
+    output. Allowance: the FP8 gate plus the bf16 rounding of the two
+    partial outputs carried through their weights."""
+    B, S, H, Hk, dqk = 1, 700, 4, 2, 128
+    print(f"case fp8 split-merge {layout} split={split} {p_mode}", flush=True)
+    q, k, v = _draw(B, S, S, H, Hk, dqk, layout, 5100 + split)
+    ((q8, qs), (k8, ks), (v8, vs)), (rq, rk, rv) = _fp8_inputs(q, k, v)
+    ksl = (lambda x, a, b: x[:, a:b]) if layout == "bshd" else (lambda x, a, b: x[:, :, a:b])
+    parts, refs = [], []
+    for a, b in ((0, split), (split, S)):
+        kk, vv = ksl(k8, a, b).contiguous(), ksl(v8, a, b).contiguous()
+        parts.append(zy.zyfa_fwd_range(q8, kk, vv, 0, a, layout=layout, q_descale=qs, k_descale=ks, v_descale=vs,
+                                       p_mode=p_mode))
+        refs.append(oracle.range_attention_ref(rq, ksl(rk, a, b), ksl(rv, a, b), 0, a, layout=layout))
+    out, lse = zy.zyfa_lse_merge(parts[0][0], parts[0][1], parts[1][0], parts[1][1], layout=layout)
+    torch.cuda.synchronize()
+    fo, fl = oracle.causal_attention_ref(rq, rk, rv, layout=layout)
+    got, gl = out_to_f64(out), lse.cpu().numpy().astype(np.float64)
+    (oa, la), (ob, lb) = refs
+    m = np.maximum(la, lb)
+    wa, wb = np.exp(la - m), np.exp(lb - m)
+    wa, wb = _lse_rows(wa / (wa + wb), layout)[..., None], _lse_rows(wb / (wa + wb), layout)[..., None]
+    carry = BF16_OUT_REL_ROUND * (wa * np.abs(oa) + wb * np.abs(ob))
+    d = np.abs(got - fo)
+    bound = FP8_OUT_MAX + BF16_OUT_REL_ROUND * np.abs(fo) + carry
+    print(f"fp8 split-merge: max|dout|={d.max():.3e} mean={d.mean():.2e} max|dLSE|={np.abs(gl - fl).max():.3e}",
+          flush=True)
+    assert np.all(d <= bound), f"max|dout|={d.max():.3e}"
+    assert d.mean() <= FP8_OUT_MEAN, f"mean|dout|={d.mean():.3e}"
+    lim = FP8_PRECISE_LSE_MAX if p_mode == "precise" else FP8_LSE_MAX
+    assert np.all(np.abs(gl - fl) < lim), f"max|dLSE|={np.abs(gl - fl).max():.3e}"
 
 
 @pytest.mark.parametrize("layout", ["bshd", "bhsd"])
