@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "zyfa.h"
+#include "args.h"
 #include "plan.h"
 #include "zyfa_internal.h"
 
@@ -59,15 +60,6 @@ bool stream_capturing(hipStream_t s) {
   return st != hipStreamCaptureStatusNone;
 }
 
-int check_shape(int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype) {
-  if (batch <= 0 || seqlen <= 0 || nheads <= 0 || nheads_k <= 0) return ZYFA_ERR_SHAPE;
-  if (!((d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128))) return ZYFA_ERR_HEADDIM;
-  if (nheads % nheads_k != 0) return ZYFA_ERR_GQA;
-  if (dtype != ZYFA_DTYPE_BF16 && dtype != ZYFA_DTYPE_FP8_E4M3FN) return ZYFA_ERR_DTYPE;
-  if (layout != ZYFA_LAYOUT_BSHD && layout != ZYFA_LAYOUT_BHSD) return ZYFA_ERR_LAYOUT;
-  return ZYFA_OK;
-}
-
 // Finds or builds the plan of a shape (shape.tile_q == 0): with tile_q
 // rows when given, else with the height set for the shape, else the
 // automatic one; caller holds g_mu.
@@ -101,20 +93,7 @@ int get_plan(const PlanKey& shape, hipStream_t stream, const Plan** out, int til
   return ZYFA_OK;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// Strides (elements) of a (batch, heads, seqlen, dim) view of a contiguous tensor.
-void strides(int layout, int seqlen, int heads, int dim, long long* sb, long long* sh, long long* ss) {
-  if (layout == ZYFA_LAYOUT_BSHD) {
-    *sb = (long long)seqlen * heads * dim;
-    *sh = dim;
-    *ss = (long long)heads * dim;
-  } else {
-    *sb = (long long)heads * seqlen * dim;
-    *sh = (long long)seqlen * dim;
-    *ss = dim;
-  }
-}
+bool aligned16(const void* p) { return aligned(p, 16); }
 
 // Whole-sequence attention is the range call with seqlen_q == seqlen_k and
 // q_pos0 == k_pos0.
@@ -124,7 +103,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
              float softmax_scale, int p_mode, void* stream_) {
   int rc = check_shape(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype);
   if (rc) return rc;
-  if (seqlen_k <= 0) return ZYFA_ERR_SHAPE;
+  if (seqlen_k <= 0 || seqlen_k > kMaxSeqlen) return ZYFA_ERR_SHAPE;
   if (p_mode != ZYFA_P_DEFAULT && p_mode != ZYFA_P_EXACT && p_mode != ZYFA_P_LEAN && p_mode != ZYFA_P_PRECISE)
     return ZYFA_ERR_PMODE;
   if (!q || !k || !v || !out) return ZYFA_ERR_NULL;
@@ -147,21 +126,17 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   a.q.ptr = q;
   a.k.ptr = k;
   a.v.ptr = v;
-  strides(layout, seqlen, nheads, d_qk, &a.q.stride_b, &a.q.stride_h, &a.q.stride_s);
-  strides(layout, seqlen_k, nheads_k, d_qk, &a.k.stride_b, &a.k.stride_h, &a.k.stride_s);
-  strides(layout, seqlen_k, nheads_k, d_v, &a.v.stride_b, &a.v.stride_h, &a.v.stride_s);
-  strides(layout, seqlen, nheads, d_v, &a.o_stride_b, &a.o_stride_h, &a.o_stride_s);
+  layout_strides(layout, seqlen, nheads, d_qk, &a.q.stride_b, &a.q.stride_h, &a.q.stride_s);
+  layout_strides(layout, seqlen_k, nheads_k, d_qk, &a.k.stride_b, &a.k.stride_h, &a.k.stride_s);
+  layout_strides(layout, seqlen_k, nheads_k, d_v, &a.v.stride_b, &a.v.stride_h, &a.v.stride_s);
+  layout_strides(layout, seqlen, nheads, d_v, &a.o_stride_b, &a.o_stride_h, &a.o_stride_s);
   a.out = out;
   a.lse = lse;
   a.batch = batch;
   a.seqlen_q = seqlen;
   a.seqlen_k = seqlen_k;
-  // key c is visible to query row r when c <= r + delta. Offsets past
-  // seqlen_k (every key visible) or below -(seqlen_q + 512) (none visible)
-  // act alike, so delta is clamped there and the kernels' index sums stay
-  // far inside int.
-  const long long dl = q_pos0 - k_pos0;
-  a.delta = (int)std::max(-(long long)seqlen - 512, std::min(dl, (long long)seqlen_k));
+  // key c is visible to query row r when c <= r + delta
+  a.delta = clamp_delta(q_pos0, k_pos0, seqlen, seqlen_k);
   a.nheads = nheads;
   a.nheads_k = nheads_k;
   a.n_qtiles = plan->n_qtiles;
@@ -177,9 +152,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   // most 64 rows) through a buffer resource of its own with a 64-bit base,
   // so only 64 rows of a tensor must fit in 31 bits of byte offset; tensors
   // and (batch, head) slices may span more than 4 GiB.
-  auto local = [&](long long ss, int dim) { return (64 * ss + dim) * esz; };
-  const long long lim = 0x7FFFFFFFll;
-  if (local(a.q.stride_s, d_qk) > lim || local(a.k.stride_s, d_qk) > lim || local(a.v.stride_s, d_v) > lim)
+  if (!rows_in_31_bits(a.q.stride_s, d_qk, esz) || !rows_in_31_bits(a.k.stride_s, d_qk, esz) ||
+      !rows_in_31_bits(a.v.stride_s, d_v, esz))
     return ZYFA_ERR_RANGE;
 
   hipError_t e;
@@ -206,14 +180,9 @@ int quantize_rotated_impl(const void* x, int x_dtype, long long rows, int d, con
                           void* stream_) {
   if (x_dtype != ZYFA_DTYPE_BF16 && x_dtype != ZYFA_DTYPE_FP32) return ZYFA_ERR_DTYPE;
   if (rows < 0) return ZYFA_ERR_SHAPE;
-  if (d != 128 && d != 192) return ZYFA_ERR_HEADDIM;
-  unsigned mask[6] = {0, 0, 0, 0, 0, 0};
-  if (signs) {
-    for (int i = 0; i < d; ++i) {
-      if (signs[i] != 1 && signs[i] != -1) return ZYFA_ERR_SIGNS;
-      if (signs[i] < 0) mask[i >> 5] |= 1u << (i & 31);
-    }
-  }
+  unsigned mask[6];
+  const int rc = sign_mask(signs, d, mask);
+  if (rc) return rc;
   if (!descale || (rows > 0 && (!x || !x8))) return ZYFA_ERR_NULL;
   if (rows > 0 && (!aligned16(x) || !aligned16(x8))) return ZYFA_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(descale) & 3u) return ZYFA_ERR_ALIGN;

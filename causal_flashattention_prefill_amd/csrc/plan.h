@@ -24,4 +24,26 @@ struct JobTable {
 // consecutive jobs (same head, hence the same K/V in that XCD's L2).
 JobTable build_job_table(int batch, int seqlen, int nheads, int nheads_k, int tile_q, int num_cus);
 
+constexpr int kNumXcd = 8;
+
+// Entry (row r, workgroup w) of the job table as {bh, tile} (bh = batch *
+// nheads + head; the job covers query tiles tile and n - 1 - tile), or
+// {-1, -1} past the last job. Jobs are numbered j = bh * pairs + tile
+// (batch, then KV head, then the query heads of its group, which are
+// consecutive, then pairs); row r hands out jobs r * num_wgs .. in XCD
+// order: the workgroups of XCD 0 (w % 8 == 0, by increasing w), then those
+// of XCD 1, and so on. A constexpr function, so the host plan and the
+// device-side table builder share this one definition.
+struct JobEntry {
+  int bh, tile;
+};
+constexpr JobEntry job_entry(int r, int w, long long njobs, int num_wgs, int pairs) {
+  const int x = w % kNumXcd;
+  long long before = 0;   // workgroups of the XCDs before x
+  for (int y = 0; y < x; ++y) before += (num_wgs - y + kNumXcd - 1) / kNumXcd;
+  const long long j = (long long)r * num_wgs + before + w / kNumXcd;
+  if (j >= njobs) return JobEntry{-1, -1};
+  return JobEntry{(int)(j / pairs), (int)(j % pairs)};
+}
+
 }  // namespace zyfa
