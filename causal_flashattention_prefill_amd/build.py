@@ -24,6 +24,10 @@ EXTRA_FLAGS = {
     "attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 BUILD_DIR = os.path.join(HERE, "_build")
+# The MFMA-shape microbenchmark (bench_mfma_shapes.py): its own library, not
+# part of the attention library.
+MB_SOURCE = "mfma_shapes.hip"
+MB_LIB = os.path.join(HERE, "libzyfa_mfma_shapes.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -76,6 +80,13 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(out)
         raise RuntimeError("hipcc failed to link libzyfa.so")
     os.replace(tmp, LIB)
+    tmp = MB_LIB + ".tmp"
+    p = _run([hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, MB_SOURCE), "-o", tmp], verbose)
+    out, _ = p.communicate()
+    if p.returncode != 0:
+        sys.stderr.write(out)
+        raise RuntimeError("hipcc failed to build the MFMA-shape microbenchmark")
+    os.replace(tmp, MB_LIB)
     return LIB
 
 
