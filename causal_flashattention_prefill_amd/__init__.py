@@ -28,6 +28,7 @@ STATUS = {
     "ZYFA_ERR_NULL": -1, "ZYFA_ERR_SHAPE": -2, "ZYFA_ERR_HEADDIM": -3, "ZYFA_ERR_GQA": -4,
     "ZYFA_ERR_DTYPE": -5, "ZYFA_ERR_LAYOUT": -6, "ZYFA_ERR_DESCALE": -7, "ZYFA_ERR_CAPTURE": -8,
     "ZYFA_ERR_HIP": -9, "ZYFA_ERR_RANGE": -10, "ZYFA_ERR_ALIGN": -11, "ZYFA_ERR_PMODE": -12, "ZYFA_ERR_SIGNS": -13,
+    "ZYFA_ERR_SCRATCH": -14,
 }
 # FP8 probability modes (zyfa_p_mode): default = lean P below the diagonal at
 # d_qk 128, exact P at d_qk 192; precise = bf16-MFMA scores and P split into
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.zyfa_fwd.restype = i
     L.zyfa_fwd_ex.argtypes = fwd_args + [f, i, vp]
     L.zyfa_fwd_ex.restype = i
+    L.zyfa_fwd_noalloc.argtypes = fwd_args + [f, i, vp]
+    L.zyfa_fwd_noalloc.restype = i
     L.zyfa_fwd_range.argtypes = [vp, vp, vp, vp, vp, i, i, i, ll, ll, i, i, i, i, i, i, vp, vp, vp, f, i, vp]
     L.zyfa_fwd_range.restype = i
     L.zyfa_lse_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
@@ -156,6 +159,28 @@ def zyfa_fwd(q, k, v, out=None, lse=None, *, layout: str = "bshd", return_lse: b
         rc = L.zyfa_fwd_ex(*args, 0.0 if softmax_scale is None else float(softmax_scale), P_MODES[p_mode],
                            _stream(stream))
     _check(rc, "zyfa_fwd")
+    return (out, lse) if lse is not None else out
+
+
+def zyfa_fwd_noalloc(q, k, v, out, lse=None, *, layout: str = "bshd", q_descale=None, k_descale=None,
+                     v_descale=None, softmax_scale: Optional[float] = None, p_mode: str = "default", stream=None):
+    """zyfa_fwd into caller-given out (and lse) with no device allocation by
+    the library: the job table goes into its static buffer (see
+    zyfa_fwd_noalloc in zyfa.h; overlapping calls on one GPU race). Returns
+    out, or (out, lse)."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    if p_mode not in P_MODES:
+        raise ValueError(f"p_mode must be one of {list(P_MODES)}")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k and v must be contiguous")
+    B, S, H, Hk, dqk, dv = _dims(q, k, v, layout)
+    rc = lib().zyfa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S, H, Hk, dqk, dv,
+                                LAYOUTS[layout], _dtype_code(q), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+                                0.0 if softmax_scale is None else float(softmax_scale), P_MODES[p_mode],
+                                _stream(stream))
+    _check(rc, "zyfa_fwd_noalloc")
     return (out, lse) if lse is not None else out
 
 

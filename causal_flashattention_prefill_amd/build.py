@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libzyfa.so")
 
-SOURCES = ["api.cpp", "args.cpp", "plan.cpp", "attn_bf16.hip", "attn_fp8.hip", "fp8_quantize.hip", "lse_merge.hip"]
+SOURCES = ["api.cpp", "args.cpp", "plan.cpp", "attn_bf16.hip", "attn_fp8.hip", "fp8_quantize.hip", "lse_merge.hip", "noalloc.hip"]
 # Extra flags per source. The attention kernels never see NaN scores, so
 # max/min need no NaN quieting (IEEE mode off): without this every fmaxf of
 # a matrix-instruction result costs an extra canonicalising instruction.

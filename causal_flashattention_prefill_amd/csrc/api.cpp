@@ -97,10 +97,12 @@ bool aligned16(const void* p) { return aligned(p, 16); }
 
 // Whole-sequence attention is the range call with seqlen_q == seqlen_k and
 // q_pos0 == k_pos0.
+// noalloc: no plan cache; the job table is written by a kernel into the
+// library's static buffer (zyfa_fwd_noalloc).
 int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen,
              int seqlen_k, long long q_pos0, long long k_pos0, int nheads, int nheads_k, int d_qk, int d_v,
              int layout, int dtype, const float* q_descale, const float* k_descale, const float* v_descale,
-             float softmax_scale, int p_mode, void* stream_) {
+             float softmax_scale, int p_mode, void* stream_, bool noalloc = false) {
   int rc = check_shape(batch, seqlen, nheads, nheads_k, d_qk, d_v, layout, dtype);
   if (rc) return rc;
   if (seqlen_k <= 0 || seqlen_k > kMaxSeqlen) return ZYFA_ERR_SHAPE;
@@ -117,10 +119,32 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   if ((rc = current_device(&dev))) return rc;
   std::lock_guard<std::mutex> lock(g_mu);
   const Plan* plan = nullptr;
+  Plan na_plan;   // noalloc: the plan's sizes, its table in the static buffer
   PlanKey key{dev, batch, seqlen, nheads, nheads_k, d_qk, dtype, 0};
   // the precise FP8 mode runs on 128-row query tiles only
   const bool precise = dtype == ZYFA_DTYPE_FP8_E4M3FN && p_mode == ZYFA_P_PRECISE;
-  if ((rc = get_plan(key, stream, &plan, precise ? 128 : 0))) return rc;
+  if (noalloc) {
+    const auto ch = g_tile_choice.find(key);
+    const int tq = precise ? 128 : ch != g_tile_choice.end() ? ch->second
+                                                            : tile_q_rows(batch, seqlen, nheads, d_qk, dtype,
+                                                                          num_cus(dev));
+    const int n_qtiles = (seqlen + tq - 1) / tq;
+    const int pairs = (n_qtiles + 1) / 2;
+    const long long njobs = (long long)batch * nheads * pairs;
+    const long long wgs = std::max<long long>(1, std::min<long long>(njobs, num_cus(dev)));
+    const long long rows = (njobs + wgs - 1) / wgs;
+    if (rows * wgs > noalloc_scratch_entries()) return ZYFA_ERR_SCRATCH;
+    int2* table = nullptr;
+    if (noalloc_scratch(dev, &table) != hipSuccess) return ZYFA_ERR_HIP;
+    na_plan.jobs = table;
+    na_plan.num_wgs = (int)wgs;
+    na_plan.jobs_per_wg = (int)rows;
+    na_plan.n_qtiles = n_qtiles;
+    na_plan.tile_q = tq;
+    plan = &na_plan;
+  } else if ((rc = get_plan(key, stream, &plan, precise ? 128 : 0))) {
+    return rc;
+  }
 
   AttnArgs a{};
   a.q.ptr = q;
@@ -157,6 +181,12 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
     return ZYFA_ERR_RANGE;
 
   hipError_t e;
+  if (noalloc) {
+    const int pairs = (plan->n_qtiles + 1) / 2;
+    e = launch_build_jobs(const_cast<int2*>(plan->jobs), plan->jobs_per_wg, plan->num_wgs,
+                          (long long)batch * nheads * pairs, pairs, stream);
+    if (e != hipSuccess) return ZYFA_ERR_HIP;
+  }
   if (dtype == ZYFA_DTYPE_BF16)
     e = launch_attn_bf16(a, d_qk, lse != nullptr, plan->tile_q, plan->num_wgs, stream);
   else
@@ -216,6 +246,13 @@ int zyfa_fwd_range(const void* q, const void* k, const void* v, void* out, float
                    float softmax_scale, int p_mode, void* stream) {
   return fwd_impl(q, k, v, out, lse, batch, seqlen_q, seqlen_k, q_pos0, k_pos0, nheads, nheads_k, d_qk, d_v, layout,
                   dtype, q_descale, k_descale, v_descale, softmax_scale, p_mode, stream);
+}
+
+int zyfa_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen,
+                     int nheads, int nheads_k, int d_qk, int d_v, int layout, int dtype, const float* q_descale,
+                     const float* k_descale, const float* v_descale, float softmax_scale, int p_mode, void* stream) {
+  return fwd_impl(q, k, v, out, lse, batch, seqlen, seqlen, 0, 0, nheads, nheads_k, d_qk, d_v, layout, dtype,
+                  q_descale, k_descale, v_descale, softmax_scale, p_mode, stream, true);
 }
 
 int zyfa_lse_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,
@@ -318,6 +355,7 @@ const char* zyfa_status_string(int status) {
     case ZYFA_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case ZYFA_ERR_PMODE: return "unknown FP8 probability mode";
     case ZYFA_ERR_SIGNS: return "rotation signs must each be +1 or -1";
+    case ZYFA_ERR_SCRATCH: return "the call's job table exceeds the no-allocation buffer (65536 entries)";
     default: return "unknown status";
   }
 }

@@ -50,6 +50,12 @@ hipError_t launch_fp8_quantize_rotated(const void* x, int x_dtype, long long row
                                        float* descale, hipStream_t s);
 hipError_t launch_key_mean(const void* x, int x_dtype, int batch, int seqlen, int nheads, int d, bool bshd,
                            float* mean, hipStream_t s);
+// zyfa_fwd_noalloc: the static job-table buffer (its capacity in entries and
+// its device address on device dev, looked up on first use) and the kernel
+// that writes a job table into it.
+int noalloc_scratch_entries();
+hipError_t noalloc_scratch(int dev, int2** out);
+hipError_t launch_build_jobs(int2* table, int rows, int num_wgs, long long njobs, int pairs, hipStream_t s);
 hipError_t launch_lse_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,
                             float* lse, int batch, int seqlen, int nheads, int d_v, bool bshd, hipStream_t s);
 

@@ -40,7 +40,8 @@ enum zyfa_status {
                               slices beyond 4 GiB are fine) */
   ZYFA_ERR_ALIGN = -11,    /* a tensor pointer is not 16-byte aligned */
   ZYFA_ERR_PMODE = -12,    /* unknown FP8 probability mode */
-  ZYFA_ERR_SIGNS = -13     /* a rotation sign other than +1 or -1 */
+  ZYFA_ERR_SIGNS = -13,    /* a rotation sign other than +1 or -1 */
+  ZYFA_ERR_SCRATCH = -14   /* zyfa_fwd_noalloc: the job table exceeds the static buffer */
 };
 
 enum zyfa_layout {
@@ -130,6 +131,28 @@ int zyfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
                 int layout, int dtype,
                 const float* q_descale, const float* k_descale, const float* v_descale,
                 float softmax_scale, int p_mode, void* stream);
+
+/*
+ * zyfa_fwd_noalloc - zyfa_fwd_ex for callers that cannot allocate device
+ * memory: code under graph capture that has not called zyfa_prepare, tight
+ * serving loops, harnesses that forbid allocation. Same arguments and
+ * results (bitwise equal to zyfa_fwd_ex). Instead of the cached per-shape
+ * plan it writes the job table with a small kernel, on `stream` just before
+ * the attention kernel, into a static device buffer of the library (65536
+ * entries of 8 bytes, 512 KiB, held on each GPU the library runs on until
+ * the process ends): no hipMalloc, no hipFree, no host-to-device copy. Calls
+ * on one GPU share that buffer, so calls that overlap (other streams,
+ * parallel graph branches) race: serialize them. The buffer's address is
+ * looked up once per device on the first call there.
+ * Returns ZYFA_ERR_SCRATCH when the table (nheads * batch * ceil(tiles / 2)
+ * jobs, rounded up to a multiple of the grid) exceeds 65536 entries, e.g.
+ * beyond about 512K tokens at 32 heads; other errors as zyfa_fwd_ex.
+ */
+int zyfa_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v,
+                     int layout, int dtype,
+                     const float* q_descale, const float* k_descale, const float* v_descale,
+                     float softmax_scale, int p_mode, void* stream);
 
 /*
  * zyfa_fwd_range - causal attention of a block of queries over a range of
