@@ -39,9 +39,15 @@
 //    and the rescale runs out of line (README, Kernel design: lazy
 //    rescaling). The causal mask is applied on diagonal tiles only.
 //  - Row sums: with LSE requested, an fp32 sum of the unrounded
-//    probabilities (so the LSE holds to ~1e-7 relative); otherwise one MFMA
-//    of the bf16 P against ones per 32 keys, so the output is divided by the
-//    sum of exactly the rounded weights that multiply V.
+//    probabilities (so the LSE holds to ~1e-7 relative); otherwise the
+//    matrix unit sums the bf16 P (the post "Attention at the Power Cap",
+//    row sums on the matrix core with a 2:4 sparse ones operand), so the
+//    output is divided by the sum of exactly the rounded weights that
+//    multiply V: one v_smfmac_f32_16x16x64_bf16 per 64 keys, whose sparse
+//    A operand is all ones with even rows keeping positions {0, 1} and odd
+//    rows {2, 3} of every group of four keys, so rows 2r and 2r + 1 of the
+//    result add up to the sum over all 64 keys (half the matrix work of
+//    two dense 16x16x32 products against ones).
 //  - Every conversion rounds to nearest even (README, Kernel design).
 #include "device_common.h"
 #include "zyfa_internal.h"
@@ -104,6 +110,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   const int dl = a.delta;
   const float sl2 = a.scale_log2;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  // 2:4 sparsity index of the row-sum operand: lane n supplies row n; 2-bit
+  // positions of its two values in each of its four groups of four keys,
+  // {0, 1} (0b0100) on even rows and {2, 3} (0b1110) on odd rows
+  const int sum_idx = (n & 1) ? 0xEEEE : 0x4444;
 
   for (int it = 0; it < a.jobs_per_wg; ++it) {
     const int2 jv = a.jobs[it * a.num_wgs + wg];
@@ -276,11 +286,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
           if (!WITH_LSE) {
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-              for (int kc = 0; kc < 2; ++kc)
-                lacc[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qg][kc], lacc[qg], 0, 0, 0);
+              lacc[qg] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+                  ones, __builtin_shufflevector(pb[qg][0], pb[qg][1], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15),
+                  lacc[qg], sum_idx, 0, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPfV, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * QG, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
           }
 #pragma unroll
           for (int idx = 0; idx < 16; ++idx) {
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
             lt = lsum[qg] + swap16(lsum[qg]);
             lt += __shfl_xor(lt, 32);
           } else {
-            lt = lacc[qg][0];
+            lt = lacc[qg][0] + lacc[qg][1];   // an even and an odd row of the sparse sum
           }
           const float inv = lt > 0.f ? 1.0f / lt : 0.f;
           const int q = qw0 + 16 * qg + n;
