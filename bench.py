@@ -9,7 +9,12 @@ precise FP8 mode, workload 5, one GPU's share, partial-range calls, the LSE
 merge, the README's own configuration) is timed the same way and reported
 under `config.cases`; none of them is part of `ms_per_step`. Inputs are
 resident in HBM before timing starts. Each launch is bracketed by HIP
-events on the stream it runs on.
+events on the stream it runs on. Before its W warm-up and K timed steps,
+every case first runs back to back for --settle-seconds (1 s by default,
+the warm-up of the README's sustained protocol): right after the GPU has
+been idle, the first tens of launches of the 16K cases run up to 20 %
+slower than the steady state while the board leaves its idle power state,
+and 5 warm-up launches (5 ms) do not cover that.
 
 Throughput is causal TFLOP/s = B * H * S^2 * (d_qk + d_v) / time, the
 count of the "ZYFA" README's kernel-benchmark protocol.
@@ -125,6 +130,8 @@ def parse():
                     help="only the README configuration cases, timed with the README's kernel-benchmark protocol")
     ap.add_argument("--sustain-seconds", type=float, default=3.0,
                     help="seconds per timed run of the sustained-clock protocol on each 16K gate case (0: skip)")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="seconds of back-to-back launches before each case's warm-up and timed steps")
     return ap.parse_args()
 
 
@@ -282,10 +289,27 @@ def sustained(fn, flops: float, seconds: float, peak_tflops: float, runs: int = 
     return rec
 
 
-def time_launches(fn, steps, warmup):
-    """Average milliseconds of fn() over `steps` back-to-back launches,
-    bracketed by events on the current stream (the stream fn launches on)."""
+def settle(fn, seconds: float):
+    """Back-to-back launches of fn() for `seconds` (the board leaves its idle
+    power state), keeping the host within 16 launches of the GPU."""
     import torch
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def time_launches(fn, steps, warmup, settle_seconds: float = 0.0):
+    """Average milliseconds of fn() over `steps` back-to-back launches,
+    bracketed by events on the current stream (the stream fn launches on),
+    after `settle_seconds` of back-to-back launches and `warmup` launches."""
+    import torch
+    if settle_seconds > 0:
+        settle(fn, settle_seconds)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -386,7 +410,7 @@ def range_or_merge_case(name, zy, args):
         zy.zyfa_fwd_range(q, k[:, h2:].contiguous(), v[:, h2:].contiguous(), 0, h2, ob, lb)
         out, lse = torch.empty_like(oa), torch.empty_like(la)
         fn = lambda: zy.zyfa_lse_merge(oa, la, ob, lb, out, lse)
-        ms, _ = time_launches(fn, args.steps, args.warmup)
+        ms, _ = time_launches(fn, args.steps, args.warmup, args.settle_seconds)
         nbytes = 3 * oa.numel() * 2 + 3 * la.numel() * 4
         gbs = nbytes / (ms * 1e-3) / 1e9
         return {"gbs": round(gbs, 1), "ms": round(ms, 4), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -403,7 +427,7 @@ def range_or_merge_case(name, zy, args):
         fn = lambda: zy.zyfa_fwd_range(q8, k8, v8, S - Sq, 0, out, lse, q_descale=qs, k_descale=ks, v_descale=vs)
     fn()
     torch.cuda.synchronize()
-    ms, _ = time_launches(fn, args.steps, args.warmup)
+    ms, _ = time_launches(fn, args.steps, args.warmup, args.settle_seconds)
     tf = range_flops(1, H, Sq, S, S - Sq, d, d) / (ms * 1e-3) / 1e12
     return {"tflops": round(tf, 2), "ms": round(ms, 4), "pct_of_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
             "shape": f"{Sq} queries at positions {S - Sq}.. over {S} keys, nheads {H}/{Hk}, d {d}, bshd, LSE"}
@@ -483,7 +507,7 @@ def context_case(name, zy, args):
         fn = lambda: zy.zyfa_fwd(q8, k8, v8, out, q_descale=qs, k_descale=ks, v_descale=vs)
     fn()
     torch.cuda.synchronize()
-    ms, _ = time_launches(fn, args.steps, args.warmup)
+    ms, _ = time_launches(fn, args.steps, args.warmup, args.settle_seconds)
     tf = float(H) * S * S * (dqk + 128) / (ms * 1e-3) / 1e12
     return {"tflops": round(tf, 2), "ms": round(ms, 4), "pct_of_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
             "readme_mi355x_tflops": readme, "ratio_to_readme": round(tf / readme, 3),
@@ -545,13 +569,15 @@ def main():
         extra = name in RESIZED or name in PMODE or name in EXTRA
         if dtype == "fp8" and not extra:
             msq, _ = time_launches(lambda: [zy.zyfa_fp8_quantize(x, x8, xs) for x, x8, xs in
-                                            ((q, q8, qs), (k, k8, ks), (v, v8, vs))], args.steps, args.warmup)
+                                            ((q, q8, qs), (k, k8, ks), (v, v8, vs))], args.steps, args.warmup,
+                                   args.settle_seconds)
             res[name + "_quantize_qkv_ms"] = round(msq, 4)
             # q and k rotated before quantization (same signs), v plain: the
             # README's recipe for models; attention then runs unchanged
             signs = np.where(np.random.default_rng(0).random(w.d_qk) < 0.5, -1, 1).astype(np.int8)
             msr, _ = time_launches(lambda: [zy.zyfa_fp8_quantize_rotated(x, signs, x8, xs) for x, x8, xs in
-                                            ((q, q8, qs), (k, k8, ks))], args.steps, args.warmup)
+                                            ((q, q8, qs), (k, k8, ks))], args.steps, args.warmup,
+                                   args.settle_seconds)
             nb = (q.numel() + k.numel()) * 3      # read bf16 once, write e4m3 once
             res[name + "_rotate_quantize_qk"] = {"ms": round(msr, 4), "gbs": round(nb / (msr * 1e-3) / 1e9, 1),
                                                  "note": "algorithmic bytes (2 B read + 1 B written per element); "
@@ -559,7 +585,7 @@ def main():
             (q8, qs), (k8, ks) = (zy.zyfa_fp8_quantize(x) for x in (q, k))
         fn()
         torch.cuda.synchronize()
-        ms, _ = time_launches(fn, args.steps, args.warmup)
+        ms, _ = time_launches(fn, args.steps, args.warmup, args.settle_seconds)
         tf = w.flops() / (ms * 1e-3) / 1e12
         tr = stored_traffic(name, dtype)
         res[name] = {"tflops": round(tf, 2), "ms": round(ms, 4),
