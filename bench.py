@@ -573,8 +573,10 @@ def main():
                                    args.settle_seconds)
             res[name + "_quantize_qkv_ms"] = round(msq, 4)
             # q and k rotated before quantization (same signs), v plain: the
-            # README's recipe for models; attention then runs unchanged
+            # README's recipe for models (the 128-point Hadamard rotation);
+            # attention then runs unchanged
             signs = np.where(np.random.default_rng(0).random(w.d_qk) < 0.5, -1, 1).astype(np.int8)
+        if dtype == "fp8" and not extra and w.d_qk == 128:
             msr, _ = time_launches(lambda: [zy.zyfa_fp8_quantize_rotated(x, signs, x8, xs) for x, x8, xs in
                                             ((q, q8, qs), (k, k8, ks))], args.steps, args.warmup,
                                    args.settle_seconds)

@@ -184,7 +184,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   if (noalloc) {
     const int pairs = (plan->n_qtiles + 1) / 2;
     e = launch_build_jobs(const_cast<int2*>(plan->jobs), plan->jobs_per_wg, plan->num_wgs,
-                          (long long)batch * nheads * pairs, pairs, stream);
+                          (long long)batch * nheads * pairs, pairs, nheads / nheads_k, stream);
     if (e != hipSuccess) return ZYFA_ERR_HIP;
   }
   if (dtype == ZYFA_DTYPE_BF16)
@@ -210,7 +210,7 @@ int quantize_rotated_impl(const void* x, int x_dtype, long long rows, int d, con
                           void* stream_) {
   if (x_dtype != ZYFA_DTYPE_BF16 && x_dtype != ZYFA_DTYPE_FP32) return ZYFA_ERR_DTYPE;
   if (rows < 0) return ZYFA_ERR_SHAPE;
-  unsigned mask[6];
+  unsigned mask[4];
   const int rc = sign_mask(signs, d, mask);
   if (rc) return rc;
   if (!descale || (rows > 0 && (!x || !x8))) return ZYFA_ERR_NULL;

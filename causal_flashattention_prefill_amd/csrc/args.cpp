@@ -41,9 +41,9 @@ bool rows_in_31_bits(long long row_stride, int dim, int esz) {
   return (64 * row_stride + dim) * esz <= 0x7FFFFFFFll;
 }
 
-int sign_mask(const signed char* signs, int d, unsigned mask[6]) {
-  if (d != 128 && d != 192) return ZYFA_ERR_HEADDIM;
-  for (int i = 0; i < 6; ++i) mask[i] = 0;
+int sign_mask(const signed char* signs, int d, unsigned mask[4]) {
+  if (d != 128) return ZYFA_ERR_HEADDIM;
+  for (int i = 0; i < 4; ++i) mask[i] = 0;
   if (!signs) return ZYFA_OK;
   for (int i = 0; i < d; ++i) {
     if (signs[i] != 1 && signs[i] != -1) return ZYFA_ERR_SIGNS;

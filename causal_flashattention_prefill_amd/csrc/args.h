@@ -29,10 +29,11 @@ int clamp_delta(long long q_pos0, long long k_pos0, int seqlen_q, int seqlen_k);
 // wave's rows through a buffer resource with a 32-bit offset.
 bool rows_in_31_bits(long long row_stride, int dim, int esz);
 
-// Rotation signs (d values, each +1 or -1; NULL: all +1) as six words of
-// sign bits, bit i set when sign i is -1. ZYFA_ERR_SIGNS for another value,
-// ZYFA_ERR_HEADDIM for d other than 128 or 192.
-int sign_mask(const signed char* signs, int d, unsigned mask[6]);
+// Rotation signs (d = 128 values, each +1 or -1; NULL: all +1) as four
+// words of sign bits, bit i set when sign i is -1. ZYFA_ERR_SIGNS for
+// another value, ZYFA_ERR_HEADDIM for d other than 128 (the rotation is the
+// 128-point Hadamard transform).
+int sign_mask(const signed char* signs, int d, unsigned mask[4]);
 
 bool aligned(const void* p, unsigned bytes);
 

@@ -147,13 +147,10 @@ __global__ __launch_bounds__(kQThreads) void convert_kernel(const void* x, long 
 }
 
 // ---- Rotation before quantization ("ZYFA" README, "Using FP8 attention in
-// a model"): each row x of d channels becomes y = x R with R orthogonal,
-//   d = 128: R = diag(s) H_128 / sqrt(128)  (Sylvester Hadamard, signs s)
-//   d = 192: R = diag(s) (C_3^T kron H_64) / 8  (Hadamard within each
-//            64-channel block, orthonormal DCT-II across the three blocks)
+// a model"): each row x of d = 128 channels becomes y = x R with
+//   R = diag(s) H_128 / sqrt(128)  (Sylvester Hadamard, signs s)
 // and the rotated tensor is quantized as above. Half a wave (32 lanes)
-// holds one row: for d = 128 lane l holds channels 4 l .. 4 l + 3, for
-// d = 192 channels 64 a + 2 l + t (a < 3, t < 2). The fast Walsh-Hadamard
+// holds one row, lane l channels 4 l .. 4 l + 3. The fast Walsh-Hadamard
 // transform does the butterflies on channel bits held in a lane in
 // registers and those held across lanes with xor shuffles inside the half
 // wave; butterfly (u, w) -> (u + w, u - w) keeps natural order, so the
@@ -162,35 +159,23 @@ __global__ __launch_bounds__(kQThreads) void convert_kernel(const void* x, long 
 
 // bit i set when s_i = -1
 struct SignMask {
-  unsigned w[6];
+  unsigned w[4];
 };
 
 constexpr float kInvSqrt128 = 0.0883883476483184405f;
-// orthonormal DCT-II matrix, kC3[k][i] = a_k cos(pi (2 i + 1) k / 6)
-__device__ constexpr float kC3[3][3] = {{0.577350269189625765f, 0.577350269189625765f, 0.577350269189625765f},
-                                       {0.707106781186547524f, 0.0f, -0.707106781186547524f},
-                                       {0.408248290463863016f, -0.816496580927726033f, 0.408248290463863016f}};
 
 template <int D>
 struct Rot {
-  static constexpr int V = D == 128 ? 4 : 6;  // values per lane
+  static_assert(D == 128, "the rotation is the 128-point Hadamard transform");
+  static constexpr int V = 4;  // values per lane
 };
 
 // Sign bits of this lane's channels, as float sign-bit masks.
 template <int D>
 __device__ __forceinline__ void lane_signs(const SignMask& sm, int hl, unsigned (&sg)[Rot<D>::V]) {
-  if (D == 128) {
-    const unsigned w = hl < 8 ? sm.w[0] : hl < 16 ? sm.w[1] : hl < 24 ? sm.w[2] : sm.w[3];
+  const unsigned w = hl < 8 ? sm.w[0] : hl < 16 ? sm.w[1] : hl < 24 ? sm.w[2] : sm.w[3];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sg[t] = ((w >> ((4 * hl + t) & 31)) & 1u) << 31;
-  } else {
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      const unsigned w = hl < 16 ? sm.w[2 * a] : sm.w[2 * a + 1];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) sg[2 * a + t] = ((w >> ((2 * hl + t) & 31)) & 1u) << 31;
-    }
-  }
+  for (int t = 0; t < 4; ++t) sg[t] = ((w >> ((4 * hl + t) & 31)) & 1u) << 31;
 }
 
 // butterfly across lanes: the partner at lane ^ M (within the 32-lane half
@@ -206,31 +191,16 @@ __device__ __forceinline__ float bfly_x(float v, bool upper) {
 template <int D, int XDT>
 __device__ __forceinline__ void load_row(const void* x, long long row, bool live, int hl, float (&y)[Rot<D>::V]) {
   const char* base = reinterpret_cast<const char*>(x);
-  if (D == 128) {
-    if (XDT == 0) {
-      u32x2 w = {0u, 0u};
-      if (live) w = *reinterpret_cast<const u32x2*>(base + row * 256 + hl * 8);
-      const unsigned w0 = w[0], w1 = w[1];
-      y[0] = bf16_lo(w0); y[1] = bf16_hi(w0); y[2] = bf16_lo(w1); y[3] = bf16_hi(w1);
-    } else {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (live) w = *reinterpret_cast<const u32x4*>(base + row * 512 + hl * 16);
-      const unsigned w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-      y[0] = as_float(w0); y[1] = as_float(w1); y[2] = as_float(w2); y[3] = as_float(w3);
-    }
+  if (XDT == 0) {
+    u32x2 w = {0u, 0u};
+    if (live) w = *reinterpret_cast<const u32x2*>(base + row * 256 + hl * 8);
+    const unsigned w0 = w[0], w1 = w[1];
+    y[0] = bf16_lo(w0); y[1] = bf16_hi(w0); y[2] = bf16_lo(w1); y[3] = bf16_hi(w1);
   } else {
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      if (XDT == 0) {
-        const unsigned w = live ? *reinterpret_cast<const unsigned*>(base + row * 384 + (64 * a + 2 * hl) * 2) : 0u;
-        y[2 * a] = bf16_lo(w); y[2 * a + 1] = bf16_hi(w);
-      } else {
-        u32x2 w = {0u, 0u};
-        if (live) w = *reinterpret_cast<const u32x2*>(base + row * 768 + (64 * a + 2 * hl) * 4);
-        const unsigned w0 = w[0], w1 = w[1];
-        y[2 * a] = as_float(w0); y[2 * a + 1] = as_float(w1);
-      }
-    }
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (live) w = *reinterpret_cast<const u32x4*>(base + row * 512 + hl * 16);
+    const unsigned w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    y[0] = as_float(w0); y[1] = as_float(w1); y[2] = as_float(w2); y[3] = as_float(w3);
   }
 }
 
@@ -246,39 +216,17 @@ template <int D>
 __device__ __forceinline__ void transform(float (&y)[Rot<D>::V], int hl, const unsigned (&sg)[Rot<D>::V]) {
 #pragma unroll
   for (int t = 0; t < Rot<D>::V; ++t) y[t] = as_float(__builtin_bit_cast(unsigned, y[t]) ^ sg[t]);
-  if (D == 128) {
-    // channel bits 0, 1 in the lane
-    const float a0 = y[0] + y[1], a1 = y[0] - y[1], a2 = y[2] + y[3], a3 = y[2] - y[3];
-    y[0] = a0 + a2; y[2] = a0 - a2; y[1] = a1 + a3; y[3] = a1 - a3;
-  } else {
-    // channel bit 0 of each 64-channel block in the lane
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      const float u = y[2 * a], w = y[2 * a + 1];
-      y[2 * a] = u + w;
-      y[2 * a + 1] = u - w;
-    }
-  }
+  // channel bits 0, 1 in the lane
+  const float a0 = y[0] + y[1], a1 = y[0] - y[1], a2 = y[2] + y[3], a3 = y[2] - y[3];
+  y[0] = a0 + a2; y[2] = a0 - a2; y[1] = a1 + a3; y[3] = a1 - a3;
   // the remaining channel bits across the lanes (lane bits 0..4)
   bfly_stage<D, 1>(y, hl);
   bfly_stage<D, 2>(y, hl);
   bfly_stage<D, 4>(y, hl);
   bfly_stage<D, 8>(y, hl);
   bfly_stage<D, 16>(y, hl);
-  if (D == 128) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) y[t] *= kInvSqrt128;
-  } else {
-    // DCT across the blocks (and the 1/8 of the normalized Hadamard)
-    float z[6];
-#pragma unroll
-    for (int c = 0; c < 3; ++c)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        z[2 * c + t] = (kC3[c][0] * y[t] + kC3[c][1] * y[2 + t] + kC3[c][2] * y[4 + t]) * 0.125f;
-#pragma unroll
-    for (int t = 0; t < 6; ++t) y[t] = z[t];
-  }
+  for (int t = 0; t < 4; ++t) y[t] *= kInvSqrt128;
 }
 
 // Each half wave takes kRotRows rows per step: their loads go out together,
@@ -304,18 +252,9 @@ __device__ __forceinline__ unsigned shift_slot(unsigned r, const ShiftDesc& sd) 
 // this lane's channels of the row's shift vector
 template <int D>
 __device__ __forceinline__ void load_shift(const float* v, int hl, float (&sv)[Rot<D>::V]) {
-  if (D == 128) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(v + 4 * hl);
-    const unsigned w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-    sv[0] = as_float(w0); sv[1] = as_float(w1); sv[2] = as_float(w2); sv[3] = as_float(w3);
-  } else {
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(v + 64 * a + 2 * hl);
-      const unsigned w0 = w[0], w1 = w[1];
-      sv[2 * a] = as_float(w0); sv[2 * a + 1] = as_float(w1);
-    }
-  }
+  const u32x4 w = *reinterpret_cast<const u32x4*>(v + 4 * hl);
+  const unsigned w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+  sv[0] = as_float(w0); sv[1] = as_float(w1); sv[2] = as_float(w2); sv[3] = as_float(w3);
 }
 
 template <int D, bool SHIFT>
@@ -381,17 +320,9 @@ __global__ __launch_bounds__(kQThreads) void rot_convert_kernel(const void* x, l
       transform<D>(y[u], hl, sg);
       const long long r = r0 + u;
       if (r >= rows) continue;
-      if (D == 128) {
-        int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[u][0] * inv, y[u][1] * inv, 0, false);
-        p = __builtin_amdgcn_cvt_pk_fp8_f32(y[u][2] * inv, y[u][3] * inv, p, true);
-        *reinterpret_cast<unsigned*>(x8 + r * 128 + 4 * hl) = (unsigned)p;
-      } else {
-#pragma unroll
-        for (int c = 0; c < 3; ++c) {
-          const int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[u][2 * c] * inv, y[u][2 * c + 1] * inv, 0, false);
-          *reinterpret_cast<unsigned short*>(x8 + r * 192 + 64 * c + 2 * hl) = (unsigned short)(p & 0xFFFF);
-        }
-      }
+      int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[u][0] * inv, y[u][1] * inv, 0, false);
+      p = __builtin_amdgcn_cvt_pk_fp8_f32(y[u][2] * inv, y[u][3] * inv, p, true);
+      *reinterpret_cast<unsigned*>(x8 + r * 128 + 4 * hl) = (unsigned)p;
     }
   }
 }
@@ -495,14 +426,12 @@ __global__ __launch_bounds__(kMeanThreads) void key_mean_kernel(const void* x, i
 hipError_t launch_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d, const unsigned* sign_mask,
                                        const float* shift, int seqlen, int nheads, bool bshd, void* x8,
                                        float* descale, hipStream_t s) {
+  if (d != 128) return hipErrorInvalidValue;
   SignMask sm;
-  for (int i = 0; i < 6; ++i) sm.w[i] = sign_mask[i];
+  for (int i = 0; i < 4; ++i) sm.w[i] = sign_mask[i];
   const ShiftDesc sd{shift, (unsigned)seqlen, (unsigned)nheads, bshd};
-  if (d == 128)
-    return shift ? launch_rot_dt<128, true>(x, x_dtype, rows, sm, sd, x8, descale, s)
-                 : launch_rot_dt<128, false>(x, x_dtype, rows, sm, sd, x8, descale, s);
-  return shift ? launch_rot_dt<192, true>(x, x_dtype, rows, sm, sd, x8, descale, s)
-               : launch_rot_dt<192, false>(x, x_dtype, rows, sm, sd, x8, descale, s);
+  return shift ? launch_rot_dt<128, true>(x, x_dtype, rows, sm, sd, x8, descale, s)
+               : launch_rot_dt<128, false>(x, x_dtype, rows, sm, sd, x8, descale, s);
 }
 
 hipError_t launch_key_mean(const void* x, int x_dtype, int batch, int seqlen, int nheads, int d, bool bshd,

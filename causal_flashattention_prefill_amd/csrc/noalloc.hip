@@ -27,11 +27,11 @@ std::mutex g_scratch_mu;
 int2* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch` per device
 
 __global__ __launch_bounds__(256) void build_jobs_kernel(int2* table, int entries, int num_wgs, long long njobs,
-                                                         int pairs) {
+                                                         int pairs, int group) {
   const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
   if (i >= entries) return;
   const int r = i / num_wgs, w = i - r * num_wgs;
-  const JobEntry e = job_entry(r, w, njobs, num_wgs, pairs);
+  const JobEntry e = job_entry(r, w, njobs, num_wgs, pairs, group);
   table[i] = int2{e.bh, e.tile};
 }
 
@@ -54,11 +54,12 @@ hipError_t noalloc_scratch(int dev, int2** out) {
   return hipSuccess;
 }
 
-hipError_t launch_build_jobs(int2* table, int rows, int num_wgs, long long njobs, int pairs, hipStream_t s) {
+hipError_t launch_build_jobs(int2* table, int rows, int num_wgs, long long njobs, int pairs, int group,
+                             hipStream_t s) {
   const int entries = rows * num_wgs;
   if (entries <= 0 || entries > kScratchEntries) return hipErrorInvalidValue;
   hipLaunchKernelGGL(build_jobs_kernel, dim3((entries + 255) / 256), dim3(256), 0, s, table, entries, num_wgs, njobs,
-                     pairs);
+                     pairs, group);
   return hipGetLastError();
 }
 

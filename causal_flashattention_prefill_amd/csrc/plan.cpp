@@ -36,7 +36,6 @@ int tile_q_rows(int batch, int seqlen, int nheads, int d_qk, int dtype, int num_
 }
 
 JobTable build_job_table(int batch, int seqlen, int nheads, int nheads_k, int tile_q, int num_cus) {
-  (void)nheads_k;   // query heads of one KV head are consecutive in the job order (see job_entry)
   JobTable t;
   t.tile_q = tile_q;
   t.n_qtiles = (int)(((long long)seqlen + tile_q - 1) / tile_q);
@@ -47,7 +46,7 @@ JobTable build_job_table(int batch, int seqlen, int nheads, int nheads_k, int ti
   t.entries.assign(size_t(2) * t.num_wgs * t.jobs_per_wg, -1);
   for (int r = 0; r < t.jobs_per_wg; ++r)
     for (int w = 0; w < t.num_wgs; ++w) {
-      const JobEntry e = job_entry(r, w, njobs, t.num_wgs, pairs);
+      const JobEntry e = job_entry(r, w, njobs, t.num_wgs, pairs, nheads / nheads_k);
       const size_t i = 2 * (size_t(r) * t.num_wgs + w);
       t.entries[i] = e.bh;
       t.entries[i + 1] = e.tile;

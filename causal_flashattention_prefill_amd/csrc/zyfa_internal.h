@@ -41,7 +41,7 @@ hipError_t launch_attn_fp8(const AttnArgs& a, int d_qk, bool with_lse, FP8Mode m
 // x8 doubles as the scratch of the amax partials (overwritten by the codes)
 hipError_t launch_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, float* descale,
                                hipStream_t s);
-// sign_mask: six words, bit i set when channel i's sign is -1
+// d: 128; sign_mask: four words, bit i set when channel i's sign is -1
 // shift: null, or a device vector per (batch, head) slot subtracted from
 // each row before the rotation (rows in the tensor's memory order, seqlen
 // positions and nheads heads per batch, bshd or bhsd)
@@ -55,7 +55,8 @@ hipError_t launch_key_mean(const void* x, int x_dtype, int batch, int seqlen, in
 // that writes a job table into it.
 int noalloc_scratch_entries();
 hipError_t noalloc_scratch(int dev, int2** out);
-hipError_t launch_build_jobs(int2* table, int rows, int num_wgs, long long njobs, int pairs, hipStream_t s);
+hipError_t launch_build_jobs(int2* table, int rows, int num_wgs, long long njobs, int pairs, int group,
+                             hipStream_t s);
 hipError_t launch_lse_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,
                             float* lse, int batch, int seqlen, int nheads, int d_v, bool bshd, hipStream_t s);
 

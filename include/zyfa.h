@@ -254,24 +254,21 @@ int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, flo
                       void* stream);
 
 /*
- * zyfa_fp8_quantize_rotated - rotate each row of d channels by an orthogonal
- * matrix R, then quantize the rotated tensor as zyfa_fp8_quantize does
+ * zyfa_fp8_quantize_rotated - rotate each row of d = 128 channels by an
+ * orthogonal matrix R, then quantize the rotated tensor as zyfa_fp8_quantize does
  * ("ZYFA" README, "Using FP8 attention in a model": a Hadamard rotation of
  * q and k before quantization; (q R)(k R)^T = q k^T, so attention on the
  * rotated q and k equals attention on the originals up to rounding, and the
  * rotation spreads channels with large values over all channels, which
  * lowers the quantization error). Rotate q and k with the same signs;
  * leave v unrotated.
- *   d = 128: R = diag(s) H_128 / sqrt(128), H Sylvester's Hadamard matrix
- *   d = 192: R = diag(s) (C_3^T kron H_64) / 8, C_3 the orthonormal 3-point
- *            DCT-II matrix: the Hadamard matrix within each 64-channel
- *            block and the DCT across the three blocks
+ *   R = diag(s) H_128 / sqrt(128), H Sylvester's Hadamard matrix
  *   y = x R (computed in fp32 with a fast Walsh-Hadamard transform), then
  *   descale = 2^ceil(log2(max|y| / 448)) (1 when y == 0, >= 2^-126) and
  *   x8 = e4m3fn RNE of y / descale.
  *  x       device pointer, rows * d values of x_dtype (ZYFA_DTYPE_BF16 or
  *          ZYFA_DTYPE_FP32), rows contiguous; 16-byte aligned.
- *  d       128 or 192 (ZYFA_ERR_HEADDIM otherwise).
+ *  d       128 (ZYFA_ERR_HEADDIM otherwise).
  *  signs   host pointer to d values, each +1 or -1 (ZYFA_ERR_SIGNS
  *          otherwise), or NULL for all +1. Read during the call only.
  *  x8      device pointer, rows * d bytes; descale: device pointer to one

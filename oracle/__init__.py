@@ -27,13 +27,13 @@ from .codecs import (bf16_round, bf16_decode, bf16_encode_bits, e4m3fn_decode,
 from .quantize import fp8_quantize_ref
 from .attention import causal_attention_ref, causal_probs_ref, causal_attention_rows_ref
 from .partial import range_attention_ref, range_attention_rows_ref, lse_merge_ref, lse_merge_layout_ref
-from .rotation import (hadamard, dct2_ortho, rotation_matrix, rotate_ref, quantize_rotated_ref, key_mean_ref,
+from .rotation import (hadamard, rotation_matrix, rotate_ref, quantize_rotated_ref, key_mean_ref,
                        quantize_shifted_rotated_ref)
 
 __all__ = [
     "bf16_round", "bf16_decode", "bf16_encode_bits", "e4m3fn_decode", "e4m3fn_encode",
     "E4M3FN_MAX", "fp8_quantize_ref", "causal_attention_ref", "causal_probs_ref",
     "causal_attention_rows_ref", "range_attention_ref",
-    "range_attention_rows_ref", "lse_merge_ref", "lse_merge_layout_ref", "hadamard", "dct2_ortho",
+    "range_attention_rows_ref", "lse_merge_ref", "lse_merge_layout_ref", "hadamard",
     "rotation_matrix", "rotate_ref", "quantize_rotated_ref", "key_mean_ref", "quantize_shifted_rotated_ref",
 ]

@@ -5,16 +5,10 @@
 an orthogonal matrix R before quantization, so (q R)(k R)^T = q k^T and only
 the rounding error changes; R = diag(s) H / sqrt(d) with H the Hadamard
 matrix of Sylvester's construction (H_1 = [1], H_2n = [[H_n, H_n], [H_n,
--H_n]]) and s a vector of random signs, for d a power of two. For d = 192,
-which is not one, the README combines a 3-point discrete cosine transform
-with a 64-point Hadamard matrix.
+-H_n]]) and s a vector of random signs, for d a power of two (the library
+rotates d = 128).
 
 Readings:
-- d = 192: R = diag(s) (C_3^T kron H_64) / 8, with C_3 the orthonormal
-  DCT-II matrix (row k = frequency k). As a transform of a row vector,
-  y = x R applies the Hadamard matrix within each 64-channel block and the
-  forward DCT across the three blocks: y[64 c + e] = sum_{a, b} s[64 a + b]
-  x[64 a + b] C_3[c, a] H_64[b, e] / 8.
 - The signs are an input (one +1 / -1 per channel).
 - Quantization of the rotated tensor follows quantize.fp8_quantize_ref: one
   power-of-two scale per tensor, round to nearest even.
@@ -36,28 +30,14 @@ def hadamard(n: int) -> np.ndarray:
     return h
 
 
-def dct2_ortho(n: int) -> np.ndarray:
-    """Orthonormal DCT-II matrix: C[k, i] = a_k cos(pi (2 i + 1) k / (2 n)),
-    a_0 = sqrt(1/n), a_k = sqrt(2/n)."""
-    k = np.arange(n)[:, None]
-    i = np.arange(n)[None, :]
-    c = np.cos(np.pi * (2 * i + 1) * k / (2 * n))
-    a = np.where(k == 0, np.sqrt(1.0 / n), np.sqrt(2.0 / n))
-    return a * c
-
-
 def rotation_matrix(d: int, signs) -> np.ndarray:
-    """R (d x d) for d = 128 (or any power of two) and d = 192."""
+    """R (d x d) for d a power of two (128 in the library)."""
     s = np.asarray(signs, dtype=np.float64)
     if s.shape != (d,) or not np.all(np.abs(s) == 1.0):
         raise ValueError("signs must be d values of +1 or -1")
-    if d & (d - 1) == 0:
-        core = hadamard(d) / np.sqrt(d)
-    elif d == 192:
-        core = np.kron(dct2_ortho(3).T, hadamard(64) / 8.0)
-    else:
-        raise ValueError("d must be a power of two or 192")
-    return s[:, None] * core
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    return s[:, None] * (hadamard(d) / np.sqrt(d))
 
 
 def rotate_ref(x, signs) -> np.ndarray:

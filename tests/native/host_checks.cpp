@@ -70,18 +70,18 @@ static void strides_and_ranges() {
 }
 
 static void signs() {
-  unsigned m[6];
-  std::vector<signed char> s(192, 1);
-  CHECK(sign_mask(nullptr, 128, m) == ZYFA_OK && m[0] == 0 && m[5] == 0);
+  unsigned m[4];
+  std::vector<signed char> s(128, 1);
+  CHECK(sign_mask(nullptr, 128, m) == ZYFA_OK && m[0] == 0 && m[3] == 0);
   s[0] = -1;
   s[37] = -1;
-  s[191] = -1;
-  CHECK(sign_mask(s.data(), 192, m) == ZYFA_OK);
-  CHECK(m[0] == 1u && m[1] == (1u << 5) && m[5] == (1u << 31));
-  CHECK(sign_mask(s.data(), 128, m) == ZYFA_OK && m[5] == 0);
+  s[127] = -1;
+  CHECK(sign_mask(s.data(), 128, m) == ZYFA_OK);
+  CHECK(m[0] == 1u && m[1] == (1u << 5) && m[2] == 0 && m[3] == (1u << 31));
   s[100] = 0;
   CHECK(sign_mask(s.data(), 128, m) == ZYFA_ERR_SIGNS);
   CHECK(sign_mask(s.data(), 64, m) == ZYFA_ERR_HEADDIM);
+  CHECK(sign_mask(s.data(), 192, m) == ZYFA_ERR_HEADDIM);
   int x = 0;
   CHECK(aligned(&x, 4) && aligned(reinterpret_cast<char*>(256), 16) && !aligned(reinterpret_cast<char*>(24), 16));
 }

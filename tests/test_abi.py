@@ -141,13 +141,16 @@ def test_job_pairs_have_equal_work():
 
 def test_job_table_xcd_locality():
     # in each table row, the workgroups of one XCD (blockIdx % 8) hold
-    # consecutive jobs, so at most two heads per XCD per row
+    # consecutive jobs: one KV head, and every query head of its group at
+    # each pair index they hold (they read the same K and V tiles)
     tq, nw, jp, table = zy.zyfa_plan_jobs(1, 16384, 32, 8, dtype=zy.DTYPE_FP8)
     assert tq == 256 and nw == 256 and jp == 4
     for r in range(jp):
         for x in range(8):
-            heads = {int(table[r, w, 0]) for w in range(x, nw, 8)}
-            assert len(heads) <= 2
+            jobs = [tuple(int(v) for v in table[r, w]) for w in range(x, nw, 8)]
+            assert len({h // 4 for h, _ in jobs}) == 1
+            for i in {i for _, i in jobs}:
+                assert sorted(h % 4 for h, t in jobs if t == i) == [0, 1, 2, 3]
 
 
 def _range(**kw):
@@ -199,6 +202,7 @@ def test_quantize_rotated_argument_errors():
     assert _rot(xd=1) == S["ZYFA_ERR_DTYPE"]
     assert _rot(rows=-1) == S["ZYFA_ERR_SHAPE"]
     assert _rot(d=64) == S["ZYFA_ERR_HEADDIM"]
+    assert _rot(d=192) == S["ZYFA_ERR_HEADDIM"]     # the Hadamard rotation is for d = 128
     bad = np.ones(128, dtype=np.int8)
     bad[7] = 0
     assert _rot(signs=bad) == S["ZYFA_ERR_SIGNS"]
@@ -228,3 +232,4 @@ def test_key_mean_and_shifted_argument_errors():
     assert f(16, 0, 1 << 20, 1 << 12, 1, 128, 0, None, 16, 16, 16, None) == S["ZYFA_ERR_RANGE"]
     assert f(16, 0, 1, 10, 2, 128, 0, None, 24, 16, 16, None) == S["ZYFA_ERR_ALIGN"]
     assert f(16, 0, 1, 10, 2, 96, 0, None, 16, 16, 16, None) == S["ZYFA_ERR_HEADDIM"]
+    assert f(16, 0, 1, 10, 2, 192, 0, None, 16, 16, 16, None) == S["ZYFA_ERR_HEADDIM"]

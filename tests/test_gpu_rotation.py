@@ -21,9 +21,8 @@ def _check_codes(got, codes, y, descale, x_abs_rowsum, d):
     """Codes equal the oracle's except where the float64 rotated value lies
     within the fp32 error of the kernel's transform of a rounding boundary:
     there the neighbouring code is also a correct rounding of the kernel's
-    fp32 value. The fp32 transform (log2 d butterfly levels, a scale and,
-    for d = 192, a three-term DCT) errs by at most 12 * 2^-24 * sum|x| /
-    sqrt(d) per output."""
+    fp32 value. The fp32 transform (log2 d butterfly levels and a scale)
+    errs by at most 12 * 2^-24 * sum|x| / sqrt(d) per output."""
     diff = got != codes
     n = int(diff.sum())
     if n == 0:
@@ -39,7 +38,7 @@ def _check_codes(got, codes, y, descale, x_abs_rowsum, d):
 
 
 @pytest.mark.parametrize("xdt", ["bf16", "fp32"])
-@pytest.mark.parametrize("d", [128, 192])
+@pytest.mark.parametrize("d", [128])
 @pytest.mark.parametrize("rows", [1, 7, 1000, 40000])
 def test_rotated_codes_match_oracle(d, xdt, rows):
     rng = np.random.Generator(np.random.PCG64(rows * 7 + d))
@@ -65,10 +64,19 @@ def test_rotated_zero_rows_and_zero_tensor():
     _, ds = zy.zyfa_fp8_quantize_rotated(x)
     torch.cuda.synchronize()
     assert float(ds.item()) == 1.0
-    z = torch.zeros((5, 192), dtype=torch.bfloat16, device="cuda")
-    x8, ds = zy.zyfa_fp8_quantize_rotated(z, _signs(192, 1))
+    z = torch.zeros((5, 128), dtype=torch.bfloat16, device="cuda")
+    x8, ds = zy.zyfa_fp8_quantize_rotated(z, _signs(128, 1))
     torch.cuda.synchronize()
     assert float(ds.item()) == 1.0 and int(x8.view(torch.uint8).sum().item()) == 0
+
+
+def test_rotation_is_for_d128_only():
+    # the README's rotation is the Hadamard transform of a power-of-two head
+    # dim; d_qk = 192 is refused
+    x = torch.zeros((5, 192), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(zy.ZyfaError) as e:
+        zy.zyfa_fp8_quantize_rotated(x)
+    assert e.value.status == zy.STATUS["ZYFA_ERR_HEADDIM"]
 
 
 def test_workload3_q_full_size():
@@ -107,7 +115,7 @@ def _attention_case(w: Workload, rotate: bool, seed_signs: int):
     return out_to_f64(out), deq, (rq, rk, rv)
 
 
-@pytest.mark.parametrize("dqk,layout", [(128, "bshd"), (192, "bhsd")])
+@pytest.mark.parametrize("dqk,layout", [(128, "bshd"), (128, "bhsd")])
 def test_attention_on_rotated_inputs(dqk, layout):
     w = Workload("rot", 1, 700, 4, 2 if dqk == 128 else 4, dqk, 128, layout, ("fp8",), False, False, 700 + dqk)
     print(f"case attention on rotated fp8 d{dqk} {layout}", flush=True)
@@ -155,7 +163,7 @@ def test_key_mean_matches_oracle(d, layout, S, xdt):
     assert torch.equal(mean, again)
 
 
-@pytest.mark.parametrize("d,layout", [(128, "bshd"), (192, "bhsd")])
+@pytest.mark.parametrize("d,layout", [(128, "bshd"), (128, "bhsd")])
 def test_shifted_rotated_codes_match_oracle(d, layout):
     B, S, H = 2, 300, 3
     rng = np.random.Generator(np.random.PCG64(5 * d))

@@ -1,8 +1,7 @@
-"""Pins of the rotation oracle (oracle/rotation.py): closed forms, a library
-DCT, orthogonality and the invariance the README states."""
+"""Pins of the rotation oracle (oracle/rotation.py): closed forms,
+orthogonality and the invariance the README states."""
 import numpy as np
 import pytest
-from scipy.fft import dct
 
 import oracle
 
@@ -16,16 +15,7 @@ def test_hadamard_closed_form(n):
     assert np.array_equal(oracle.hadamard(n), (-1.0) ** pc)
 
 
-def test_dct_matches_scipy():
-    # scipy's orthonormal DCT-II of the unit vectors gives the matrix column by column
-    np.testing.assert_allclose(oracle.dct2_ortho(3), dct(np.eye(3), type=2, norm="ortho", axis=0), atol=1e-15)
-    c = oracle.dct2_ortho(3)
-    np.testing.assert_allclose(c[0], [3 ** -0.5] * 3, atol=1e-15)
-    np.testing.assert_allclose(c[1], [2 ** -0.5, 0.0, -(2 ** -0.5)], atol=1e-15)
-    np.testing.assert_allclose(c[2], [6 ** -0.5, -2 * 6 ** -0.5, 6 ** -0.5], atol=1e-15)
-
-
-@pytest.mark.parametrize("d", [128, 192])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_rotation_is_orthogonal_and_keeps_scores(d):
     rng = np.random.default_rng(d)
     s = rng.choice([-1.0, 1.0], d)
@@ -44,25 +34,16 @@ def test_d128_spreads_a_channel_evenly():
         np.testing.assert_allclose(y, s[i] * (-1.0) ** pc / np.sqrt(128), atol=1e-15)
 
 
-def test_d192_block_structure():
-    rng = np.random.default_rng(2)
-    s = rng.choice([-1.0, 1.0], 192)
-    c = oracle.dct2_ortho(3)
-    h = oracle.hadamard(64)
-    for a, b in ((0, 0), (1, 17), (2, 63)):
-        y = oracle.rotate_ref(np.eye(192)[64 * a + b], s).reshape(3, 64)
-        want = s[64 * a + b] * c[:, a][:, None] * h[b][None, :] / 8.0
-        np.testing.assert_allclose(y, want, atol=1e-15)
-
-
 def test_signs_must_be_plus_minus_one():
     with pytest.raises(ValueError):
         oracle.rotation_matrix(128, np.zeros(128))
     with pytest.raises(ValueError):
         oracle.rotation_matrix(96, np.ones(96))
+    with pytest.raises(ValueError):
+        oracle.rotation_matrix(192, np.ones(192))
 
 
-@pytest.mark.parametrize("d", [128, 192])
+@pytest.mark.parametrize("d", [128])
 def test_rotated_quantize_round_trip(d):
     rng = np.random.default_rng(3 + d)
     s = rng.choice([-1.0, 1.0], d)
