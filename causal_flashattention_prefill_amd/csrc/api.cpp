@@ -39,18 +39,21 @@ struct Plan {
 std::mutex g_mu;
 std::map<PlanKey, Plan> g_plans;
 std::map<PlanKey, int> g_tile_choice;   // query-tile heights set by zyfa_set_tile_q
-std::map<int, int> g_num_cus;
+// compute units per device, looked up once (a fixed array: zyfa_fwd_noalloc
+// allocates nothing, host memory included)
+constexpr int kMaxDevices = 64;
+int g_num_cus[kMaxDevices] = {};
 
 int current_device(int* dev) {
   return hipGetDevice(dev) == hipSuccess ? ZYFA_OK : ZYFA_ERR_HIP;
 }
 
 int num_cus(int dev) {
-  auto it = g_num_cus.find(dev);
-  if (it != g_num_cus.end()) return it->second;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && g_num_cus[dev] > 0) return g_num_cus[dev];
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  g_num_cus[dev] = n;
+  if (cached) g_num_cus[dev] = n;
   return n;
 }
 
