@@ -1,7 +1,10 @@
 """Equal-FLOP matrix-instruction streams of two tile shapes on one MI355X, at
 the board's power cap: the measurement behind the attention kernels' MFMA
 shape ("Attention at the Power Cap", sections 2 and 3.2, compares
-16x16x32 and 32x32x16 bf16 streams by TF/s, clock and power at the cap).
+16x16x32 and 32x32x16 bf16 streams by TF/s, clock and power at the cap),
+and the rate of the older v_mfma_f32_16x16x32_fp8_fp8, which the FP8 kernel
+uses for the channels past 128 of d_qk = 192 (cycles per instruction =
+FLOP per instruction x 1024 SIMDs x clock / FLOP/s).
 
 Each case runs the microbenchmark kernels of csrc/mfma_shapes.hip (one
 512-thread workgroup per CU, 8 waves, independent instructions on random
@@ -24,8 +27,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 KINDS = {0: ("bf16", "v_mfma_f32_16x16x32_bf16"), 1: ("bf16", "v_mfma_f32_32x32x16_bf16"),
-         2: ("fp8", "v_mfma_scale_f32_16x16x128_f8f6f4"), 3: ("fp8", "v_mfma_scale_f32_32x32x64_f8f6f4")}
-ITERS = {0: 2000, 1: 2000, 2: 1000, 3: 1000}
+         2: ("fp8", "v_mfma_scale_f32_16x16x128_f8f6f4"), 3: ("fp8", "v_mfma_scale_f32_32x32x64_f8f6f4"),
+         4: ("fp8", "v_mfma_f32_16x16x32_fp8_fp8")}
+ITERS = {0: 2000, 1: 2000, 2: 1000, 3: 1000, 4: 1000}
 
 
 def main():

@@ -56,8 +56,14 @@
 //    score layout of the MFMA puts key 16g + 4c + i (and 64 + ...) in lane
 //    group g: the MFMA k index of P equals the key's offset in the tile and
 //    each E8M0 scale block is 32 consecutive keys.
-//  - d_qk = 192 adds d 128..191 to every score block through two
-//    v_mfma_f32_16x16x32_fp8_fp8 (8-byte operands, no zero padding).
+//  - d_qk = 192: with two query groups per wave, d 128..191 of all 32
+//    query columns and 128 keys take four v_mfma_scale_f32_32x32x64_f8f6f4,
+//    the FP8 rate of the 16x16x128 instruction; their results reach the
+//    16x16 score layout through v_permlane16_swap (one per pair of values)
+//    and start the accumulators of the 16x16x128 products over d 0..127.
+//    With one query group (16 columns, too few for the 32-column product)
+//    each score block adds two v_mfma_f32_16x16x32_fp8_fp8, which run at
+//    half that rate.
 //  - Precise mode (for inputs whose channels differ widely in magnitude,
 //    such as activations with outlier channels): gfx950's FP8 matrix
 //    instructions sum their products with an error of up to 2^-11.5 of
@@ -157,6 +163,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   constexpr int RW = 16 * QG;                       // query rows per wave (QG 16-row groups)
   constexpr int kTileQ = 8 * RW;                    // query rows per tile
   constexpr bool D192 = DQK == 192;
+  // d_qk = 192 with two query groups: the scores over d 128..191 come from
+  // the 32x32x64 scaled instruction at the full FP8 rate and are brought
+  // into the 16x16 layout by lane swaps; with one group (16 query columns
+  // per wave, too few for a 32-column product) they come from two 16x16x32
+  // FP8 instructions per block, which run at half the rate
+  constexpr bool kWide = D192 && QG == 2 && !PRECISE;
   constexpr int KA_BYTES = kTileK * 128;            // K region for d 0..127
   constexpr int KB_BYTES = D192 ? kTileK * 64 : 0;  // K region for d 128..191
   constexpr int K_SLOT = KA_BYTES + KB_BYTES;
@@ -197,6 +209,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   const float c8s = 8.0f * sl2 * kInv65535;
   // ds_bpermute source of the lane's E8M0 scale: lane groups 1 and 2 swap
   const int psc_addr = 4 * (((g == 1) || (g == 2)) ? (lane ^ 48) : lane);
+  // LDS base of this lane's d 128..191 K reads on the 32x32x64 instruction
+  // (instruction row x = lane % 32 = 8 j + 4 h + i on LDS row 16 j + 8 h + i,
+  // chunks 2 (lane / 32) and 2 (lane / 32) + 1 swizzled by 2 h)
+  const int khb = [&] {
+    const int x = lane & 31;
+    const int row0 = 16 * (x >> 3) + 8 * ((x >> 2) & 1) + (x & 3);
+    return kTileK * 128 + row0 * 64 + (((2 * (lane >> 5)) ^ (2 * ((x >> 2) & 1))) << 4);
+  }();
   const float dvs = a.v_descale[0];
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3fn 1.0
@@ -245,25 +265,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       const int K0 = min(qb + dl + 1, Sk) >= 256 ? (qb + dl + 1) / kTileK : 0;
 
       // Q fragments (B operand): lane (g, n) holds q[row n][16g..16g+15] and
-      // q[row n][64+16g..]; for d 192 also q[row n][128+8g..+7] and
-      // q[row n][160+8g..+7], the B operands of two 16x16x32 FP8 MFMAs over
-      // d 128..191. They are read through a resource based at the wave's
-      // first row.
+      // q[row n][64+16g..]; for d 192 with one query group also
+      // q[row n][128+8g..+7] and q[row n][160+8g..+7], the B operands of two
+      // 16x16x32 FP8 MFMAs over d 128..191. They are read through a resource
+      // based at the wave's first row.
       const int qr0 = q0 + RW * ws;
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (unsigned long long)qr0 * (unsigned)qrs,
                                                   rows_extent(min(Sq - qr0, RW), qrs, DQK));
       i32x8 qf[QG];
       long qx[QG][2];
+      // kWide: the B operand of the 32x32x64 instruction over d 128..191,
+      // lane l holding q[row l % 32][128 + 32 (l / 32) .. +31]
+      i32x8 qh = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int qg = 0; qg < QG; ++qg) {
         const int off = (16 * qg + n) * qrs;
         const u32x4 lo = buf_load16(rq, off + 16 * g);
         const u32x4 hi = buf_load16(rq, off + 64 + 16 * g);
         qf[qg] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        if (D192) {
+        if (D192 && !kWide) {
           qx[qg][0] = __builtin_bit_cast(long, buf_load8(rq, off + 128 + 8 * g));
           qx[qg][1] = __builtin_bit_cast(long, buf_load8(rq, off + 160 + 8 * g));
         }
+      }
+      if (kWide) {
+        const int off = (lane & 31) * qrs + 128 + 32 * (lane >> 5);
+        const u32x4 lo = buf_load16(rq, off), hi = buf_load16(rq, off + 16);
+        qh = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
       // Precise mode: the B operands of the bf16 score MFMAs, k-step c of
       // lane group g holding the same d values as the K operand: c = 0..3
@@ -401,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         const u32x4 lo = lds_load<u32x4>(ka + row * 128 + ((g ^ sw) << 4));
         const u32x4 hi = lds_load<u32x4>(ka + row * 128 + (((4 + g) ^ sw) << 4));
         f.a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        if (D192) {
+        if (D192 && !kWide) {
           // 64-byte rows, 16-byte chunks swizzled by (row >> 2) & 3: d
           // 128+8g.. is half g & 1 of chunk g >> 1, d 160+8g.. of chunk
           // 2 + (g >> 1)
@@ -411,6 +439,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
           f.b1 = __builtin_bit_cast(long, lds_load<u32x2>(kr + (((2 + (g >> 1)) ^ sw2) << 4)));
         }
         return f;
+      };
+
+      // kWide: K operand of 32x32x64 instruction w = 2 p + o over d
+      // 128..191. Lane l supplies row x = l % 32 = 8 j + 4 h + i of the
+      // instruction, bytes 32 (l / 32) .. +31 of the key's d 128..191. Row x
+      // of instruction w is key 64 p + 16 (2 h + o) + 4 j + i, so that after
+      // the lane swaps lane group g holds the keys of the 16x16 layout
+      // (16 g .., 64 + 16 g ..). kswap puts that key on LDS row 64 p + 16 j +
+      // 8 h + 4 o + i, whose chunk swizzle is 2 h + o: every read is the
+      // lane's base address khb plus a constant (4096 p + 256 o; for o = 1
+      // the two chunks trade places).
+      auto khi_frag = [&](const char* ka, int w) {
+        const char* kr = ka + khb + 4096 * (w >> 1) + 256 * (w & 1);
+        const u32x4 lo = lds_load<u32x4>(kr + ((w & 1) ? 16 : 0));
+        const u32x4 hi = lds_load<u32x4>(kr + ((w & 1) ? 0 : 16));
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       };
 
       // Matrix cluster of tile t: O^T += V^T P^T and the row sum for tile
@@ -515,11 +559,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
         }
         if (t <= kt_w && !PRECISE) {
           const char* ka = kring + (t % kSlots) * K_SLOT;
+          // kWide: the d 128..191 scores first, four 32x32x64 instructions
+          // (keys 0..63, then 64..127; in each half the keys of lane groups
+          // 0, 2, then of lane groups 1, 3); they start where the PV
+          // instructions end, so the matrix pipe stays busy
+          f32x16 hw[kWide ? 4 : 1];
+          if (kWide) {
+            i32x8 kh = khi_frag(ka, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const i32x8 cur = kh;
+              if (w < 3) kh = khi_frag(ka, w + 1);
+              hw[w] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur, qh, f32x16{}, 0, 0, 0, kE8M0One, 0, kE8M0One);
+              if (w < 3) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            }
+            // all four issued before the first swap, which then finds the
+            // results of instructions 0 and 1 ready while 3 still runs
+            __builtin_amdgcn_sched_barrier(0);
+          }
           // K fragments are read kPfK 16-key blocks ahead of their MFMAs
           KFrag kfb[kPfK];
 #pragma unroll
           for (int u = 0; u < kPfK; ++u) kfb[u] = k_frag(ka, u);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (D192 ? 4 : 2) * kPfK, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (D192 && !kWide ? 4 : 2) * kPfK, 0);
           // d 128..191 (d_qk = 192) accumulate onto the result of the scaled
           // instruction. Issued straight after that result, such a pair was
           // given no wait states and read a stale accumulator on the GPU, so
@@ -534,9 +598,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
           for (int kb = 0; kb < 8; ++kb) {
             const KFrag cur = kfb[kb % kPfK];
             if (kb + kPfK < 8) kfb[kb % kPfK] = k_frag(ka, kb + kPfK);
+            if (kWide) {
+              // Lane swaps. Value 4 j + i of instruction w = 2 p + o holds, in
+              // lane group g, the score of query column 16 (g % 2) + n and
+              // key 64 p + 16 (2 (g / 2) + o) + 4 j + i: lane groups 0, 2 of
+              // w = 2 p and 1, 3 of w = 2 p + 1 already hold their own keys;
+              // v_permlane16_swap trades the odd lane groups of its first
+              // operand for the even lane groups of its second, after which
+              // the first holds query group 0 and the second query group 1,
+              // in the 16x16 layout of key block 4 p + j.
+              const int pw = 2 * (kb >> 2), j = kb & 3;
+              // (elements are copied to scalars before the bit casts: a bit
+              // cast of a vector element in place has been compiled as a
+              // cast of element 0)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float e0 = hw[pw][4 * j + i], e1 = hw[pw + 1][4 * j + i];
+                const auto pr = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, e0),
+                                                                 __builtin_bit_cast(unsigned, e1), false, false);
+                const unsigned r0 = pr[0], r1 = pr[1];
+                s[0][kb][i] = __builtin_bit_cast(float, r0);
+                s[1][kb][i] = __builtin_bit_cast(float, r1);
+              }
+              __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+            }
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg)
-              s[qg][kb] = mfma_fp8(cur.a, qf[qg], f32x4{0.f, 0.f, 0.f, 0.f}, kE8M0One, kE8M0One);
+              s[qg][kb] = mfma_fp8(cur.a, qf[qg], kWide ? s[qg][kb] : f32x4{0.f, 0.f, 0.f, 0.f}, kE8M0One, kE8M0One);
             if (kDefer) {
               if (kb >= 1) {
                 // keeps the pair after this block's scaled instruction
@@ -546,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
               }
               pb0 = cur.b0;
               pb1 = cur.b1;
-            } else if (D192) {
+            } else if (D192 && !kWide) {
               // both groups' scaled instructions first, held there by a
               // scheduling barrier: the other group's scaled instruction then
               // separates each pair from the result it accumulates onto
@@ -557,9 +645,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
                 s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur.b1, qx[qg][1], s[qg][kb], 0, 0, 0);
               }
             }
-            if (kb + kPfK < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 ? 4 : 2, 0);
+            if (kb + kPfK < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 && !kWide ? 4 : 2, 0);
             if (kDefer && kb == 0) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            else __builtin_amdgcn_sched_group_barrier(kSchedMfma, (D192 ? 3 : 1) * QG, 0);
+            else __builtin_amdgcn_sched_group_barrier(kSchedMfma, (D192 && !kWide ? 3 : 1) * QG, 0);
           }
           if (kDefer) {
             // the pair of the last block follows the pair of block 6

@@ -10,6 +10,7 @@ namespace zyfa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -160,5 +161,6 @@ __device__ __forceinline__ float mask_above(float x, int ko, int q, float ninf) 
 // sched_group_barrier instruction classes.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedValu = 0x002;
 
 }  // namespace zyfa

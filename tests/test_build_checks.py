@@ -101,7 +101,53 @@ def test_scaled_result_is_not_read_by_the_next_matrix_instruction(fp8_asm):
 
 
 def test_d192_kernels_mix_the_two_kinds(fp8_asm):
-    # the check above only means something where the two kinds meet
+    # the check above only means something where the two kinds meet: the
+    # d_qk = 192 kernels with one query group per wave (exact and lean P,
+    # with and without LSE) use the 16x16x32 FP8 instruction over d 128..191
     ks = kernels(fp8_asm)
     mixed = [n for n, ins in ks.items() if "Li192E" in n and any("fp8_fp8" in x[0] for x in ins)]
-    assert len(mixed) >= 8, mixed
+    assert len(mixed) == 4 and all("Li1EEEv" in n for n in mixed), mixed
+
+
+def test_d192_two_group_kernels_use_the_32x32x64_instruction(fp8_asm):
+    # with two query groups per wave, d 128..191 go to the 32x32x64 scaled
+    # instruction (full FP8 rate) and no 16x16x32 FP8 instruction is left
+    ks = kernels(fp8_asm)
+    wide = [n for n in ks if "Li192E" in n and n.endswith("Li2EEEvNS_8AttnArgsE")]
+    assert len(wide) == 4, wide
+    for n in wide:
+        ops = [x[0] for x in ks[n]]
+        assert "v_mfma_scale_f32_32x32x64_f8f6f4" in ops and not any("fp8_fp8" in o for o in ops), n
+
+
+def _wait_states(line):
+    """Wait states an instruction line provides (s_nop N gives N + 1)."""
+    m = re.match(r"^\s*s_nop\s+(\d+)", line)
+    return int(m.group(1)) + 1 if m else 1
+
+
+def test_lane_swaps_wait_for_the_32x32x64_results(fp8_asm):
+    # a vector instruction that reads the result of a 16-pass matrix
+    # instruction needs 18 wait states after it; the compiler inserts them,
+    # and this holds it to that in the built code of the d 192 kernels
+    bad, seen = [], 0
+    for line_block in re.split(r"\n(?=_Z\w+attn_fwd_fp8_kernel\w+:)", fp8_asm):
+        if not re.match(r"_Z\w+attn_fwd_fp8_kernelILi192E", line_block):
+            continue
+        lines = [l for l in line_block.splitlines() if l.strip() and not l.strip().startswith((";", "."))]
+        pending = []   # [registers written, wait states since]
+        for l in lines:
+            m = re.match(r"^\s*v_permlane16_swap_b32_e32\s+(v\d+),\s*(v\d+)", l)
+            if m:
+                seen += 1
+                for reg in (_regs(m.group(1)), _regs(m.group(2))):
+                    for dst, ws in pending:
+                        if _overlap(dst, reg) and ws < 18:
+                            bad.append((l.strip(), ws))
+            w = _wait_states(l)
+            pending = [[d, ws + w] for d, ws in pending if ws + w < 64]
+            m = re.match(r"^\s*v_mfma_scale_f32_32x32x64_f8f6f4\s+(v\[\d+:\d+\])", l)
+            if m:
+                pending.append([_regs(m.group(1)), 0])
+    assert seen > 0
+    assert not bad, bad[:5]
