@@ -84,6 +84,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
   __shared__ __attribute__((aligned(16))) char smem[kSlots * (K_SLOT + V_SLOT)];
   char* const kring = smem;
   char* const vring = smem + kSlots * K_SLOT;
+  // the rings' LDS byte addresses, for the direct-to-LDS loads
+  const unsigned kring_lds = lds_addr(smem);
+  const unsigned vring_lds = kring_lds + kSlots * K_SLOT;
 
   // work-item and group ids from the hardware registers directly (the
   // device-library accessors are not inlined into a kernel compiled with
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       auto issue_k = [&](int j) {
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          char* base = kring + (j % kSlots) * K_SLOT + hs * (K_SLOT / 2);
+          const unsigned base = kring_lds + (j % kSlots) * K_SLOT + hs * (K_SLOT / 2);
           const i32x4 r = tile_rsrc(kbase, krs, 2 * DQK, tile_of(j), hs);
 #pragma unroll
           for (int u = 0; u < KLD; ++u) dma16(r, kvo[u], base + (wq * KLD + u) * 1024);
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const AttnAr
       auto issue_v = [&](int j) {
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          char* base = vring + (j % kSlots) * V_SLOT + hs * (V_SLOT / 2);
+          const unsigned base = vring_lds + (j % kSlots) * V_SLOT + hs * (V_SLOT / 2);
           const i32x4 r = tile_rsrc(vbase, vrs, 2 * DV, tile_of(j), hs);
 #pragma unroll
           for (int u = 0; u < VLD; ++u) dma16(r, vvo[u], base + (wq * VLD + u) * 1024);

@@ -182,6 +182,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   __shared__ __attribute__((aligned(16))) char smem[kSlots * (K_SLOT + V_SLOT)];
   char* const kring = smem;
   char* const vring = smem + kSlots * K_SLOT;
+  // the rings' LDS byte addresses, for the direct-to-LDS loads
+  const unsigned kring_lds = lds_addr(smem);
+  const unsigned vring_lds = kring_lds + kSlots * K_SLOT;
 
   // work-item and group ids from the hardware registers directly (the
   // device-library accessors are not inlined into a kernel compiled with
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       auto issue_k = [&](int kt) {
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          char* base = kring + (kt % kSlots) * K_SLOT;
+          const unsigned base = kring_lds + (kt % kSlots) * K_SLOT;
           const i32x4 r = tile_rsrc(kbase, krs, DQK, kt, hs);
 #pragma unroll
           for (int u = 0; u < 2; ++u) dma16(r, kvo[u], base + hs * (KA_BYTES / 2) + (wsc * 2 + u) * 1024);
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       auto issue_v = [&](int kt) {
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          char* base = vring + (kt % kSlots) * V_SLOT;
+          const unsigned base = vring_lds + (kt % kSlots) * V_SLOT;
           const i32x4 r = tile_rsrc(vbase, vrs, DV, kt, hs);
 #pragma unroll
           for (int u = 0; u < 2; ++u) dma16(r, vvo[u], base + hs * (V_SLOT / 2) + (wsc * 2 + u) * 1024);

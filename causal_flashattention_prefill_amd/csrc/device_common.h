@@ -71,11 +71,18 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, unsigned nbyt
 // with wait_vm() and barriers itself. Lane L's 16 bytes go to
 // lds_wave_base + 16 L (M0 holds the wave-uniform base); past the resource's
 // extent they are zero.
-__device__ __forceinline__ void dma16(const i32x4& rsrc, int voff, const char* lds_wave_base) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_wave_base);
+// lds_wave_base is an LDS byte address (see lds_addr), kept in 32 bits: a
+// generic pointer would be converted, null check included, at every load.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, int voff, unsigned lds_wave_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
                : "memory", "m0");
+}
+
+// LDS byte address of a pointer into a __shared__ array (taken once per
+// kernel from the array itself, whose address the compiler knows).
+__device__ __forceinline__ unsigned lds_addr(const char* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
 // s_waitcnt vmcnt(N) leaving the LDS and export counters alone (gfx9
