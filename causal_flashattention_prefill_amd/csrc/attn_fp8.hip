@@ -104,6 +104,15 @@ __device__ __forceinline__ int vsw(int r) { return ((r >> 1) & 3) | ((r >> 2) & 
 // Key held by LDS row r of a K tile: bits [5:4] and [3:2] of r swapped.
 __device__ __forceinline__ int kswap(int r) { return (r & ~0x3C) | ((r & 0x30) >> 2) | ((r & 0x0C) << 2); }
 
+// Chunk swizzle of the 64-byte d 128..191 K rows. Each 16-lane group of a
+// read should touch 16 distinct 16-byte bank groups of the 256 bytes the
+// LDS serves per cycle; a row's 256-byte offset is its bits 0, 1. The 8-byte
+// reads of the one-group kernels cover rows 16 kb + n (n < 16): swizzle by
+// bits 2, 3. The 16-byte reads of the 32x32x64 operand cover rows 16 j +
+// 8 h + i (j < 2): swizzle by bits 3, 4.
+template <bool WIDE>
+__device__ __forceinline__ int kbsw_of(int r) { return WIDE ? ((r >> 3) & 3) : ((r >> 2) & 3); }
+
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
@@ -169,6 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   // per wave, too few for a 32-column product) they come from two 16x16x32
   // FP8 instructions per block, which run at half the rate
   constexpr bool kWide = D192 && QG == 2 && !PRECISE;
+  auto kbsw = [](int r) { return kbsw_of<kWide>(r); };
   constexpr int KA_BYTES = kTileK * 128;            // K region for d 0..127
   constexpr int KB_BYTES = D192 ? kTileK * 64 : 0;  // K region for d 128..191
   constexpr int K_SLOT = KA_BYTES + KB_BYTES;
@@ -212,14 +222,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
   const float c8s = 8.0f * sl2 * kInv65535;
   // ds_bpermute source of the lane's E8M0 scale: lane groups 1 and 2 swap
   const int psc_addr = 4 * (((g == 1) || (g == 2)) ? (lane ^ 48) : lane);
-  // LDS base of this lane's d 128..191 K reads on the 32x32x64 instruction
-  // (instruction row x = lane % 32 = 8 j + 4 h + i on LDS row 16 j + 8 h + i,
-  // chunks 2 (lane / 32) and 2 (lane / 32) + 1 swizzled by 2 h)
-  const int khb = [&] {
-    const int x = lane & 31;
-    const int row0 = 16 * (x >> 3) + 8 * ((x >> 2) & 1) + (x & 3);
-    return kTileK * 128 + row0 * 64 + (((2 * (lane >> 5)) ^ (2 * ((x >> 2) & 1))) << 4);
-  }();
+  // LDS bases of this lane's d 128..191 K reads on the 32x32x64
+  // instruction: instruction row x = lane % 32 = 8 j + 4 h + i on LDS row
+  // 16 j + 8 h + i (+ 64 p + 4 o), chunks 2 (lane / 32) (lo) and
+  // 2 (lane / 32) + 1 (hi), swizzled as kbsw below
+  const int x32 = lane & 31;
+  const int krow0 = 16 * (x32 >> 3) + 8 * ((x32 >> 2) & 1) + (x32 & 3);
+  const int khb_lo = kTileK * 128 + krow0 * 64 + (((2 * (lane >> 5)) ^ ((krow0 >> 3) & 3)) << 4);
+  const int khb_hi = kTileK * 128 + krow0 * 64 + (((2 * (lane >> 5) + 1) ^ ((krow0 >> 3) & 3)) << 4);
   const float dvs = a.v_descale[0];
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3fn 1.0
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // Direct global-to-LDS tile loads; K row r of a slot holds key
       // kswap(r), V row r holds key r; 16-byte chunks XOR-swizzled by row:
       //  K d 0..127:   row * 128 + ((c ^ ((row >> 1) & 7)) << 4)
-      //  K d 128..191: row * 64  + ((c ^ ((row >> 2) & 3)) << 4)
+      //  K d 128..191: row * 64  + ((c ^ kbsw(row)) << 4)
       //  V:            row * 128 + ((c ^ vsw(row)) << 4)
       // The V swizzle puts the sixteen rows that a half-wave of each
       // transposing read touches (8 consecutive keys in each of two lane
@@ -373,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       }
       if (D192) {
         const int p = wsc * 1024 + lane * 16;
-        const int row = p >> 6, x = ((p & 63) >> 4) ^ ((row >> 2) & 3);
+        const int row = p >> 6, x = ((p & 63) >> 4) ^ kbsw(row);
         kvo[2] = kswap(row) * krs + 128 + x * 16;
       }
       // resource at rows 64 hs .. of key tile kt
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
           // 128+8g.. is half g & 1 of chunk g >> 1, d 160+8g.. of chunk
           // 2 + (g >> 1)
           const char* kr = ka + KA_BYTES + row * 64 + (g & 1) * 8;
-          const int sw2 = (row >> 2) & 3;
+          const int sw2 = kbsw(row);
           f.b0 = __builtin_bit_cast(long, lds_load<u32x2>(kr + (((g >> 1) ^ sw2) << 4)));
           f.b1 = __builtin_bit_cast(long, lds_load<u32x2>(kr + (((2 + (g >> 1)) ^ sw2) << 4)));
         }
@@ -450,13 +460,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
       // of instruction w is key 64 p + 16 (2 h + o) + 4 j + i, so that after
       // the lane swaps lane group g holds the keys of the 16x16 layout
       // (16 g .., 64 + 16 g ..). kswap puts that key on LDS row 64 p + 16 j +
-      // 8 h + 4 o + i, whose chunk swizzle is 2 h + o: every read is the
-      // lane's base address khb plus a constant (4096 p + 256 o; for o = 1
-      // the two chunks trade places).
+      // 8 h + 4 o + i, whose chunk swizzle (rows bits 3, 4: h + 2 (j % 2))
+      // does not depend on p and o: every read is one of the lane's two base
+      // addresses plus 4096 p + 256 o.
       auto khi_frag = [&](const char* ka, int w) {
-        const char* kr = ka + khb + 4096 * (w >> 1) + 256 * (w & 1);
-        const u32x4 lo = lds_load<u32x4>(kr + ((w & 1) ? 16 : 0));
-        const u32x4 hi = lds_load<u32x4>(kr + ((w & 1) ? 0 : 16));
+        const int off = 4096 * (w >> 1) + 256 * (w & 1);
+        const u32x4 lo = lds_load<u32x4>(ka + khb_lo + off);
+        const u32x4 hi = lds_load<u32x4>(ka + khb_hi + off);
         return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       };
 
