@@ -597,15 +597,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
 #pragma unroll
           for (int u = 0; u < kPfK; ++u) kfb[u] = k_frag(ka, u);
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (D192 && !kWide ? 4 : 2) * kPfK, 0);
-          // d 128..191 (d_qk = 192) accumulate onto the result of the scaled
-          // instruction. Issued straight after that result, such a pair was
-          // given no wait states and read a stale accumulator on the GPU, so
-          // another instruction always sits between them: with two query
-          // groups the other group's scaled instruction, with one the scaled
-          // instruction of block kb + 1 (the pair of block kb - 1 is issued
-          // after the scaled instruction of block kb). Scheduling barriers
-          // hold the order; a CPU test checks it in the built code.
-          constexpr bool kDefer = D192 && QG == 1;
+          // d_qk = 192 with one query group: the pair of 16x16x32 FP8
+          // instructions over d 128..191 accumulates onto the result of the
+          // scaled instruction. Issued straight after that result, such a
+          // pair was given no wait states and read a stale accumulator on the
+          // GPU, so the scaled instruction of block kb + 1 always sits between
+          // them (the pair of block kb - 1 is issued after the scaled
+          // instruction of block kb), held there by a scheduling barrier; a
+          // CPU test checks the order in the built code.
+          constexpr bool kDefer = D192 && !kWide;
+          static_assert(!kDefer || QG == 1 || PRECISE, "two-group d 192 kernels take the 32x32x64 path");
           long pb0 = 0, pb1 = 0;   // d 128..191 K fragments of the deferred block
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) {
@@ -647,16 +648,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(const AttnArg
               }
               pb0 = cur.b0;
               pb1 = cur.b1;
-            } else if (D192 && !kWide) {
-              // both groups' scaled instructions first, held there by a
-              // scheduling barrier: the other group's scaled instruction then
-              // separates each pair from the result it accumulates onto
-              __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-              for (int qg = 0; qg < QG; ++qg) {
-                s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur.b0, qx[qg][0], s[qg][kb], 0, 0, 0);
-                s[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur.b1, qx[qg][1], s[qg][kb], 0, 0, 0);
-              }
             }
             if (kb + kPfK < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D192 && !kWide ? 4 : 2, 0);
             if (kDefer && kb == 0) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
