@@ -84,3 +84,66 @@ def test_quantize_on_two_streams_concurrently():
             x8, ds = outs[j][i]
             assert float(ds.item()) == float(d), f"stream {j} call {i}: descale {ds.item()} vs {d}"
             assert np.array_equal(x8.view(torch.uint8).cpu().numpy(), codes), f"stream {j} call {i}: codes differ"
+
+
+def test_attention_on_two_streams_concurrently():
+    """Two host threads, each on its own stream, run attention on different
+    shapes (BF16 d 128 GQA with the LSE on the automatic 128-row tiles; FP8
+    d_qk 192 set to 256-row tiles) at the same time, right after
+    zyfa_release, so both build their plans concurrently under the library's
+    lock and their persistent grids share the GPU. Every result must equal
+    the same call run alone, bit for bit."""
+    import threading
+    rng = np.random.default_rng(45)
+    zy.zyfa_set_tile_q(1, 2500, 16, 16, d_qk=192, dtype=zy.DTYPE_FP8, tile_q=256)
+
+    def bf16(shape, s=1.0):
+        return torch.from_numpy((rng.standard_normal(shape) * s).astype(np.float32)).to(torch.bfloat16).cuda()
+
+    qa, ka, va = bf16((1, 3000, 8, 128)), bf16((1, 3000, 2, 128)), bf16((1, 3000, 2, 128))
+    qb, kb, vb = bf16((1, 16, 2500, 192)), bf16((1, 16, 2500, 192)), bf16((1, 16, 2500, 128))
+    (qb8, dq), (kb8, dk), (vb8, dv) = (zy.zyfa_fp8_quantize(x) for x in (qb, kb, vb))
+    calls = [lambda out, lse, s: zy.zyfa_fwd(qa, ka, va, out, lse, stream=s),
+             lambda out, lse, s: zy.zyfa_fwd(qb8, kb8, vb8, out, None, layout="bhsd", q_descale=dq, k_descale=dk,
+                                             v_descale=dv, stream=s)]
+    shapes = [((1, 3000, 8, 128), (1, 8, 3000)), ((1, 16, 2500, 128), None)]
+    print("case attention on two streams", flush=True)
+    refs = []
+    for f, (os_, ls) in zip(calls, shapes):
+        o = torch.empty(os_, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(ls, dtype=torch.float32, device="cuda") if ls else None
+        f(o, lse, torch.cuda.current_stream())
+        refs.append((o, lse))
+    torch.cuda.synchronize()
+    n = 6
+    outs = [[(torch.empty(os_, dtype=torch.bfloat16, device="cuda"),
+              torch.empty(ls, dtype=torch.float32, device="cuda") if ls else None) for _ in range(n)]
+            for os_, ls in shapes]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    errors = []
+
+    def worker(j):
+        try:
+            with torch.cuda.stream(streams[j]):
+                for i in range(n):
+                    calls[j](outs[j][i][0], outs[j][i][1], streams[j])
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    zy.zyfa_release()
+    torch.cuda.synchronize()
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    zy.zyfa_set_tile_q(1, 2500, 16, 16, d_qk=192, dtype=zy.DTYPE_FP8, tile_q=0)
+    for j in range(2):
+        ro, rl = refs[j]
+        for i in range(n):
+            o, lse = outs[j][i]
+            assert torch.equal(o, ro), f"shape {j} call {i}: out differs"
+            if rl is not None:
+                assert torch.equal(lse, rl), f"shape {j} call {i}: lse differs"
