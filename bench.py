@@ -517,7 +517,7 @@ def context_case(name, zy, args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "the attention path runs on one GPU and bench.py measures one GPU; run with --gpus 1"}))
         sys.exit(2)
     # the CPU baseline runs first, in fresh worker processes, before this
     # process touches the GPU
