@@ -84,13 +84,15 @@ def check_fp8(out, ref_out, what=""):
 
 
 def fp8_known_limit(out, ref_out, allowance, what=""):
-    """The fast FP8 modes on activation-like inputs, which do not meet the
-    max gate (the FP8 matrix instructions' score sums; see FP8_MFMA_REL):
-    prints the literal max and the number of elements over the gate, holds
-    the mean gate, and, as a separate diagnostic, checks that every element
-    stays within the gate plus the error that score precision explains
-    (allowance: per row, leading axes of out). The precise mode meets the
-    gate itself (check_fp8)."""
+    """The fast FP8 modes where they do not meet the max gate: on
+    activation-like inputs (the FP8 matrix instructions' score sums; see
+    FP8_MFMA_REL) and on rows with a handful of keys of nearly equal weight
+    (the e4m3 rounding of the probabilities; see FP8_P_REL). Prints the
+    literal max and the number of elements over the gate, holds the mean
+    gate, and, as a separate diagnostic, checks that every element stays
+    within the gate plus the error that the named cause explains (allowance:
+    per row, leading axes of out). The precise mode meets the gate itself
+    (check_fp8)."""
     d = np.abs(out - ref_out)
     bound = FP8_OUT_MAX + BF16_OUT_REL_ROUND * np.abs(ref_out)
     over = int(np.count_nonzero(d > bound))
@@ -101,6 +103,41 @@ def fp8_known_limit(out, ref_out, allowance, what=""):
     diag = bound + allowance[..., None]
     assert np.all(d <= diag), f"{what}: error beyond what FP8 score precision explains: max {d.max():.3e}"
     return d.max(), d.mean(), over
+
+
+# An e4m3 value keeps 3 mantissa bits, so rounding a normal probability to
+# nearest moves it by at most 2^-4 of itself; with the per-block scaling a
+# probability below 2^-6 of its block's largest is subnormal and moves by at
+# most 2^-10 of that largest one, at most 2^-10 of the row's largest weight
+# (FP8_P_ABS allows twice that). On a row with two keys of weights w0, w1
+# the output can move by up to w0 w1 2^-4 |v1 - v0|: over 6e-2 for
+# |v1 - v0| ~ 4.
+FP8_P_REL = 2.0 ** -4
+FP8_P_ABS = 2.0 ** -9
+
+
+def fp8_p_rounding_allowance(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, rows) -> np.ndarray:
+    """Per-row bound on |d out| caused by rounding the probabilities to e4m3
+    alone (a diagnostic of that known limit, never part of the gate).
+
+    With the exact softmax weights w_j of row i and o = sum_j w_j v_j, weights
+    perturbed to w_j (1 + d_j) + a_j (|d_j| <= FP8_P_REL, |a_j| <= FP8_P_ABS
+    max_j w_j) give o' - o = sum_j (w_j d_j + a_j) (v_j - o) / sum_j (w_j (1 +
+    d_j) + a_j), since sum_j w_j (v_j - o) = 0. Returns, per row, the maximum
+    over the columns of that bound."""
+    rows = np.asarray(rows)
+    out = np.empty(rows.shape[0])
+    for r, i in enumerate(rows):
+        s = (kh[: i + 1] @ qh[i]) * scale
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        o = w @ vh[: i + 1]
+        dev = np.abs(vh[: i + 1] - o)                      # (keys, d_v)
+        a = FP8_P_ABS * w.max()
+        num = FP8_P_REL * (w @ dev) + a * dev.sum(axis=0)
+        den = 1.0 - FP8_P_REL - a * (i + 1)
+        out[r] = (num / den).max()
+    return out
 
 
 # gfx950's FP8 matrix instructions (v_mfma_scale_f32_16x16x128_f8f6f4 and the

@@ -63,6 +63,8 @@ def test_workload1_full():
     (1, 255, 2, 2, 128, "bhsd"),
     (1, 257, 2, 1, 128, "bshd"),
     (1, 4097, 2, 1, 128, "bshd"),
+    (37, 100, 6, 2, 128, "bshd"),    # many short sequences: one partial tile per slice
+    (37, 100, 4, 4, 192, "bhsd"),
 ])
 @pytest.mark.parametrize("tile_q", [256, 128])
 def test_small_shapes(B, S, H, Hk, dqk, layout, with_lse, tile_q):
