@@ -4,6 +4,8 @@ Both sides see the same inputs: the seeded float32 draws of `workloads`
 are cast to bf16 by torch for the GPU and by the oracle's own codec for the
 oracle; `bf16_pair` checks that the two casts agree bit for bit.
 """
+import math
+
 import numpy as np
 import torch
 
@@ -116,15 +118,22 @@ FP8_P_REL = 2.0 ** -4
 FP8_P_ABS = 2.0 ** -9
 
 
-def fp8_p_rounding_allowance(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, rows) -> np.ndarray:
+def fp8_p_rounding_allowance(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, rows,
+                             rel: float = FP8_P_REL, absc: float = FP8_P_ABS) -> np.ndarray:
     """Per-row bound on |d out| caused by rounding the probabilities to e4m3
     alone (a diagnostic of that known limit, never part of the gate).
 
     With the exact softmax weights w_j of row i and o = sum_j w_j v_j, weights
-    perturbed to w_j (1 + d_j) + a_j (|d_j| <= FP8_P_REL, |a_j| <= FP8_P_ABS
-    max_j w_j) give o' - o = sum_j (w_j d_j + a_j) (v_j - o) / sum_j (w_j (1 +
-    d_j) + a_j), since sum_j w_j (v_j - o) = 0. Returns, per row, the maximum
-    over the columns of that bound."""
+    perturbed to w_j (1 + d_j) + a_j (|d_j| <= rel, and |a_j| <= min(absc
+    max_j w_j, w_j): a probability that is too small for a normal code is
+    rounded to a subnormal one or to zero, never by more than itself) give
+    o' - o = sum_j (w_j d_j + a_j) (v_j - o) / sum_j (w_j (1 + d_j) + a_j),
+    since sum_j w_j (v_j - o) = 0. Returns, per row, the maximum over the
+    columns of that bound. rel = 2^-4 is rounding to nearest; 2^-3 (one code
+    step) also covers a code that the kernel's fp32 score rounds the other
+    way at a tie, and lean P, whose value 2^floor(y) (1 + frac(y)) stays
+    within about 9 % of 2^y; lean P writes code 0 for probabilities below
+    about 2^-6.9 of their block's scale (absc = 2^-5 covers it)."""
     rows = np.asarray(rows)
     out = np.empty(rows.shape[0])
     for r, i in enumerate(rows):
@@ -133,10 +142,27 @@ def fp8_p_rounding_allowance(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, sca
         w /= w.sum()
         o = w @ vh[: i + 1]
         dev = np.abs(vh[: i + 1] - o)                      # (keys, d_v)
-        a = FP8_P_ABS * w.max()
-        num = FP8_P_REL * (w @ dev) + a * dev.sum(axis=0)
-        den = 1.0 - FP8_P_REL - a * (i + 1)
+        a = np.minimum(absc * w.max(), w)
+        num = rel * (w @ dev) + a @ dev
+        den = 1.0 - rel - a.sum()
         out[r] = (num / den).max()
+    return out
+
+
+def fp8_p_rounding_lse_allowance(qh: np.ndarray, kh: np.ndarray, scale: float, rows, rel: float = FP8_P_REL,
+                                 absc: float = FP8_P_ABS) -> np.ndarray:
+    """Per-row bound on |d LSE| (natural log) from the same perturbed weights
+    as fp8_p_rounding_allowance: the rounded sum lies within a factor
+    (1 +- (rel + sum_j a_j)) of the exact one, so |d LSE| <= -ln(1 - rel -
+    sum_j a_j)."""
+    rows = np.asarray(rows)
+    out = np.empty(rows.shape[0])
+    for r, i in enumerate(rows):
+        s = (kh[: i + 1] @ qh[i]) * scale
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        a = np.minimum(absc * w.max(), w)
+        out[r] = -math.log(1.0 - rel - a.sum())
     return out
 
 
