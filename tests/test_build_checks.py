@@ -10,6 +10,9 @@ instruction once read a stale accumulator. The kernel orders its
 instructions so that another matrix instruction always sits between the two
 (scheduling barriers); this test reads the built code and fails if any
 scaled FP8 result is read by the next matrix instruction of another kind.
+Further checks hold the built code to the instruction mix of the d_qk = 192
+kernels, the wait states before the lane swaps, and the register-spill
+counts each kernel was measured with.
 """
 import os
 import re
@@ -27,19 +30,28 @@ def _hipcc():
     return p if os.path.exists(p) else shutil.which("hipcc")
 
 
-@pytest.fixture(scope="module")
-def fp8_asm(tmp_path_factory):
+def _build_asm(tmp_path_factory, name):
     hipcc = _hipcc()
     if hipcc is None:
         pytest.skip("hipcc not available")
     from causal_flashattention_prefill_amd.build import EXTRA_FLAGS, HIPCC_FLAGS
-    out = str(tmp_path_factory.mktemp("asm") / "attn_fp8.s")
+    out = str(tmp_path_factory.mktemp("asm") / (name + ".s"))
     flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
-    cmd = [hipcc, *flags, *EXTRA_FLAGS["attn_fp8.hip"], "-I", os.path.join(ROOT, "include"),
-           "--cuda-device-only", "-S", SRC, "-o", out]
+    cmd = [hipcc, *flags, *EXTRA_FLAGS.get(name, []), "-I", os.path.join(ROOT, "include"),
+           "--cuda-device-only", "-S", os.path.join(os.path.dirname(SRC), name), "-o", out]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     with open(out) as f:
         return f.read()
+
+
+@pytest.fixture(scope="module")
+def fp8_asm(tmp_path_factory):
+    return _build_asm(tmp_path_factory, "attn_fp8.hip")
+
+
+@pytest.fixture(scope="module")
+def bf16_asm(tmp_path_factory):
+    return _build_asm(tmp_path_factory, "attn_bf16.hip")
 
 
 _MFMA = re.compile(r"^\s*(v_mfma\w*)\s+([va]\[?[\d:]+\]?),\s*([va]\[?[\d:]+\]?),\s*([va]\[?[\d:]+\]?),\s*"
@@ -151,3 +163,30 @@ def test_lane_swaps_wait_for_the_32x32x64_results(fp8_asm):
                 pending.append([_regs(m.group(1)), 0])
     assert seen > 0
     assert not bad, bad[:5]
+
+
+def _kernel_metadata(asm):
+    """{kernel symbol: {field: int}} from the code-object metadata."""
+    out = {}
+    for blk in re.split(r"\n\s+- \.", asm):
+        m = re.search(r"^\s*\.name:\s+(_Z\S+attn_fwd_\w+)$", "." + blk, re.M)
+        if not m:
+            continue
+        fields = dict((k, int(v)) for k, v in re.findall(r"\.(\w+):\s+(\d+)$", "." + blk, re.M))
+        out[m.group(1)] = fields
+    return out
+
+
+def test_register_spills_stay_within_their_measured_budget(fp8_asm, bf16_asm):
+    # the kernels keep their scores, output and fragments in registers; a
+    # spill to scratch memory costs a load and a store per use. Three kernels
+    # spill a few registers (BF16 d_qk 192 without the LSE: 3; FP8 lean P at
+    # d_qk 192 on 256-row tiles: 1), which measured within noise of an
+    # unspilled build; anything beyond that is a regression.
+    md = {**_kernel_metadata(fp8_asm), **_kernel_metadata(bf16_asm)}
+    assert len(md) == 20 + 8, sorted(md)
+    assert all({"vgpr_spill_count", "private_segment_fixed_size", "vgpr_count"} <= set(f) for f in md.values())
+    over = {n: (f.get("vgpr_spill_count"), f.get("private_segment_fixed_size")) for n, f in md.items()
+            if f.get("vgpr_spill_count", 0) > 3 or f.get("private_segment_fixed_size", 0) > 16}
+    assert not over, over
+    assert all(f.get("vgpr_count", 0) <= 256 for f in md.values())
