@@ -273,8 +273,8 @@ def zyfa_fp8_quantize(x, x8=None, descale=None, stream=None):
 
 def zyfa_fp8_quantize_rotated(x, signs=None, x8=None, descale=None, *, shift=None, layout: str = "bshd",
                               stream=None):
-    """Rotate the last axis of x (d = 128 or 192) by the orthogonal matrix of
-    zyfa.h's zyfa_fp8_quantize_rotated, then quantize per tensor. signs:
+    """Rotate the last axis of x (d = 128; other d raise) by the orthogonal
+    matrix of zyfa.h's zyfa_fp8_quantize_rotated, then quantize per tensor. signs:
     d values of +1 / -1 (a sequence or array on the host), or None for all
     +1. shift: optional (batch, heads, d) fp32 CUDA tensor subtracted from
     every position of its head before the rotation (K smoothing; x is then
