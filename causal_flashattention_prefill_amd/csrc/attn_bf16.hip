@@ -31,8 +31,8 @@
 //    block kb: a lane owns part of one query row, and P goes from registers
 //    straight into the PV product as the B operand.
 //  - O^T += V^T P^T with V^T read from LDS by ds_read_b64_tr_b16, which
-//    transposes 16-bit values during the read, so V is stored in LDS as it
-//    arrives from memory.
+//    transposes 16-bit values during the read, so the V tile keeps its
+//    memory layout in LDS and no transposing pass is needed.
 //  - Online softmax in base 2 (log2(e) folded into the scale, one FMA per
 //    score before the exponential) with a lazy reference maximum: it moves
 //    only when some score passes it by kTau; one wave-wide ballot decides,

@@ -2,10 +2,10 @@
 // BF16 output, for gfx950 (CDNA4).
 //
 // What is computed: "ZYFA" README, Usage (descales read from device memory
-// and applied by the kernel), Supported configurations, Accuracy (the output
-// is divided by the sum of the same rounded probabilities that multiply V,
-// and the LSE comes from those rounded probabilities, so that results over
-// different key ranges merge consistently). Query row r sits at position
+// and applied by the kernel), Supported configurations, Accuracy (the row
+// sum that normalises the output, and the LSE, are taken over exactly the
+// rounded probabilities that weight V, which keeps partial results over
+// separate key ranges mergeable). Query row r sits at position
 // r + delta relative to the keys (key c is visible to row r when
 // c <= r + delta): delta = 0 with seqlen_q == seqlen_k is whole-sequence
 // causal attention, other values give partial results over a key range.

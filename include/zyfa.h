@@ -75,9 +75,9 @@ enum zyfa_dtype {
  *  query heads share a KV head). The softmax scale is 1/sqrt(d_qk).
  *  Any seqlen >= 1 works: rows past seqlen read as zeros up to the kernel's
  *  query-tile multiple, which is exact for causal attention (README, Usage).
- *  The first call for a shape builds a plan (job table) with a blocking
- *  host-to-device copy; call zyfa_prepare first if the call is to be
- *  captured into a graph.
+ *  A shape's plan (its job table) is made on its first call, with a
+ *  blocking host-to-device copy; call zyfa_prepare first if the call is to
+ *  be captured into a graph.
  */
 int zyfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int batch, int seqlen, int nheads, int nheads_k, int d_qk, int d_v,
@@ -259,9 +259,9 @@ int zyfa_fp8_quantize(const void* x, int x_dtype, long long numel, void* x8, flo
  * ("ZYFA" README, "Using FP8 attention in a model": a Hadamard rotation of
  * q and k before quantization; (q R)(k R)^T = q k^T, so attention on the
  * rotated q and k equals attention on the originals up to rounding, and the
- * rotation spreads channels with large values over all channels, which
- * lowers the quantization error). Rotate q and k with the same signs;
- * leave v unrotated.
+ * rotation mixes the few large channels into all of them, so one
+ * power-of-two scale fits the tensor better and its codes lose less).
+ * Rotate q and k with the same signs; leave v unrotated.
  *   R = diag(s) H_128 / sqrt(128), H Sylvester's Hadamard matrix
  *   y = x R (computed in fp32 with a fast Walsh-Hadamard transform), then
  *   descale = 2^ceil(log2(max|y| / 448)) (1 when y == 0, >= 2^-126) and
@@ -291,9 +291,10 @@ int zyfa_fp8_quantize_rotated(const void* x, int x_dtype, long long rows, int d,
  *  k       device pointer, bf16 or fp32 (k_dtype), [batch, seqlen, nheads_k,
  *          d] (bshd) or [batch, nheads_k, seqlen, d] (bhsd), 16-byte aligned.
  *  mean    device pointer, batch * nheads_k * d fp32 (caller-owned).
- *  d is 128 or 192. Deterministic; asynchronous on `stream`. Chunked prefill
- *  and prefix caching need a mean fixed in advance (every key of a row must
- *  lose the same vector): compute it once and pass the same one each time.
+ *  d is 128 or 192. Deterministic; asynchronous on `stream`. When the keys
+ *  of a sequence are quantized in several calls (chunks, a cached prefix),
+ *  every key of a row must lose the same vector: compute the mean once and
+ *  pass that same vector to every call.
  */
 int zyfa_key_mean(const void* k, int k_dtype, int batch, int seqlen, int nheads_k, int d, int layout,
                   float* mean, void* stream);

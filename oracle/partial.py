@@ -2,8 +2,8 @@
 results, in float64 (oracle; test infrastructure only).
 
 What is computed, from the pages:
-- "ZYFA" README, Accuracy: the log-sum-exp is returned so that results
-  computed over different key ranges can be merged consistently.
+- "ZYFA" README, Accuracy: the log-sum-exp comes back with the output so
+  that outputs over disjoint key ranges can be combined into the whole.
 - flash-attention RDNA3 extension page, kernel notes: a split of the keys
   across workers yields partial outputs with their LSE, combined by an LSE
   reduction.

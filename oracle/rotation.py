@@ -54,7 +54,8 @@ def quantize_rotated_ref(x, signs):
 
 
 # ---- K smoothing ("ZYFA" README, "Using FP8 attention in a model"):
-# subtract the mean key of each head over the sequence before the rotation.
+# before the rotation, take from every key of a head that head's average
+# key over all positions.
 # Every key of a row then loses the same vector c, so each score of the row
 # moves by the same q . c and the softmax, hence the output, is unchanged;
 # the log-sum-exp moves by scale * q . c.

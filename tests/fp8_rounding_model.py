@@ -3,8 +3,8 @@ check of the FP8 kernels, not an oracle).
 
 The oracle (oracle/attention.py) is exact softmax attention on the
 dequantized inputs, and every FP8 accuracy claim is made against it. An FP8
-kernel instead multiplies V by e4m3fn-rounded probabilities and divides by
-the sum of the same rounded values. This module writes out which rounded
+kernel instead weights V by e4m3fn-rounded probabilities and normalises by
+the total of those rounded weights. This module writes out which rounded
 values THIS library's kernels use, so a GPU result can be checked far more
 tightly than the accuracy gate allows. Its constants are the kernels'
 choices, not the pages': 128-key tiles, 32-key scale blocks (the scaled
