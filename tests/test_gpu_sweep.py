@@ -121,3 +121,113 @@ def test_random_range(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, dtype, tq):
     else:
         assert np.array_equal(np.isneginf(got_l), np.isneginf(rows(rl)))
         check_partial(out_to_f64(out), ro, None, rows(rl), f"sweep range fp8 Sq{Sq} Sk{Sk}", fp8=True)
+
+
+def _draw_mode_case(i):
+    rng = np.random.default_rng(9700 + i)
+    B = int(rng.integers(1, 3))
+    S = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 1300))]))
+    Hk = int(rng.choice([1, 2, 3]))
+    H = Hk * int(rng.choice([1, 2, 4]))
+    dqk = int(rng.choice([128, 192]))
+    layout = str(rng.choice(["bshd", "bhsd"]))
+    lse = bool(rng.integers(0, 2))
+    tq = int(rng.choice([128, 256]))
+    p_mode = str(rng.choice(["exact", "lean", "precise"]))
+    return B, S, H, Hk, dqk, layout, lse, tq, p_mode
+
+
+MODE_CASES = [_draw_mode_case(i) for i in range(32)]
+
+
+@pytest.mark.parametrize("B,S,H,Hk,dqk,layout,lse,tq,p_mode", MODE_CASES)
+def test_random_shape_fp8_modes(B, S, H, Hk, dqk, layout, lse, tq, p_mode):
+    """FP8 in every probability mode over seeded random shapes. Against the
+    oracle: the precise mode at the full gate; exact and lean P at the gate,
+    or, on rows that rest on a few keys, within what one e4m3 code step of
+    each probability explains (the known limit of e4m3 probabilities; on
+    sequences of at most 64 tokens it may reach the mean too). Against
+    the rounding model of the kernels (tests/fp8_rounding_model.py) on
+    sampled rows, its output rounded to bf16 as the kernel's is: the tight
+    regression bound, in every mode."""
+    import fp8_rounding_model
+    from parity import (BF16_OUT_REL_ROUND, FP8_LSE_MAX, FP8_OUT_MAX, FP8_OUT_MEAN, FP8_PRECISE_LSE_MAX,
+                        check_fp8_rounding, fp8_p_rounding_allowance, fp8_p_rounding_lse_allowance)
+    print(f"case sweep fp8 {p_mode} B{B} S{S} H{H}/{Hk} d{dqk} {layout} lse={lse} tile_q {tq}", flush=True)
+    w = Workload("sweep_modes", B, S, H, Hk, dqk, 128, layout, ("fp8",), lse, False, 7000 + S + 7 * H + dqk)
+    q, k, v = generate(w)
+    dev, deq = [], []
+    for t, r in (bf16_pair(x) for x in (q, k, v)):
+        x8, ds = zy.zyfa_fp8_quantize(t)
+        codes, d = oracle.fp8_quantize_ref(r)
+        dev.append((x8, ds))
+        deq.append(oracle.e4m3fn_decode(codes) * float(d))
+    (q8, qs), (k8, ks), (v8, vs) = dev
+    rq, rk, rv = deq
+    with tile_height(zy, B, S, H, Hk, dqk, zy.DTYPE_FP8, tq):
+        res = zy.zyfa_fwd(q8, k8, v8, layout=layout, return_lse=True, q_descale=qs, k_descale=ks, v_descale=vs,
+                          p_mode=p_mode)
+        torch.cuda.synchronize()
+    out, got_lse = res
+    o = out_to_f64(out)
+    gl = got_lse.cpu().numpy().astype(np.float64)
+    ref_out, ref_lse = oracle.causal_attention_ref(rq, rk, rv, layout=layout)
+    what = f"sweep fp8 {p_mode} S{S}"
+    hv = (lambda x: np.swapaxes(x, 1, 2)) if layout == "bshd" else (lambda x: x)
+    Q, K, V = hv(rq), hv(rk), hv(rv)
+    g = H // Hk
+    scale = 1.0 / np.sqrt(dqk)
+    rows = np.arange(S)
+    if p_mode == "precise":
+        check_fp8(o, ref_out, what)
+        lse_bound = np.full(gl.shape, FP8_PRECISE_LSE_MAX)
+    else:
+        # one code step of each probability (2^-3 relative: rounding to
+        # nearest, a tie the fp32 score rounds the other way, and lean P's
+        # linear 2^y), and lean P's zeroing below 2^-6.9 of the block's
+        # scale (absolute 2^-5 of the largest weight)
+        rel, absc = (2.0 ** -3, 2.0 ** -9) if p_mode == "exact" else (2.0 ** -3, 2.0 ** -5)
+        try:
+            check_fp8(o, ref_out, what)
+        except AssertionError:
+            # the known limit: every element within the gate plus what the
+            # e4m3 rounding of its row's probabilities explains. On a
+            # sequence of a dozen tokens every row rests on a few keys, and
+            # the mean can pass the mean gate too (12 tokens, exact P: the
+            # rounding model's mean is 5.05e-3); the rounding-model check
+            # below still holds the kernel to its design.
+            allow = np.stack([np.stack([fp8_p_rounding_allowance(Q[b, h], K[b, h // g], V[b, h // g], scale, rows,
+                                                                 rel=rel, absc=absc) for h in range(H)])
+                              for b in range(B)])
+            allow = np.swapaxes(allow, 1, 2) if layout == "bshd" else allow
+            d = np.abs(o - ref_out)
+            bound = FP8_OUT_MAX + BF16_OUT_REL_ROUND * np.abs(ref_out)
+            print(f"{what}: KNOWN LIMIT literal max|dout|={d.max():.3e}, {int(np.count_nonzero(d > bound))} of "
+                  f"{d.size} elements over the 6e-2 gate, mean={d.mean():.2e}", flush=True)
+            assert np.all(np.isfinite(o))
+            assert np.all(d <= bound + allow[..., None]), f"{what}: error beyond what e4m3 probabilities explain"
+            assert S <= 64 or d.mean() <= FP8_OUT_MEAN, f"{what}: mean|dout|={d.mean():.3e}"
+        lal = np.stack([np.stack([fp8_p_rounding_lse_allowance(Q[b, h], K[b, h // g], scale, rows, rel=rel,
+                                                               absc=absc) for h in range(H)]) for b in range(B)])
+        lse_bound = np.maximum(FP8_LSE_MAX, lal)
+    dl = np.abs(gl - ref_lse)
+    assert np.all(np.isfinite(dl)) and np.all(dl <= lse_bound), f"{what}: max|dLSE|={dl.max():.3e}"
+    # the rounding model on sampled rows: first and last rows, 256-row block
+    # edges, random ones
+    rng = np.random.default_rng(S)
+    edges = np.array([r for r in (255, 256, 511, 512, 767, 768, 1023, 1024) if r < S], dtype=np.int64)
+    pick = np.unique(np.concatenate([np.arange(min(S, 8)), np.arange(max(0, S - 8), S), edges,
+                                     rng.integers(0, S, size=min(S, 24))]).astype(np.int64))
+    model_mode = "precise" if p_mode == "precise" else ("exact" if p_mode == "exact" else "lean_offdiag")
+    gots, refs, glse, rlse = [], [], [], []
+    O = hv(o)
+    for b in range(B):
+        for h in range(H):
+            ro, rl = fp8_rounding_model.fp8_attention_rows_ref(rq, rk, rv, b, h, pick, layout=layout,
+                                                               p_mode=model_mode)
+            gots.append(O[b, h][pick])
+            refs.append(oracle.bf16_round(ro.astype(np.float32)))   # the kernel rounds O to bf16 last
+            glse.append(gl[b, h][pick])
+            rlse.append(rl)
+    check_fp8_rounding(np.concatenate(gots), np.concatenate(refs), np.concatenate(glse), np.concatenate(rlse),
+                       what + " rounding")
