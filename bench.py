@@ -68,16 +68,24 @@ RANGE_CASES = {
     "fp8_chunk4096_s16384": "fp8",
 }
 CHUNK_Q = 4096
-# The README's own benchmark configuration at 16K tokens (Performance,
-# kernel-benchmark protocol): causal MHA, batch 1, max(32, 262144 / S) = 32
-# heads, q, k, v Gaussian with standard deviation 0.1, bshd. Reported beside
-# the README's MI355X figure for the same configuration (another software
-# stack and board: context, not the target).
+# The README's own benchmark configuration (Performance, kernel-benchmark
+# protocol): causal MHA, batch 1, max(32, 262144 / S) heads (128 at 2K, 32 at
+# 16K and 32K), q, k, v Gaussian with standard deviation 0.1, bshd. Reported
+# beside the README's MI355X figure for the same configuration (another
+# software stack and board: context, not the target). (dtype, d_qk, S, TF/s)
 CONTEXT_CASES = {
-    "ctx_bf16_d128_std01_s16384": ("bf16", 128, 1237.0),
-    "ctx_bf16_d192_std01_s16384": ("bf16", 192, 1296.0),
-    "ctx_fp8_d128_std01_s16384": ("fp8", 128, 2597.0),
-    "ctx_fp8_d192_std01_s16384": ("fp8", 192, 2391.0),
+    "ctx_bf16_d128_std01_s16384": ("bf16", 128, 16384, 1237.0),
+    "ctx_bf16_d192_std01_s16384": ("bf16", 192, 16384, 1296.0),
+    "ctx_fp8_d128_std01_s16384": ("fp8", 128, 16384, 2597.0),
+    "ctx_fp8_d192_std01_s16384": ("fp8", 192, 16384, 2391.0),
+    "ctx_bf16_d128_std01_s2048": ("bf16", 128, 2048, 1000.0),
+    "ctx_bf16_d192_std01_s2048": ("bf16", 192, 2048, 1008.0),
+    "ctx_fp8_d128_std01_s2048": ("fp8", 128, 2048, 1942.0),
+    "ctx_fp8_d192_std01_s2048": ("fp8", 192, 2048, 1929.0),
+    "ctx_bf16_d128_std01_s32768": ("bf16", 128, 32768, 1265.0),
+    "ctx_bf16_d192_std01_s32768": ("bf16", 192, 32768, 1330.0),
+    "ctx_fp8_d128_std01_s32768": ("fp8", 128, 32768, 2672.0),
+    "ctx_fp8_d192_std01_s32768": ("fp8", 192, 32768, 2464.0),
 }
 MERGE_CASE = "merge_bf16_s16384"
 HBM_PEAK_GBS = 8000.0
@@ -437,8 +445,8 @@ def context_setup(name, zy):
     """Inputs and the launch of one README-configuration case: (fn, flops)."""
     import numpy as np
     import torch
-    dtype, dqk, readme = CONTEXT_CASES[name]
-    S, H = 16384, max(32, 262144 // 16384)
+    dtype, dqk, S, readme = CONTEXT_CASES[name]
+    H = max(32, 262144 // S)
     rng = np.random.Generator(np.random.PCG64(dqk))
     dev = torch.device("cuda:0")
     q, k = (torch.from_numpy(0.1 * rng.standard_normal((1, S, H, dqk), dtype=np.float32)).to(torch.bfloat16).to(dev)
@@ -481,7 +489,7 @@ def protocol_a(zy, runs: int = 3, warmup: int = 500, timed: int = 100, idle: flo
     res = {}
     for n in names:
         t = sorted(per[n])[len(per[n]) // 2]
-        readme = CONTEXT_CASES[n][2]
+        readme = CONTEXT_CASES[n][3]
         res[n] = {"tflops": round(t, 2), "runs": [round(x, 1) for x in per[n]], "readme_mi355x_tflops": readme,
                   "ratio_to_readme": round(t / readme, 3)}
     return {"protocol": f"{idle:g} s idle, {warmup} warm-up launches, mean of {timed}, {runs} runs with the order "
@@ -492,8 +500,8 @@ def context_case(name, zy, args):
     """The README's benchmark configuration (see CONTEXT_CASES)."""
     import numpy as np
     import torch
-    dtype, dqk, readme = CONTEXT_CASES[name]
-    S, H = 16384, max(32, 262144 // 16384)
+    dtype, dqk, S, readme = CONTEXT_CASES[name]
+    H = max(32, 262144 // S)
     rng = np.random.Generator(np.random.PCG64(dqk))
     dev = torch.device("cuda:0")
     q, k = (torch.from_numpy(0.1 * rng.standard_normal((1, S, H, dqk), dtype=np.float32)).to(torch.bfloat16).to(dev)
