@@ -162,7 +162,10 @@ def fp8_p_rounding_lse_allowance(qh: np.ndarray, kh: np.ndarray, scale: float, r
         w = np.exp(s - s.max())
         w /= w.sum()
         a = np.minimum(absc * w.max(), w)
-        out[r] = -math.log(1.0 - rel - a.sum())
+        x = 1.0 - rel - a.sum()
+        # on long flat rows the absolute terms (taken against the row's
+        # largest weight) can sum past 1 - rel: the bound is vacuous there
+        out[r] = -math.log(x) if x > 0.0 else math.inf
     return out
 
 
@@ -207,21 +210,71 @@ FP8_ROUND_LSE_MAX = 1e-2
 FP8_ROUND_LSE_MEAN = 1e-4
 
 
-def check_fp8_rounding(out, ref_out, lse, ref_lse, what=""):
+# One probability landing one code step away from the model's moves its
+# weight w_j by at most 2^-3 w_j (a mantissa step of e4m3 is at most 2^-3 of
+# the value; a lean code step 2^(1/8) - 1 < 2^-3), so, with weights summing
+# to 1, the row's output by at most 2^-3 w_j max_c |v_jc - o_c| / (1 - 2^-3
+# w_j) and its LSE by at most -ln(1 - 2^-3 w_j).
+FP8_FLIP_REL = 2.0 ** -3
+FP8_FLIP_ROWS = 2e-2        # rows with a flip, at most (at least 4 allowed)
+
+
+def fp8_code_flip_bounds(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, rows):
+    """Per-row (out, LSE) bounds of one code flip of the worst key, from the
+    exact softmax weights (a diagnostic allowance of check_fp8_rounding)."""
+    rows = np.asarray(rows)
+    ob = np.empty(rows.shape[0])
+    lb = np.empty(rows.shape[0])
+    for r, i in enumerate(rows):
+        s = (kh[: i + 1] @ qh[i]) * scale
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        o = w @ vh[: i + 1]
+        dev = np.abs(vh[: i + 1] - o).max(axis=1)
+        step = FP8_FLIP_REL * w
+        ob[r] = (step * dev / (1.0 - step)).max()
+        lb[r] = -math.log(1.0 - step.max())
+    return ob, lb
+
+
+def check_fp8_rounding(out, ref_out, lse, ref_lse, what="", flip=None, flip_lse=None):
+    """The kernel against the rounding model. flip, flip_lse (per row of
+    out's leading axes, from fp8_code_flip_bounds): where given, an element
+    may pass the tight bound by what one code flip in its row explains, in
+    at most FP8_FLIP_ROWS of the rows (at least 4; a flip moves every
+    column of its row); the LSE of every row stays within the tight bound
+    plus its flip bound, and the mean of all but the FP8_FLIP_ROWS largest
+    LSE errors (at least 4) within the tight mean."""
     d = np.abs(out - ref_out)
     bound = FP8_ROUND_MAX + BF16_OUT_REL_ROUND * np.abs(ref_out)
     worst = np.unravel_index(np.argmax(d - bound), d.shape)
-    stats = f"{what}: max|dout|={d.max():.3e} mean={d.mean():.3e}"
+    over = int(np.count_nonzero(d > bound))
+    stats = f"{what}: max|dout|={d.max():.3e} mean={d.mean():.3e} over the tight bound {over}"
     if lse is not None:
         dl = np.abs(lse - ref_lse)
         stats += f" max|dLSE|={dl.max():.3e} mean={dl.mean():.3e}"
     print(stats, flush=True)
     assert np.all(np.isfinite(out)), what + ": non-finite output"
-    assert np.all(d <= bound), f"{stats} worst at {worst} (ref {ref_out[worst]:.4f} got {out[worst]:.4f})"
+    if flip is None:
+        assert np.all(d <= bound), f"{stats} worst at {worst} (ref {ref_out[worst]:.4f} got {out[worst]:.4f})"
+    else:
+        # a flip moves every column of its row, so rows are counted
+        rows_over = int(np.count_nonzero((d > bound).reshape(d.shape[0], -1).any(axis=1)))
+        assert rows_over <= max(4, FP8_FLIP_ROWS * d.shape[0]), f"{stats}, in {rows_over} rows"
+        assert np.all(d <= bound + flip[..., None]), f"{stats}: beyond one code flip at {worst}"
     assert d.mean() <= FP8_ROUND_MEAN, stats
     if lse is not None:
         assert np.all(np.isfinite(lse)), what + ": non-finite lse"
-        assert dl.max() <= FP8_ROUND_LSE_MAX and dl.mean() <= FP8_ROUND_LSE_MEAN, stats
+        if flip_lse is None:
+            assert dl.max() <= FP8_ROUND_LSE_MAX and dl.mean() <= FP8_ROUND_LSE_MEAN, stats
+        else:
+            # rows with a flipped code are held to the flip bound; the mean
+            # of the others (all but the FP8_FLIP_ROWS largest, at least 4)
+            # stays tight
+            assert np.all(dl <= FP8_ROUND_LSE_MAX + flip_lse), stats
+            k = max(4, int(np.ceil(FP8_FLIP_ROWS * dl.size)))
+            rest = np.sort(dl.ravel())[:-k]
+            assert rest.size == 0 or rest.mean() <= FP8_ROUND_LSE_MEAN, f"{stats} (mean of the rest {rest.mean():.3e})"
 
 
 def check_partial(out, ref_out, lse, ref_lse, what="", fp8=False):
