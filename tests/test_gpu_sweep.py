@@ -106,8 +106,8 @@ def _fp8_gate_or_known_limit(o, ref_out, rq, rk, rv, layout, H, Hk, dqk, S, p_mo
     assert S <= 64 or d.mean() <= FP8_OUT_MEAN, f"{what}: mean|dout|={d.mean():.3e}"
 
 
-def _draw_range_case(i):
-    rng = np.random.default_rng(9500 + i)
+def _draw_range_case(i, base=9500):
+    rng = np.random.default_rng(base + i)
     B = int(rng.integers(1, 3))
     Sq = int(rng.integers(1, 900))
     Sk = int(rng.integers(1, 1500))
@@ -262,7 +262,8 @@ def test_random_shape_fp8_modes(B, S, H, Hk, dqk, layout, lse, tq, p_mode):
 
 # An extended sweep, off by default: ZYFA_SWEEP_EXTRA=N adds N seeded cases
 # (seed base ZYFA_SWEEP_BASE, default 20000) over BF16 and every FP8 mode,
-# lengths 1..3000, with the checks of the two tests above. Sizes are capped
+# lengths 1..3000, with the checks of the tests above, and N / 3 more range
+# calls. Sizes are capped
 # so that the float64 oracle stays at a few seconds per case.
 _N_EXTRA = int(os.environ.get("ZYFA_SWEEP_EXTRA", "0"))
 _EXTRA_BASE = int(os.environ.get("ZYFA_SWEEP_BASE", "20000"))
@@ -289,6 +290,11 @@ def _draw_extra_case(i):
 
 
 if _N_EXTRA > 0:
+    @pytest.mark.parametrize("B,Sq,Sk,qp,kp,H,Hk,dqk,layout,dtype,tq",
+                             [_draw_range_case(i, _EXTRA_BASE + 30000) for i in range(_N_EXTRA // 3)])
+    def test_random_range_extended(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, dtype, tq):
+        test_random_range(B, Sq, Sk, qp, kp, H, Hk, dqk, layout, dtype, tq)
+
     @pytest.mark.parametrize("B,S,H,Hk,dqk,layout,lse,tq,kind", [_draw_extra_case(i) for i in range(_N_EXTRA)])
     def test_random_shape_extended(B, S, H, Hk, dqk, layout, lse, tq, kind):
         if kind in ("bf16", "fp8"):
