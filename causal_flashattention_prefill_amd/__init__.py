@@ -117,14 +117,64 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported input dtype {t.dtype}")
 
 
-def _dims(q, k, v, layout: str):
-    if layout == "bshd":
-        B, S, H, dqk = q.shape
-        Hk = k.shape[2]
-    else:
-        B, H, S, dqk = q.shape
-        Hk = k.shape[1]
-    return B, S, H, Hk, dqk, v.shape[-1]
+# The C ABI takes plain pointers and cannot see buffer sizes, so the binding
+# checks every tensor it passes: shape, dtype and contiguity first, then that
+# all of them live on the same GPU (a host pointer or a short buffer would
+# otherwise reach the kernels).
+
+def _require(t, name: str, shape, dtypes) -> None:
+    if t.dim() != len(shape) or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_gpu(ref, named) -> None:
+    if not ref.is_cuda:
+        raise ValueError("tensors must be on a GPU (cuda) device")
+    for name, t in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _check_descales(named) -> None:
+    import torch
+    for name, t in named:
+        if t is not None and (t.dtype != torch.float32 or t.numel() < 1 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 tensor with at least one element")
+
+
+def _attn_checks(q, k, v, out, lse, layout: str, descales, seqlen_k: Optional[int] = None):
+    """Shapes of q, k, v (k and v with seqlen_k positions when given, else
+    q's), out and lse; one input dtype; descales; one GPU. Returns the dims
+    (B, Sq, Sk, H, Hk, d_qk, d_v)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D ({layout})")
+    in_dtypes = (torch.bfloat16, torch.float8_e4m3fn, torch.uint8)
+    if q.dtype not in in_dtypes:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    bshd = layout == "bshd"
+    B, Sq, H, dqk = (q.shape[0], q.shape[1], q.shape[2], q.shape[3]) if bshd else \
+        (q.shape[0], q.shape[2], q.shape[1], q.shape[3])
+    Sk = Sq if seqlen_k is None else seqlen_k          # whole-sequence calls: k and v have q's length
+    Hk = k.shape[2] if bshd else k.shape[1]
+    dv = v.shape[3]
+    shp = (lambda s, h, d: (B, s, h, d)) if bshd else (lambda s, h, d: (B, h, s, d))
+    same = (q.dtype,) if q.dtype == torch.bfloat16 else (torch.float8_e4m3fn, torch.uint8)
+    _require(q, "q", shp(Sq, H, dqk), in_dtypes)
+    _require(k, "k", shp(Sk, Hk, dqk), same)
+    _require(v, "v", shp(Sk, Hk, dv), same)
+    if out is not None:
+        _require(out, "out", shp(Sq, H, dv), (torch.bfloat16,))
+    if lse is not None:
+        _require(lse, "lse", (B, H, Sq), (torch.float32,))
+    _check_descales(descales)
+    _same_gpu(q, [("k", k), ("v", v), ("out", out), ("lse", lse)] + list(descales))
+    return B, Sq, Sk, H, Hk, dqk, dv
 
 
 def zyfa_fwd(q, k, v, out=None, lse=None, *, layout: str = "bshd", return_lse: bool = False,
@@ -138,10 +188,8 @@ def zyfa_fwd(q, k, v, out=None, lse=None, *, layout: str = "bshd", return_lse: b
     import torch
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {list(LAYOUTS)}")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k and v must be contiguous")
-    B, S, H, Hk, dqk, dv = _dims(q, k, v, layout)
+    desc = [("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)]
+    B, S, _, H, Hk, dqk, dv = _attn_checks(q, k, v, out, lse, layout, desc, None)
     dt = _dtype_code(q)
     if out is None:
         shape = (B, S, H, dv) if layout == "bshd" else (B, H, S, dv)
@@ -172,10 +220,10 @@ def zyfa_fwd_noalloc(q, k, v, out, lse=None, *, layout: str = "bshd", q_descale=
         raise ValueError(f"layout must be one of {list(LAYOUTS)}")
     if p_mode not in P_MODES:
         raise ValueError(f"p_mode must be one of {list(P_MODES)}")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k and v must be contiguous")
-    B, S, H, Hk, dqk, dv = _dims(q, k, v, layout)
+    if out is None:
+        raise ValueError("zyfa_fwd_noalloc writes into a caller-given out")
+    desc = [("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)]
+    B, S, _, H, Hk, dqk, dv = _attn_checks(q, k, v, out, lse, layout, desc, None)
     rc = lib().zyfa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S, H, Hk, dqk, dv,
                                 LAYOUTS[layout], _dtype_code(q), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
                                 0.0 if softmax_scale is None else float(softmax_scale), P_MODES[p_mode],
@@ -197,11 +245,11 @@ def zyfa_fwd_range(q, k, v, q_pos0: int, k_pos0: int, out=None, lse=None, *, lay
         raise ValueError(f"layout must be one of {list(LAYOUTS)}")
     if p_mode not in P_MODES:
         raise ValueError(f"p_mode must be one of {list(P_MODES)}")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k and v must be contiguous")
-    B, Sq, H, Hk, dqk, dv = _dims(q, k, v, layout)
+    desc = [("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)]
+    if k.dim() != 4:
+        raise ValueError(f"k must be 4-D ({layout})")
     Sk = k.shape[1] if layout == "bshd" else k.shape[2]
+    B, Sq, Sk, H, Hk, dqk, dv = _attn_checks(q, k, v, out, lse, layout, desc, Sk)
     if out is None:
         shape = (B, Sq, H, dv) if layout == "bshd" else (B, H, Sq, dv)
         out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
@@ -229,8 +277,17 @@ def zyfa_lse_merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, *, layout: st
         raise ValueError("the two partial results must have the same shapes")
     if out_a.dtype != torch.bfloat16 or lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
         raise TypeError("out must be bf16 and lse fp32")
+    if lse_a.dim() != 3 or out_a.dim() != 4:
+        raise ValueError("lse must be (batch, heads, seqlen) and out 4-D")
     B, H, S = lse_a.shape
     dv = out_a.shape[-1]
+    want = (B, S, H, dv) if layout == "bshd" else (B, H, S, dv)
+    _require(out_a, "out_a", want, (torch.bfloat16,))
+    if out is not None:
+        _require(out, "out", want, (torch.bfloat16,))
+    if lse is not None:
+        _require(lse, "lse", (B, H, S), (torch.float32,))
+    _same_gpu(out_a, [("out_b", out_b), ("lse_a", lse_a), ("lse_b", lse_b), ("out", out), ("lse", lse)])
     if out is None:
         out = torch.empty_like(out_a)
     if lse is None:
@@ -262,6 +319,10 @@ def zyfa_fp8_quantize(x, x8=None, descale=None, stream=None):
     xd = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}.get(x.dtype)
     if xd is None:
         raise TypeError(f"unsupported dtype {x.dtype}")
+    if x8 is not None:
+        _require(x8, "x8", tuple(x.shape), (torch.float8_e4m3fn, torch.uint8))
+    _check_descales([("descale", descale)])
+    _same_gpu(x, [("x8", x8), ("descale", descale)])
     if x8 is None:
         x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
     if descale is None:
@@ -294,6 +355,10 @@ def zyfa_fp8_quantize_rotated(x, signs=None, x8=None, descale=None, *, shift=Non
         sg = np.ascontiguousarray(np.asarray(signs.cpu() if hasattr(signs, "cpu") else signs).astype(np.int8))
         if sg.shape != (d,):
             raise ValueError(f"signs must hold {d} values")
+    if x8 is not None:
+        _require(x8, "x8", tuple(x.shape), (torch.float8_e4m3fn, torch.uint8))
+    _check_descales([("descale", descale)])
+    _same_gpu(x, [("x8", x8), ("descale", descale), ("shift", shift)])
     if x8 is None:
         x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
     if descale is None:
@@ -324,6 +389,9 @@ def zyfa_key_mean(k, *, layout: str = "bshd", mean=None, stream=None):
         raise TypeError(f"unsupported dtype {k.dtype}")
     B, S, H = (k.shape[0], k.shape[1], k.shape[2]) if layout == "bshd" else (k.shape[0], k.shape[2], k.shape[1])
     d = k.shape[3]
+    if mean is not None:
+        _require(mean, "mean", (B, H, d), (torch.float32,))
+    _same_gpu(k, [("mean", mean)])
     if mean is None:
         mean = torch.empty((B, H, d), dtype=torch.float32, device=k.device)
     _check(lib().zyfa_key_mean(_ptr(k), kd, B, S, H, d, LAYOUTS[layout], _ptr(mean), _stream(stream)),
