@@ -101,11 +101,20 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, ref=None) -> Optional[int]:
+    """The HIP stream handle: `stream`, or the current stream of ref's device."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(ref.device if ref is not None and ref.is_cuda else None)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _on_device(ref):
+    """Makes ref's GPU the current device for a library call: the library
+    keeps its plans per current device and launches on the given stream."""
+    import contextlib
+    import torch
+    return torch.cuda.device(ref.device) if ref is not None and ref.is_cuda else contextlib.nullcontext()
 
 
 def _dtype_code(t) -> int:
@@ -201,11 +210,12 @@ def zyfa_fwd(q, k, v, out=None, lse=None, *, layout: str = "bshd", return_lse: b
             _ptr(q_descale), _ptr(k_descale), _ptr(v_descale))
     if p_mode not in P_MODES:
         raise ValueError(f"p_mode must be one of {list(P_MODES)}")
-    if softmax_scale is None and p_mode == "default":
-        rc = L.zyfa_fwd(*args, _stream(stream))
-    else:
-        rc = L.zyfa_fwd_ex(*args, 0.0 if softmax_scale is None else float(softmax_scale), P_MODES[p_mode],
-                           _stream(stream))
+    with _on_device(q):
+        if softmax_scale is None and p_mode == "default":
+            rc = L.zyfa_fwd(*args, _stream(stream, q))
+        else:
+            rc = L.zyfa_fwd_ex(*args, 0.0 if softmax_scale is None else float(softmax_scale), P_MODES[p_mode],
+                               _stream(stream, q))
     _check(rc, "zyfa_fwd")
     return (out, lse) if lse is not None else out
 
@@ -224,10 +234,11 @@ def zyfa_fwd_noalloc(q, k, v, out, lse=None, *, layout: str = "bshd", q_descale=
         raise ValueError("zyfa_fwd_noalloc writes into a caller-given out")
     desc = [("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)]
     B, S, _, H, Hk, dqk, dv = _attn_checks(q, k, v, out, lse, layout, desc, None)
-    rc = lib().zyfa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S, H, Hk, dqk, dv,
-                                LAYOUTS[layout], _dtype_code(q), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
-                                0.0 if softmax_scale is None else float(softmax_scale), P_MODES[p_mode],
-                                _stream(stream))
+    with _on_device(q):
+        rc = lib().zyfa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S, H, Hk, dqk, dv,
+                                    LAYOUTS[layout], _dtype_code(q), _ptr(q_descale), _ptr(k_descale),
+                                    _ptr(v_descale), 0.0 if softmax_scale is None else float(softmax_scale),
+                                    P_MODES[p_mode], _stream(stream, q))
     _check(rc, "zyfa_fwd_noalloc")
     return (out, lse) if lse is not None else out
 
@@ -255,10 +266,12 @@ def zyfa_fwd_range(q, k, v, q_pos0: int, k_pos0: int, out=None, lse=None, *, lay
         out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    rc = lib().zyfa_fwd_range(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, int(q_pos0), int(k_pos0),
-                              H, Hk, dqk, dv, LAYOUTS[layout], _dtype_code(q), _ptr(q_descale), _ptr(k_descale),
-                              _ptr(v_descale), 0.0 if softmax_scale is None else float(softmax_scale),
-                              P_MODES[p_mode], _stream(stream))
+    with _on_device(q):
+        rc = lib().zyfa_fwd_range(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, int(q_pos0),
+                                  int(k_pos0), H, Hk, dqk, dv, LAYOUTS[layout], _dtype_code(q), _ptr(q_descale),
+                                  _ptr(k_descale), _ptr(v_descale),
+                                  0.0 if softmax_scale is None else float(softmax_scale), P_MODES[p_mode],
+                                  _stream(stream, q))
     _check(rc, "zyfa_fwd_range")
     return (out, lse) if lse is not None else out
 
@@ -292,8 +305,10 @@ def zyfa_lse_merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, *, layout: st
         out = torch.empty_like(out_a)
     if lse is None:
         lse = torch.empty_like(lse_a)
-    _check(lib().zyfa_lse_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out), _ptr(lse), B, S, H,
-                                dv, LAYOUTS[layout], _stream(stream)), "zyfa_lse_merge")
+    with _on_device(out_a):
+        rc = lib().zyfa_lse_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out), _ptr(lse), B, S, H,
+                                  dv, LAYOUTS[layout], _stream(stream, out_a))
+    _check(rc, "zyfa_lse_merge")
     return out, lse
 
 
@@ -327,8 +342,9 @@ def zyfa_fp8_quantize(x, x8=None, descale=None, stream=None):
         x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
     if descale is None:
         descale = torch.empty(1, dtype=torch.float32, device=x.device)
-    _check(lib().zyfa_fp8_quantize(_ptr(x), xd, x.numel(), _ptr(x8), _ptr(descale), _stream(stream)),
-           "zyfa_fp8_quantize")
+    with _on_device(x):
+        rc = lib().zyfa_fp8_quantize(_ptr(x), xd, x.numel(), _ptr(x8), _ptr(descale), _stream(stream, x))
+    _check(rc, "zyfa_fp8_quantize")
     return x8, descale
 
 
@@ -365,15 +381,18 @@ def zyfa_fp8_quantize_rotated(x, signs=None, x8=None, descale=None, *, shift=Non
         descale = torch.empty(1, dtype=torch.float32, device=x.device)
     sp = None if sg is None else sg.ctypes.data
     if shift is None:
-        rc = lib().zyfa_fp8_quantize_rotated(_ptr(x), xd, rows, d, sp, _ptr(x8), _ptr(descale), _stream(stream))
+        with _on_device(x):
+            rc = lib().zyfa_fp8_quantize_rotated(_ptr(x), xd, rows, d, sp, _ptr(x8), _ptr(descale),
+                                                 _stream(stream, x))
     else:
         if x.dim() != 4 or layout not in LAYOUTS:
             raise ValueError("a shift needs a 4-D x in bshd or bhsd")
         B, S, H = (x.shape[0], x.shape[1], x.shape[2]) if layout == "bshd" else (x.shape[0], x.shape[2], x.shape[1])
         if shift.dtype != torch.float32 or tuple(shift.shape) != (B, H, d) or not shift.is_contiguous():
             raise ValueError(f"shift must be a contiguous fp32 tensor of shape {(B, H, d)}")
-        rc = lib().zyfa_fp8_quantize_rotated_shifted(_ptr(x), xd, B, S, H, d, LAYOUTS[layout], sp, _ptr(shift),
-                                                     _ptr(x8), _ptr(descale), _stream(stream))
+        with _on_device(x):
+            rc = lib().zyfa_fp8_quantize_rotated_shifted(_ptr(x), xd, B, S, H, d, LAYOUTS[layout], sp, _ptr(shift),
+                                                         _ptr(x8), _ptr(descale), _stream(stream, x))
     _check(rc, "zyfa_fp8_quantize_rotated")
     return x8, descale
 
@@ -394,8 +413,9 @@ def zyfa_key_mean(k, *, layout: str = "bshd", mean=None, stream=None):
     _same_gpu(k, [("mean", mean)])
     if mean is None:
         mean = torch.empty((B, H, d), dtype=torch.float32, device=k.device)
-    _check(lib().zyfa_key_mean(_ptr(k), kd, B, S, H, d, LAYOUTS[layout], _ptr(mean), _stream(stream)),
-           "zyfa_key_mean")
+    with _on_device(k):
+        rc = lib().zyfa_key_mean(_ptr(k), kd, B, S, H, d, LAYOUTS[layout], _ptr(mean), _stream(stream, k))
+    _check(rc, "zyfa_key_mean")
     return mean
 
 
