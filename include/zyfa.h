@@ -318,7 +318,10 @@ int zyfa_fp8_quantize_rotated_shifted(const void* x, int x_dtype, int batch, int
 const char* zyfa_status_string(int status);
 
 /* zyfa_release - free every cached plan on every device (device memory of
- * the job tables). Must not race with calls in flight. */
+ * the job tables). Must not race with calls in flight. Plans are kept until
+ * this call: one per shape and query-tile height, 8 bytes per job-table
+ * entry (8 KiB for 16K tokens at 32 heads), so a server that sees many
+ * distinct shapes can release them between phases. */
 void zyfa_release(void);
 
 /*
