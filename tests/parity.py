@@ -118,53 +118,77 @@ FP8_P_REL = 2.0 ** -4
 FP8_P_ABS = 2.0 ** -9
 
 
+FP8_P_BLOCK = 32   # keys per power-of-two scale block of the FP8 kernels (aligned at key 0)
+
+
+def _p_rounding_terms(qh, kh, scale, i, nkeys, absc):
+    """Exact weights w of row i over its visible keys 0..nkeys-1 and the
+    absolute terms a_j = min(absc * (largest weight of j's scale block), w_j)."""
+    s = (kh[:nkeys] @ qh[i]) * scale
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    starts = np.arange(0, nkeys, FP8_P_BLOCK)
+    bmax = np.repeat(np.maximum.reduceat(w, starts), FP8_P_BLOCK)[:nkeys]
+    return w, np.minimum(absc * bmax, w)
+
+
+def _visible(rows, nkeys):
+    rows = np.asarray(rows)
+    return rows, (rows + 1 if nkeys is None else np.asarray(nkeys))
+
+
 def fp8_p_rounding_allowance(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, rows,
-                             rel: float = FP8_P_REL, absc: float = FP8_P_ABS) -> np.ndarray:
+                             rel: float = FP8_P_REL, absc: float = FP8_P_ABS, nkeys=None) -> np.ndarray:
     """Per-row bound on |d out| caused by rounding the probabilities to e4m3
     alone (a diagnostic of that known limit, never part of the gate).
 
     With the exact softmax weights w_j of row i and o = sum_j w_j v_j, weights
     perturbed to w_j (1 + d_j) + a_j (|d_j| <= rel, and |a_j| <= min(absc
-    max_j w_j, w_j): a probability that is too small for a normal code is
-    rounded to a subnormal one or to zero, never by more than itself) give
+    b_j, w_j) with b_j the largest weight of key j's 32-key scale block: the
+    kernels scale each block so that its largest probability lands in [1, 2),
+    and a probability too small for a normal code there is rounded to a
+    subnormal one or to zero, never by more than itself) give
     o' - o = sum_j (w_j d_j + a_j) (v_j - o) / sum_j (w_j (1 + d_j) + a_j),
     since sum_j w_j (v_j - o) = 0. Returns, per row, the maximum over the
-    columns of that bound. rel = 2^-4 is rounding to nearest; 2^-3 (one code
-    step) also covers a code that the kernel's fp32 score rounds the other
-    way at a tie, and lean P, whose value 2^floor(y) (1 + frac(y)) stays
-    within about 9 % of 2^y; lean P writes code 0 for probabilities below
-    about 2^-6.9 of their block's scale (absc = 2^-5 covers it)."""
-    rows = np.asarray(rows)
+    columns of that bound (infinite where rel + sum_j a_j reaches 1). rel =
+    2^-4 is rounding to nearest; 2^-3 (one code step) also covers a code that
+    the kernel's fp32 score rounds the other way at a tie, and lean P, whose
+    value 2^floor(y) (1 + frac(y)) stays within about 9 % of 2^y; lean P
+    writes code 0 for probabilities below 2^-7 of their block's scale
+    (absc = 2^-5 covers it; exact P's subnormals lie below 2^-6 of it and
+    move by at most 2^-10 of it: absc = 2^-9). Row i sees keys 0..i, or
+    0..nkeys[r]-1 when nkeys is given (range calls)."""
+    rows, nk = _visible(rows, nkeys)
     out = np.empty(rows.shape[0])
     for r, i in enumerate(rows):
-        s = (kh[: i + 1] @ qh[i]) * scale
-        w = np.exp(s - s.max())
-        w /= w.sum()
-        o = w @ vh[: i + 1]
-        dev = np.abs(vh[: i + 1] - o)                      # (keys, d_v)
-        a = np.minimum(absc * w.max(), w)
+        n = int(nk[r])
+        if n <= 0:
+            out[r] = 0.0
+            continue
+        w, a = _p_rounding_terms(qh, kh, scale, i, n, absc)
+        o = w @ vh[:n]
+        dev = np.abs(vh[:n] - o)                           # (keys, d_v)
         num = rel * (w @ dev) + a @ dev
         den = 1.0 - rel - a.sum()
-        out[r] = (num / den).max()
+        out[r] = (num / den).max() if den > 0.0 else math.inf
     return out
 
 
 def fp8_p_rounding_lse_allowance(qh: np.ndarray, kh: np.ndarray, scale: float, rows, rel: float = FP8_P_REL,
-                                 absc: float = FP8_P_ABS) -> np.ndarray:
+                                 absc: float = FP8_P_ABS, nkeys=None) -> np.ndarray:
     """Per-row bound on |d LSE| (natural log) from the same perturbed weights
     as fp8_p_rounding_allowance: the rounded sum lies within a factor
     (1 +- (rel + sum_j a_j)) of the exact one, so |d LSE| <= -ln(1 - rel -
-    sum_j a_j)."""
-    rows = np.asarray(rows)
+    sum_j a_j) (infinite where rel + sum_j a_j reaches 1)."""
+    rows, nk = _visible(rows, nkeys)
     out = np.empty(rows.shape[0])
     for r, i in enumerate(rows):
-        s = (kh[: i + 1] @ qh[i]) * scale
-        w = np.exp(s - s.max())
-        w /= w.sum()
-        a = np.minimum(absc * w.max(), w)
+        n = int(nk[r])
+        if n <= 0:
+            out[r] = 0.0
+            continue
+        _, a = _p_rounding_terms(qh, kh, scale, i, n, absc)
         x = 1.0 - rel - a.sum()
-        # on long flat rows the absolute terms (taken against the row's
-        # largest weight) can sum past 1 - rel: the bound is vacuous there
         out[r] = -math.log(x) if x > 0.0 else math.inf
     return out
 
